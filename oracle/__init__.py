@@ -1,0 +1,187 @@
+"""fp64 CPU oracle for the selective scan -- TEST INFRASTRUCTURE.
+
+Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of `bench.py`
+may import this package. The product path (the HIP library and its binding) never
+does: it shares no code with it and fails loudly when its own library is missing.
+
+The arithmetic lives in `ssm_oracle.c` (plain C, fp64, one sequential loop per
+row; see `ssm_oracle.h` for the recurrence and where each part of it comes from
+on the pages). This module only builds that file with gcc, widens inputs exactly
+to fp64 and calls it through ctypes.
+
+Every oracle function is pinned by CPU tests against things other than itself
+(closed forms, library routines, brute force, invariants): see tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssmoracle.so")
+_lib = None
+_lock = threading.Lock()
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True, out: str | None = None, extra_flags=()) -> str:
+    """Compile ssm_oracle.c with gcc (no fast-math: IEEE fp64 throughout)."""
+    out = out or _LIB_PATH
+    src = _SRC
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+           "-ffp-contract=off", *extra_flags, src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    return out
+
+
+def _load(path: str | None = None):
+    lib = ctypes.CDLL(path or _LIB_PATH)
+    lib.ssm_oracle_softplus.restype = ctypes.c_double
+    lib.ssm_oracle_softplus.argtypes = [ctypes.c_double]
+    lib.ssm_oracle_silu.restype = ctypes.c_double
+    lib.ssm_oracle_silu.argtypes = [ctypes.c_double]
+    lib.ssm_oracle_scan_rows.restype = ctypes.c_int
+    lib.ssm_oracle_scan_rows.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _ip, _ip,
+        _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, ctypes.c_int]
+    lib.ssm_oracle_step_rows.restype = ctypes.c_int
+    lib.ssm_oracle_step_rows.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, _ip, _ip, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+        _dp, ctypes.c_int, _dp]
+    return lib
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            _lib = _load()
+        return _lib
+
+
+class Oracle:
+    """A handle on one built copy of the oracle (tests build planted-mistake
+    copies of the same source to show the pins catch them)."""
+
+    def __init__(self, path: str | None = None):
+        self._l = _load(path) if path else lib()
+
+    # ---- scalar helpers -------------------------------------------------
+    def softplus(self, v: float) -> float:
+        return self._l.ssm_oracle_softplus(float(v))
+
+    def silu(self, z: float) -> float:
+        return self._l.ssm_oracle_silu(float(z))
+
+    # ---- scan -----------------------------------------------------------
+    def scan_rows(self, x_rows, delta_rows, A, B, C, row_b, row_d, z_rows=None, D=None,
+                  delta_bias=None, delta_softplus=True, h0_rows=None, nthreads=1,
+                  want_final=True):
+        """Rows given explicitly: x_rows/delta_rows/z_rows are [R][L]; B, C are
+        [batch][L][N]; A is [dim][N]; row_b/row_d name each row's batch and channel."""
+        x_rows = f64(x_rows)
+        delta_rows = f64(delta_rows)
+        R, L = x_rows.shape
+        A = f64(A)
+        N = A.shape[1]
+        B = f64(B)
+        C = f64(C)
+        assert B.shape[1:] == (L, N) and C.shape == B.shape and delta_rows.shape == (R, L)
+        rb = np.ascontiguousarray(np.asarray(row_b, dtype=np.int64).reshape(R))
+        rd = np.ascontiguousarray(np.asarray(row_d, dtype=np.int64).reshape(R))
+        assert rb.size == 0 or (rb.min() >= 0 and rb.max() < B.shape[0])
+        assert rd.size == 0 or (rd.min() >= 0 and rd.max() < A.shape[0])
+        z_rows = None if z_rows is None else f64(z_rows)
+        if z_rows is not None:
+            assert z_rows.shape == (R, L)
+        D = None if D is None else f64(D)
+        delta_bias = None if delta_bias is None else f64(delta_bias)
+        h0_rows = None if h0_rows is None else f64(h0_rows).reshape(R, N)
+        y = np.empty((R, L), dtype=np.float64)
+        hf = np.empty((R, N), dtype=np.float64) if want_final else None
+        rc = self._l.ssm_oracle_scan_rows(
+            R, L, N, _ptr_i(rb), _ptr_i(rd), _ptr(x_rows), _ptr(delta_rows), _ptr(z_rows),
+            _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), int(bool(delta_softplus)),
+            _ptr(h0_rows), _ptr(y), _ptr(hf), int(nthreads))
+        if rc != 0:
+            raise RuntimeError("ssm_oracle_scan_rows failed")
+        return y, hf
+
+    def scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+             h0=None, nthreads=1):
+        """Full tensors: x, delta, z are [batch][dim][L]; h0 [batch][dim][N].
+        Returns y [batch][dim][L] and h_final [batch][dim][N] in fp64."""
+        x = f64(x)
+        b, d, L = x.shape
+        N = f64(A).shape[1]
+        rb = np.repeat(np.arange(b, dtype=np.int64), d)
+        rd = np.tile(np.arange(d, dtype=np.int64), b)
+        y, hf = self.scan_rows(
+            x.reshape(b * d, L), f64(delta).reshape(b * d, L), A, B, C, rb, rd,
+            z_rows=None if z is None else f64(z).reshape(b * d, L), D=D,
+            delta_bias=delta_bias, delta_softplus=delta_softplus,
+            h0_rows=None if h0 is None else f64(h0).reshape(b * d, N), nthreads=nthreads)
+        return y.reshape(b, d, L), hf.reshape(b, d, N)
+
+    # ---- decode step ----------------------------------------------------
+    def step(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+             delta_softplus=True):
+        """One token for every (batch, channel): state [batch][dim][N] (fp64, updated
+        and returned), x/delta/z [batch][dim], B/C [batch][N]. Returns (y, state)."""
+        st = np.array(f64(state), dtype=np.float64, copy=True)
+        b, d, N = st.shape
+        rb = np.repeat(np.arange(b, dtype=np.int64), d)
+        rd = np.tile(np.arange(d, dtype=np.int64), b)
+        y = np.empty(b * d, dtype=np.float64)
+        xs = f64(x).reshape(b * d)
+        ds = f64(delta).reshape(b * d)
+        zs = None if z is None else f64(z).reshape(b * d)
+        rc = self._l.ssm_oracle_step_rows(
+            b * d, N, _ptr_i(rb), _ptr_i(rd), _ptr(st), _ptr(xs), _ptr(ds), _ptr(zs),
+            _ptr(f64(A)), _ptr(f64(B)), _ptr(f64(C)), _ptr(None if D is None else f64(D)),
+            _ptr(None if delta_bias is None else f64(delta_bias)), int(bool(delta_softplus)),
+            _ptr(y))
+        if rc != 0:
+            raise RuntimeError("ssm_oracle_step_rows failed")
+        return y.reshape(b, d), st
+
+
+def f64(a) -> np.ndarray:
+    """Exact widening to a C-contiguous fp64 numpy array (torch bf16/fp32 tensors
+    on any device, numpy arrays, Python sequences)."""
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu")
+            if a.dtype in (torch.bfloat16, torch.float16):
+                a = a.to(torch.float32)  # exact
+            a = a.to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_dp)
+
+
+def _ptr_i(a):
+    return a.ctypes.data_as(_ip)
+
+
+def default() -> Oracle:
+    return Oracle()

@@ -1,0 +1,318 @@
+"""Pins for the fp64 oracle: each check ties the oracle to something other than
+itself -- a closed form worked by hand, a library routine (numpy.cumsum,
+numpy.convolve, numpy.fft, numpy.logaddexp), an O(L^2) brute force written
+independently, or an exact invariant.
+
+Every function takes an `oracle.Oracle` and raises AssertionError on a mismatch.
+tests/test_oracle_pins.py runs them on the real oracle; tests/test_oracle_mutants.py
+runs them on copies of the oracle with planted mistakes and requires each copy to
+fail at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(float(np.max(np.abs(b))), 1e-300)
+    return float(np.max(np.abs(a - b))) / den
+
+
+def _rows(batch, dim):
+    rb = np.repeat(np.arange(batch), dim)
+    rd = np.tile(np.arange(dim), batch)
+    return rb, rd
+
+
+# ---------------------------------------------------------------------------
+# P1: one token and two tokens worked by hand (closed forms).
+# ---------------------------------------------------------------------------
+def pin_hand_example(orc):
+    """tests/golden/hand_two_tokens.json: N=2, A=(-1,-2), v = delta_raw + bias = 0
+    so Delta = softplus(0) = ln 2 and exp(Delta*A) = (1/2, 1/4) exactly."""
+    with open(os.path.join(GOLDEN, "hand_two_tokens.json")) as f:
+        g = json.load(f)
+    inp = g["inputs"]
+    ln2 = math.log(2.0)
+    e1 = math.exp(-1.0)
+    # Closed forms derived in the fixture (evaluated here with math only).
+    h1 = [0.5 + 2 * ln2, -0.25 + 4 * ln2]
+    y1 = (2.75 + 2 * ln2) / (1 + e1)
+    # token 2: x = 0, z = 2, same Delta -> h2 = (h1[0]/2, h1[1]/4)
+    h2 = [h1[0] / 2, h1[1] / 4]
+    s2 = -1.0 * h2[0] + 2.0 * h2[1]          # C_2 = (-1, 2), D*x = 0
+    y2 = s2 * 2.0 / (1 + math.exp(-2.0))
+    for got, want in zip(g["expected_decimal"]["h1"], h1):
+        assert abs(got - want) < 1e-15 * max(1, abs(want)), (got, want)
+    assert abs(g["expected_decimal"]["y1"] - y1) < 1e-15
+
+    x = np.array([inp["x"]])
+    dl = np.array([inp["delta_raw"]])
+    z = np.array([inp["z"]])
+    A = np.array([inp["A"]])
+    B = np.array([inp["B"]])
+    C = np.array([inp["C"]])
+    y, hf = orc.scan_rows(x, dl, A, B, C, [0], [0], z_rows=z, D=[inp["D"]],
+                          delta_bias=[inp["delta_bias"]], delta_softplus=True,
+                          h0_rows=np.array([inp["h0"]]))
+    assert abs(y[0, 0] - y1) <= 1e-14 * abs(y1), (y[0, 0], y1)
+    assert abs(y[0, 1] - y2) <= 1e-14 * abs(y2), (y[0, 1], y2)
+    assert _rel(hf[0], h2) < 1e-15, (hf[0], h2)
+    # the same first token through the decode step
+    yy, st = orc.step(np.array([[inp["h0"]]]), [[inp["x"][0]]], [[inp["delta_raw"][0]]], A,
+                      [inp["B"][0]], [inp["C"][0]], D=[inp["D"]], z=[[inp["z"][0]]],
+                      delta_bias=[inp["delta_bias"]], delta_softplus=True)
+    assert abs(yy[0, 0] - y1) <= 1e-14 * abs(y1)
+    assert _rel(st[0, 0], h1) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# P2: A = 0 -> exp(Delta*A) = 1, the state is a cumulative sum (numpy.cumsum).
+# ---------------------------------------------------------------------------
+def pin_cumsum(orc):
+    rng = np.random.default_rng(11)
+    batch, dim, L, N = 2, 3, 50, 4
+    x = rng.integers(-3, 4, size=(batch, dim, L)).astype(np.float64)
+    dr = rng.choice([0.25, 0.5, 1.0, 2.0], size=(batch, dim, L))
+    bias = np.array([0.0, 0.5, -0.125])
+    B = rng.integers(-2, 3, size=(batch, L, N)).astype(np.float64)
+    C = rng.integers(-2, 3, size=(batch, L, N)).astype(np.float64)
+    D = np.array([1.0, -2.0, 0.5])
+    A = np.zeros((dim, N))
+    y, hf = orc.scan(x, dr, A, B, C, D=D, delta_bias=bias, delta_softplus=False)
+    delta = dr + bias[None, :, None]
+    # contributions Delta_s * x_s * B_s[n], accumulated with the library cumsum
+    contrib = (delta * x)[:, :, :, None] * B[:, None, :, :]
+    h = np.cumsum(contrib, axis=2)
+    y_ref = np.einsum("btn,bdtn->bdt", C, h) + D[None, :, None] * x
+    assert np.array_equal(y, y_ref), _rel(y, y_ref)
+    assert np.array_equal(hf, h[:, :, -1, :])
+
+
+# ---------------------------------------------------------------------------
+# P3: Delta, B, C constant -> the LTI SSM is a convolution (the S4 view).
+# ---------------------------------------------------------------------------
+def pin_lti_convolution(orc):
+    rng = np.random.default_rng(12)
+    dim, L, N = 2, 300, 6
+    A = -rng.uniform(0.2, 3.0, size=(dim, N))
+    delta_c = np.array([0.07, 0.31])          # constant step per channel (softplus off)
+    Bc = rng.standard_normal(N)
+    Cc = rng.standard_normal(N)
+    D = np.array([0.5, -1.25])
+    x = rng.standard_normal((1, dim, L))
+    B = np.tile(Bc, (1, L, 1))
+    C = np.tile(Cc, (1, L, 1))
+    dr = np.zeros((1, dim, L))
+    y, _ = orc.scan(x, dr, A, B, C, D=D, delta_bias=delta_c, delta_softplus=False)
+    k = np.arange(L)
+    for d in range(dim):
+        dl = delta_c[d]
+        # closed-form kernel K_k = sum_n C_n * Delta * B_n * exp(k * Delta * A_n)
+        K = (Cc * dl * Bc)[None, :] * np.exp(k[:, None] * dl * A[d][None, :])
+        K = K.sum(axis=1)
+        ref = np.convolve(x[0, d], K)[:L] + D[d] * x[0, d]
+        assert _rel(y[0, d], ref) < 1e-12, _rel(y[0, d], ref)
+        # and once more through an FFT convolution
+        nfft = 2 * L
+        ref_fft = np.fft.irfft(np.fft.rfft(x[0, d], nfft) * np.fft.rfft(K, nfft), nfft)[:L]
+        ref_fft += D[d] * x[0, d]
+        assert _rel(y[0, d], ref_fft) < 1e-10
+
+
+def pin_step_response(orc):
+    """N = 1, A = -1, Delta = softplus(0) = ln 2 (so r = exp(-ln 2) = 1/2), B = C = 1,
+    D = 0, x_t = 1: y_t = ln2 * sum_{k<=t} 2^-k = 2 ln2 (1 - 2^-(t+1))."""
+    with open(os.path.join(GOLDEN, "lti_step_response.json")) as f:
+        g = json.load(f)
+    L = len(g["y"])
+    y, _ = orc.scan(np.ones((1, 1, L)), np.zeros((1, 1, L)), [[-1.0]], np.ones((1, L, 1)),
+                    np.ones((1, L, 1)), delta_softplus=True)
+    ln2 = math.log(2.0)
+    for t in range(L):
+        want = 2 * ln2 * (1 - 2.0 ** -(t + 1))
+        assert abs(g["y"][t] - want) < 1e-15
+        assert abs(y[0, 0, t] - want) < 1e-14, (t, y[0, 0, t], want)
+
+
+# ---------------------------------------------------------------------------
+# P4: x = 0, h0 != 0 -> pure decay with time-varying Delta, closed form.
+# ---------------------------------------------------------------------------
+def pin_free_decay(orc):
+    rng = np.random.default_rng(13)
+    batch, dim, L, N = 2, 3, 64, 5
+    A = -rng.uniform(0.1, 4.0, size=(dim, N))
+    dr = rng.uniform(0.001, 0.2, size=(batch, dim, L))
+    bias = np.array([0.0, 0.01, 0.03])
+    h0 = rng.standard_normal((batch, dim, N))
+    C = rng.standard_normal((batch, L, N))
+    B = rng.standard_normal((batch, L, N))
+    x = np.zeros((batch, dim, L))
+    y, hf = orc.scan(x, dr, A, B, C, D=np.ones(dim), delta_bias=bias, delta_softplus=False,
+                     h0=h0)
+    S = np.cumsum(dr + bias[None, :, None], axis=2)            # sum_{s<=t} Delta_s
+    h = np.exp(A[None, :, None, :] * S[..., None]) * h0[:, :, None, :]
+    y_ref = np.einsum("btn,bdtn->bdt", C, h)
+    assert _rel(hf, h[:, :, -1, :]) < 1e-13
+    for b in range(batch):
+        for d in range(dim):
+            assert _rel(y[b, d], y_ref[b, d]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P5: brute force, the recurrence unrolled into its O(L^2) closed form.
+# ---------------------------------------------------------------------------
+def brute_force(x, dr, A, B, C, D, z, bias, softplus, h0):
+    """y_t = [sum_{s<=t} sum_n C_t[n] exp(A_n sum_{u=s+1..t} Delta_u) Delta_s B_s[n] x_s
+              + sum_n C_t[n] exp(A_n sum_{u<=t} Delta_u) h0[n] + D x_t] * silu(z_t).
+    Written from the unrolled recurrence; softplus via numpy.logaddexp, silu via
+    numpy exp -- no code shared with the oracle."""
+    batch, dim, L = x.shape
+    N = A.shape[1]
+    v = dr + (0 if bias is None else bias[None, :, None])
+    delta = np.logaddexp(0.0, v) if softplus else v
+    y = np.zeros_like(x)
+    hf = np.zeros((batch, dim, N))
+    for b in range(batch):
+        for d in range(dim):
+            S = np.concatenate([[0.0], np.cumsum(delta[b, d])])    # S[k] = sum_{u<k} Delta_u
+            hs = np.zeros(N)
+            for t in range(L):
+                # state after token t, summed term by term
+                hs = np.zeros(N)
+                for s in range(t + 1):
+                    hs += (np.exp(A[d] * (S[t + 1] - S[s + 1])) * delta[b, d, s] * B[b, s]
+                           * x[b, d, s])
+                if h0 is not None:
+                    hs += np.exp(A[d] * S[t + 1]) * h0[b, d]
+                val = float(np.dot(C[b, t], hs))
+                if D is not None:
+                    val += D[d] * x[b, d, t]
+                if z is not None:
+                    zz = z[b, d, t]
+                    val *= zz / (1.0 + np.exp(-zz))
+                y[b, d, t] = val
+            hf[b, d] = hs
+    return y, hf
+
+
+def pin_brute_force(orc):
+    rng = np.random.default_rng(14)
+    batch, dim, L, N = 2, 3, 40, 5
+    A = -rng.uniform(0.1, 3.0, size=(dim, N))
+    x = rng.standard_normal((batch, dim, L))
+    dr = rng.normal(0, 0.5, size=(batch, dim, L))
+    bias = rng.normal(-1.0, 0.5, size=dim)
+    z = rng.standard_normal((batch, dim, L)) * 2
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    D = rng.standard_normal(dim)
+    h0 = rng.standard_normal((batch, dim, N))
+    for use_z, use_D, use_h0, sp in [(True, True, True, True), (False, False, False, True),
+                                     (True, False, True, False)]:
+        dr_ = dr if sp else np.abs(dr) * 0.2
+        args = dict(D=D if use_D else None, z=z if use_z else None, delta_bias=bias if sp else None,
+                    delta_softplus=sp, h0=h0 if use_h0 else None)
+        y, hf = orc.scan(x, dr_, A, B, C, **args)
+        y_ref, hf_ref = brute_force(x, dr_, A, B, C, args["D"], args["z"], args["delta_bias"],
+                                    sp, args["h0"])
+        for b in range(batch):
+            for d in range(dim):
+                assert _rel(y[b, d], y_ref[b, d]) < 1e-11, (b, d, _rel(y[b, d], y_ref[b, d]))
+        assert _rel(hf, hf_ref) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# P6 / P7 / P8: invariants (bitwise in fp64: same operations in the same order).
+# ---------------------------------------------------------------------------
+def _rand_problem(seed, batch=2, dim=3, L=97, N=16):
+    rng = np.random.default_rng(seed)
+    return dict(
+        x=rng.standard_normal((batch, dim, L)),
+        delta=rng.normal(0, 0.1, size=(batch, dim, L)),
+        A=-np.tile(np.arange(1.0, N + 1), (dim, 1)) * rng.uniform(0.5, 1.5, size=(dim, 1)),
+        B=rng.standard_normal((batch, L, N)),
+        C=rng.standard_normal((batch, L, N)),
+        D=rng.standard_normal(dim),
+        z=rng.standard_normal((batch, dim, L)),
+        delta_bias=rng.uniform(-6.9, -2.3, size=dim),
+    )
+
+
+def pin_chunked_equals_unchunked(orc):
+    p = _rand_problem(15)
+    L = p["x"].shape[2]
+    y, hf = orc.scan(**p)
+    for L1 in (1, 37, 64, 96):
+        a = {k: (v[:, :, :L1] if k in ("x", "delta", "z") else v[:, :L1] if k in ("B", "C") else v)
+             for k, v in p.items()}
+        b_ = {k: (v[:, :, L1:] if k in ("x", "delta", "z") else v[:, L1:] if k in ("B", "C") else v)
+              for k, v in p.items()}
+        y1, h1 = orc.scan(**a)
+        y2, h2 = orc.scan(**b_, h0=h1)
+        assert np.array_equal(np.concatenate([y1, y2], axis=2), y), L1
+        assert np.array_equal(h2, hf), L1
+
+
+def pin_decode_equals_scan(orc):
+    rng = np.random.default_rng(16)
+    batch, dim, L, N = 3, 2, 10, 16           # batch >= dim on purpose
+    p = _rand_problem(16, batch=batch, dim=dim, L=L, N=N)
+    S = rng.standard_normal((batch, dim, N))
+    y, hf = orc.scan(**p, h0=S)
+    st = S.copy()
+    for t in range(L):
+        yt, st = orc.step(st, p["x"][:, :, t], p["delta"][:, :, t], p["A"], p["B"][:, t],
+                          p["C"][:, t], D=p["D"], z=p["z"][:, :, t], delta_bias=p["delta_bias"])
+        assert np.array_equal(yt, y[:, :, t]), t
+    assert np.array_equal(st, hf)
+
+
+def pin_linearity_and_causality(orc):
+    p = _rand_problem(17)
+    p.pop("z")
+    rng = np.random.default_rng(17)
+    h0 = rng.standard_normal((2, 3, 16))
+    y, hf = orc.scan(**p, h0=h0)
+    q = dict(p)
+    q["x"] = p["x"] * 8.0
+    y8, hf8 = orc.scan(**q, h0=h0 * 8.0)
+    assert np.array_equal(y8, y * 8.0) and np.array_equal(hf8, hf * 8.0)
+    # causality: a change at t0 leaves every earlier output bit-identical
+    t0 = 50
+    q = dict(p)
+    q["x"] = p["x"].copy()
+    q["x"][:, :, t0] += 1.0
+    yc, _ = orc.scan(**q, h0=h0)
+    assert np.array_equal(yc[:, :, :t0], y[:, :, :t0])
+    assert not np.array_equal(yc[:, :, t0], y[:, :, t0])
+
+
+# ---------------------------------------------------------------------------
+# P10: the element-wise functions.
+# ---------------------------------------------------------------------------
+def pin_elementwise(orc):
+    assert orc.softplus(0.0) == math.log(2.0)
+    assert orc.silu(0.0) == 0.0
+    vs = np.concatenate([np.linspace(-40, 40, 161), [-700.0, -1e-9, 1e-9, 700.0]])
+    for v in vs:
+        sp = orc.softplus(v)
+        assert abs(sp - np.logaddexp(0.0, v)) <= 4e-16 * max(1.0, abs(sp)), v
+        assert abs((orc.softplus(v) - orc.softplus(-v)) - v) <= 1e-14 * max(1.0, abs(v)), v
+        s = orc.silu(v)
+        ref = v * 0.5 * (1.0 + math.tanh(0.5 * v))   # sigma(v) = (1 + tanh(v/2)) / 2
+        assert abs(s - ref) <= 1e-15 * max(1.0, abs(v)), (v, s, ref)
+        assert abs((orc.silu(v) - orc.silu(-v)) - v) <= 1e-14 * max(1.0, abs(v)), v
+
+
+ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response,
+            pin_free_decay, pin_brute_force, pin_chunked_equals_unchunked,
+            pin_decode_equals_scan, pin_linearity_and_causality, pin_elementwise]

@@ -1,0 +1,61 @@
+"""Plants plausible mistakes in copies of the oracle source (on the CPU) and
+checks that every mutant fails at least one pin. This shows the pins would catch
+a dropped term, a wrong sign, a wrong index or a transposed operand."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC_DIR = os.path.dirname(os.path.abspath(oracle.__file__))
+
+# (name, exact text in ssm_oracle.c, replacement)
+MUTANTS = [
+    ("decay_sign", "exp(delta * a[n]) * h[n]", "exp(-delta * a[n]) * h[n]"),
+    ("euler_decay", "exp(delta * a[n]) * h[n]", "(1.0 + delta * a[n]) * h[n]"),
+    ("drop_delta_in_input", "(delta * x_t) * B_t[n]", "x_t * B_t[n]"),
+    ("input_wrong_state_index", "(delta * x_t) * B_t[n]", "(delta * x_t) * B_t[0]"),
+    ("readout_uses_B", "s += C_t[n] * h[n];", "s += B_t[n] * h[n];"),
+    ("skip_drops_x", "s += (*D_d) * x_t;", "s += (*D_d);"),
+    ("gate_is_z", "s *= ssm_oracle_silu(*z_t);", "s *= *z_t;"),
+    ("bias_dropped", "double v = delta_raw_t + (bias_d ? *bias_d : 0.0);",
+     "double v = delta_raw_t;"),
+    ("softplus_pos_branch", "return v + log1p(exp(-v));", "return log1p(exp(-v));"),
+    ("softplus_is_exp", "return log1p(exp(v));", "return exp(v);"),
+    ("silu_neg_branch", "sig = e / (1.0 + e);", "sig = 1.0 / (1.0 + e);"),
+    ("B_time_off_by_one", "const double* Bt = j->B + (b * L + t) * N;",
+     "const double* Bt = j->B + (b * L + (t > 0 ? t - 1 : 0)) * N;"),
+    ("A_indexed_by_batch", "const double* a = j->A + d * N;", "const double* a = j->A + b * N;"),
+    ("h0_ignored", "h[n] = j->h0 ? j->h0[r * N + n] : 0.0;", "h[n] = 0.0;"),
+    ("z_first_token_only", "const double* zt = j->z ? j->z + r * L + t : NULL;",
+     "const double* zt = j->z ? j->z + r * L : NULL;"),
+    ("step_B_by_channel", "A + d * dstate, B + b * dstate, C + b * dstate,",
+     "A + d * dstate, B + d * dstate, C + b * dstate,"),
+    ("readout_before_update_skip", "    /* skip term D * x, then the gate silu(z) */\n    if (D_d)",
+     "    /* skip term D * x, then the gate silu(z) */\n    if (0)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(os.path.join(SRC_DIR, "ssm_oracle.c")).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    d = tmp_path / name
+    d.mkdir()
+    shutil.copy(os.path.join(SRC_DIR, "ssm_oracle.h"), d / "ssm_oracle.h")
+    (d / "ssm_oracle.c").write_text(src.replace(old, new))
+    so = d / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+                    "-ffp-contract=off", str(d / "ssm_oracle.c"), "-o", str(so), "-lm"],
+                   check=True)
+    orc = oracle.Oracle(str(so))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
