@@ -1,0 +1,154 @@
+/*
+ * ssm_scan.h - C ABI of libssmscan, the MI355X (gfx950) selective scan.
+ *
+ * The operation (per batch b, channel d, state n; t = 0..L-1):
+ *
+ *   Delta_t  = softplus(delta[b,d,t] + delta_bias[d])   (or no softplus, see flag)
+ *   h_t[n]   = exp(Delta_t * A[d,n]) * h_{t-1}[n] + Delta_t * B[b,t,n] * x[b,d,t]
+ *   y[b,d,t] = (sum_n C[b,t,n] * h_t[n] + D[d] * x[b,d,t]) * silu(z[b,d,t])
+ *
+ * with h_{-1} = h0 (zeros when h0 is NULL); D and z are optional.
+ * Where this comes from on the pages:
+ *  - the continuous SSM h' = Ah + Bu, y = Ch + Du with D as a skip term:
+ *    "State-Space Models (SSMs) & Mamba" (aidatadrop), section "State-Space
+ *    Models (SSMs): A Resurgent Paradigm for Sequence Modeling";
+ *  - B, C and the step Delta depend on the token, A and D do not: "Mamba: How
+ *    Selective State Spaces Achieve 5x Faster Inference Than Transformers"
+ *    (promptingindex), section "The selective mechanism: input-dependent SSM
+ *    parameters"; aidatadrop, section "The Magic of Selective Scan";
+ *  - the discretized recurrence is run per token and the output is read after the
+ *    update; the scan output is gated by SiLU of the second branch: "Mamba
+ *    Architecture Explained: Why Transformers Aren't the Final Word" (sivaro),
+ *    sections "The Mamba Innovation: Selective State Updates" and "The
+ *    Architecture in Practice". The pages print no discretization formula;
+ *    exp(Delta*A) and Delta*B*x, softplus and the bias are the readings this
+ *    library takes.
+ *  - recurrent inference, one token at a time with a state of fixed size:
+ *    promptingindex, "The selective mechanism"; aidatadrop, "The Payoff".
+ *
+ * Conventions for every entry point:
+ *  - Every buffer pointer is a DEVICE pointer owned by the caller; the library
+ *    allocates nothing and keeps no state between calls except a thread-local error
+ *    string. Calls on different streams may run concurrently.
+ *  - Buffers are dense, row-major, in the shapes given below. x, delta, z, y,
+ *    B and C are in `io_dtype`; A, D, delta_bias, h0, h_final and state are fp32.
+ *    Base pointers must be 16-byte aligned (4-byte for D and delta_bias);
+ *    otherwise SSM_ERR_UNSUPPORTED is returned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued asynchronously; results are valid once the stream is synchronized.
+ *  - Arguments are validated on the host before anything is launched. On any
+ *    status other than SSM_OK nothing was launched and no buffer was touched;
+ *    ssm_last_error() describes why. A device fault surfaces at the caller's next
+ *    synchronization. No C++ exception crosses this interface.
+ *  - Outputs are deterministic for a given shape and plan (no float atomics).
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, size <= 0, overlap, bad flag  */
+    SSM_ERR_UNSUPPORTED = 2,        /* dstate != 16, misaligned buffer                      */
+    SSM_ERR_WORKSPACE_TOO_SMALL = 3,/* workspace NULL or smaller than the query returned    */
+    SSM_ERR_HIP = 4                 /* a HIP launch failed; ssm_last_error() has the text   */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* Plan selection, for tests and tuning. Pass NULL for the library's choice. */
+typedef struct {
+    int64_t chunk_len;  /* tokens per chunk in the chunked plan; 0 = library choice.
+                           Must be a positive multiple of 32 when set.                 */
+    int32_t plan;       /* 0 = library choice, 1 = single pass (one sweep over L per
+                           channel group), 2 = chunked (per-chunk end states, a carry
+                           pass over chunks, then the chunks again with their carried-in
+                           state).                                                       */
+    int32_t group_channels; /* channels per workgroup: 0 = library choice, else one of
+                           32, 48, 64, 80, 96 (all 16 states of a channel stay in one
+                           workgroup; 2 states per lane, group_channels/8 waves)        */
+    void* timing_begin; /* hipEvent_t or NULL: recorded on `stream` right before the
+                           launch of the scan kernel that writes y                     */
+    void* timing_end;   /* hipEvent_t or NULL: recorded right after that launch        */
+} ssm_scan_options;
+
+/*
+ * Workspace bytes that ssm_scan_fwd needs for this shape (and plan, when opts is
+ * not NULL). Returns 0 for an invalid shape. The caller allocates it (any device
+ * allocation, 16-byte aligned) and may reuse it across calls on the same stream.
+ * Layout, with Lp = seqlen rounded up to a multiple of 32 and K chunks:
+ *   [0, batch*4*Lp*32 bytes)  B and C widened to fp32, per state quad q:
+ *                             [batch][q][Lp][B[4q..4q+3], C[4q..4q+3]]
+ *   then (256-byte aligned, chunked plan only) [batch*dim][K][16] fp32: after the
+ *   call, the state entering each chunk (h0 or zeros for chunk 0);
+ *   then (256-byte aligned) [batch*dim][K] fp32: the sum of Delta over each chunk.
+ */
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                ssm_dtype io_dtype, const ssm_scan_options* opts);
+
+/*
+ * Forward selective scan over a whole sequence (the parallel training /
+ * prefill form: promptingindex, "The selective mechanism"; aidatadrop,
+ * "Hardware-Aware Parallelism: The Secret Sauce").
+ *
+ *   x          [batch][dim][seqlen]    io_dtype   input u
+ *   delta      [batch][dim][seqlen]    io_dtype   raw step (before bias / softplus)
+ *   A          [dim][dstate]           fp32       diagonal state matrix per channel
+ *   B, C       [batch][seqlen][dstate] io_dtype   per-token, shared by all channels
+ *   D          [dim] fp32 or NULL (no skip term)
+ *   z          [batch][dim][seqlen] io_dtype or NULL (no gate)
+ *   delta_bias [dim] fp32 or NULL (zero)
+ *   delta_softplus  1: Delta = softplus(delta + bias); 0: Delta = delta + bias
+ *   h0         [batch][dim][dstate] fp32 or NULL (zero initial state)
+ *   y          [batch][dim][seqlen] io_dtype out; must not overlap any other buffer
+ *   h_final    [batch][dim][dstate] fp32 out (the state after the last token) or
+ *              NULL. It may be exactly h0 (in-place resume) but not partly overlap it.
+ *   workspace  device buffer of at least ssm_scan_workspace_bytes(...) bytes
+ *   opts       plan options or NULL
+ * batch, seqlen, dim >= 1; dstate must be 16.
+ */
+ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z,
+                        const float* delta_bias, int delta_softplus, const float* h0,
+                        void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
+                        int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                        size_t workspace_bytes, const ssm_scan_options* opts, void* stream);
+
+/*
+ * One recurrent decode step: one token for every (batch, channel), the state
+ * updated in place (constant memory per step: promptingindex, "The selective
+ * mechanism"; aidatadrop, "The Payoff").
+ *
+ *   state      [batch][dim][dstate] fp32 in: h_{t-1}, out: h_t
+ *   x, delta   [batch][dim]          io_dtype
+ *   A          [dim][dstate]         fp32
+ *   B, C       [batch][dstate]       io_dtype
+ *   D, z, delta_bias, delta_softplus  as for ssm_scan_fwd (z is [batch][dim])
+ *   y          [batch][dim]          io_dtype out; must not overlap any other buffer
+ * batch, dim >= 1; dstate must be 16.
+ */
+ssm_status ssm_state_update(float* state, const void* x, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z,
+                            const float* delta_bias, int delta_softplus, void* y,
+                            int64_t batch, int64_t dim, int64_t dstate, ssm_dtype io_dtype,
+                            void* stream);
+
+/* Static text for a status code ("ok", "invalid argument", ...). */
+const char* ssm_status_string(ssm_status s);
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char* ssm_last_error(void);
+/* SSM_SCAN_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,185 @@
+"""ctypes binding of libssmscan (include/ssm_scan.h), same entry-point names.
+
+Argument marshalling only: every step of the scan runs in the library's HIP
+kernels. torch provides device memory (outputs and the workspace are
+torch.empty allocations) and the stream. There is no CPU fallback: without the
+built library, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssmscan.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it first with "
+        "`python -m selective_state_space_53_amd.build` (or __graft_entry__.build())")
+
+SSM_OK, SSM_ERR_INVALID_ARGUMENT, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE_TOO_SMALL, \
+    SSM_ERR_HIP = range(5)
+SSM_F32, SSM_BF16 = 0, 1
+EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
+           "ssm_status_string", "ssm_last_error", "ssm_abi_version")
+
+
+class ScanOptions(ctypes.Structure):
+    _fields_ = [("chunk_len", ctypes.c_int64), ("plan", ctypes.c_int32),
+                ("group_channels", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
+                ("timing_end", ctypes.c_void_p)]
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+lib = ctypes.CDLL(_LIB_PATH)
+lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
+lib.ssm_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
+                                         ctypes.POINTER(ScanOptions)]
+lib.ssm_scan_fwd.restype = ctypes.c_int
+lib.ssm_scan_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                             _i64, _i64, _i64, _i64, ctypes.c_int, _vp, ctypes.c_size_t,
+                             ctypes.POINTER(ScanOptions), _vp]
+lib.ssm_state_update.restype = ctypes.c_int
+lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                 _i64, _i64, _i64, ctypes.c_int, _vp]
+lib.ssm_status_string.restype = ctypes.c_char_p
+lib.ssm_status_string.argtypes = [ctypes.c_int]
+lib.ssm_last_error.restype = ctypes.c_char_p
+lib.ssm_last_error.argtypes = []
+lib.ssm_abi_version.restype = ctypes.c_int
+lib.ssm_abi_version.argtypes = []
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{lib.ssm_status_string(status).decode()}: "
+                         f"{lib.ssm_last_error().decode()}")
+
+
+def _check(status: int):
+    if status != SSM_OK:
+        raise SSMError(status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    if t.dtype == torch.float32:
+        return SSM_F32
+    raise TypeError(f"io tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0):
+    if plan == 0 and chunk_len == 0 and events is None and group_channels == 0:
+        return None
+    ev0, ev1 = (None, None) if events is None else events
+    return ctypes.byref(ScanOptions(chunk_len, plan, group_channels, ev0, ev1))
+
+
+def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
+                             group_channels=0) -> int:
+    return lib.ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype,
+                                        _options(plan, chunk_len, None, group_channels))
+
+
+def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 h0=None, return_final_state=False, y=None, h_final=None, workspace=None,
+                 plan=0, chunk_len=0, stream=None, timing_events=None, group_channels=0):
+    """x, delta, z: [batch][dim][seqlen]; B, C: [batch][seqlen][16]; A: [dim][16];
+    D, delta_bias: [dim]; h0: [batch][dim][16]. Returns y (and h_final).
+    timing_events: optional (begin, end) pair of raw hipEvent_t handles (ints) that
+    the library records around the launch of the scan kernel that writes y."""
+    _dev(x, "x")
+    io = x.dtype
+    batch, dim, seqlen = x.shape
+    N = A.shape[-1]
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(A, "A", torch.float32, (dim, N))
+    _dev(B, "B", io, (batch, seqlen, N))
+    _dev(C, "C", io, (batch, seqlen, N))
+    _dev(D, "D", torch.float32, (dim,))
+    _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    _dev(h0, "h0", torch.float32, (batch, dim, N))
+    code = _dtype_code(x)
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", io, x.shape)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _dev(h_final, "h_final", torch.float32, (batch, dim, N))
+    opts = _options(plan, chunk_len, timing_events, group_channels)
+    ws_bytes = lib.ssm_scan_workspace_bytes(batch, seqlen, dim, N, code, opts)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        _check(lib.ssm_scan_fwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, N,
+            code, _ptr(workspace), 0 if workspace is None else workspace.numel(), opts, s))
+    return (y, h_final) if return_final_state else y
+
+
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                     delta_softplus=True, y=None, stream=None):
+    """state: [batch][dim][16] fp32, updated in place; x, delta, z: [batch][dim];
+    B, C: [batch][16]. Returns y [batch][dim]."""
+    _dev(x, "x")
+    io = x.dtype
+    batch, dim = x.shape
+    N = A.shape[-1]
+    _dev(state, "state", torch.float32, (batch, dim, N))
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(A, "A", torch.float32, (dim, N))
+    _dev(B, "B", io, (batch, N))
+    _dev(C, "C", io, (batch, N))
+    _dev(D, "D", torch.float32, (dim,))
+    _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", io, x.shape)
+    dev = x.device
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        _check(lib.ssm_state_update(
+            _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), batch, dim, N,
+            _dtype_code(x), s))
+    return y
+
+
+def ssm_status_string(status: int) -> str:
+    return lib.ssm_status_string(status).decode()
+
+
+def ssm_last_error() -> str:
+    return lib.ssm_last_error().decode()
+
+
+def ssm_abi_version() -> int:
+    return lib.ssm_abi_version()

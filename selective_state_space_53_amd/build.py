@@ -1,0 +1,65 @@
+"""Builds libssmscan.so (the gfx950 selective-scan library) in this folder.
+
+    python -m selective_state_space_53_amd.build
+
+hipcc compiles the kernels for gfx950 only. Packed-FP32 instruction selection is
+switched off (`-packed-fp32-ops`); hipcc's host pass warns that it does not know
+that feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libssmscan.so")
+ARCH = "gfx950"
+
+DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{msg}")
+    if msg.strip() and verbose:
+        print(msg)
+
+
+def build(verbose: bool = False, save_temps: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
+    k_obj = os.path.join(BUILD_DIR, "ssm_kernels.o")
+    a_obj = os.path.join(BUILD_DIR, "ssm_abi.o")
+    extra = []
+    if save_temps:
+        extra = ["--save-temps"]
+    cwd = os.getcwd()
+    try:
+        os.chdir(BUILD_DIR)  # --save-temps writes next to the working directory
+        _run(["hipcc", "-c", *DEVICE_FLAGS, *inc, *extra,
+              os.path.join(CSRC, "ssm_kernels.hip"), "-o", k_obj], verbose)
+    finally:
+        os.chdir(cwd)
+    _run(["hipcc", "-c", *HOST_FLAGS, *inc, os.path.join(CSRC, "ssm_abi.cpp"), "-o", a_obj],
+         verbose)
+    tmp = LIB + ".tmp"
+    _run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", k_obj, a_obj, "-o", tmp],
+         verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, save_temps="--save-temps" in sys.argv))

@@ -1,0 +1,63 @@
+// ssm_internal.h - shared between the C ABI (ssm_abi.cpp) and the kernels
+// (ssm_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr int kDState = 16;        // states per channel supported by the kernels
+constexpr int kTokenTile = 32;     // tokens per scan tile (chunk lengths are multiples)
+
+struct ScanPlan {
+    int group_channels = 64;  // channels per scan workgroup (32, 48, 64, 80 or 96)
+    int64_t ngroups = 0;      // batch * ceil(dim / group_channels)
+    int nchunks = 1;        // 1 = single pass
+    int64_t chunk_len = 0;  // tokens per chunk (== seqlen for a single pass)
+    size_t ws_bcq = 0;      // workspace byte offsets / sizes
+    size_t ws_state = 0;
+    size_t ws_sum = 0;
+    size_t ws_total = 0;
+};
+
+struct ScanParams {
+    const void* x;
+    const void* delta;
+    const void* z;
+    void* y;
+    const float* A;
+    const float* D;
+    const float* bias;
+    const float* h0;
+    float* h_final;
+    float* bcq;          // [batch][8][lpad][4] fp32: B and C widened, per state pair
+    float* chunk_state;  // [batch*dim][nchunks][16] (chunked plan) or null
+    float* chunk_sum;    // [batch*dim][nchunks]
+    int64_t batch, seqlen, dim, lpad, chunk_len;
+    int32_t nchunks, ngroups, groups_per_batch, chunk_offset;
+    int32_t softplus, aligned;
+};
+
+struct DecodeParams {
+    float* state;
+    const void* x;
+    const void* delta;
+    const void* z;
+    void* y;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* bias;
+    int64_t batch, dim;
+    int32_t softplus;
+};
+
+// ev_begin / ev_end (may be null) are recorded around the launch of the scan kernel
+// that writes y.
+hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* B, const void* C,
+                       bool bf16, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream);
+
+}  // namespace ssm

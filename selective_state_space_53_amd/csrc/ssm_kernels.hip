@@ -1,0 +1,545 @@
+// ssm_kernels.hip - gfx950 kernels of the selective scan and its decode step.
+//
+// The recurrence (per batch b, channel d, state n, token t):
+//   Delta = softplus(delta_raw + bias[d]);  h[n] = exp(Delta*A[d,n])*h[n] + Delta*x*B_t[n]
+//   y     = (sum_n C_t[n]*h[n] + D[d]*x) * silu(z)
+// State and output equations: "State-Space Models (SSMs) & Mamba" (aidatadrop),
+// section "State-Space Models (SSMs): A Resurgent Paradigm for Sequence Modeling".
+// Input-dependent B, C, Delta: "Mamba: How Selective State Spaces Achieve 5x
+// Faster Inference Than Transformers", section "The selective mechanism".
+// Update-then-read and the SiLU gate: "Mamba Architecture Explained", sections
+// "The Mamba Innovation: Selective State Updates" and "The Architecture in Practice".
+//
+// How the work maps onto CDNA4 (the pages' SRAM-tiled CUDA scan, in "The
+// convolution trick is gone" of the creativeworksofknowledge Mamba lesson, is prior
+// art; what carries over is "keep the state on chip, stream the sequence once,
+// write back only boundary states"):
+//
+//  * A workgroup owns 64 channels of one batch row and all 16 states: four waves,
+//    wave w holding states 4w..4w+3 of all 64 channels, one channel per lane. Each
+//    lane keeps its 4 states in VGPRs for the whole sequence (or chunk). B_t and C_t
+//    do not depend on the channel, so for a wave they are uniform: they arrive by
+//    scalar loads and enter the VALU ops as SGPR operands.
+//  * The sequence is streamed in tiles of 32 tokens. Per tile: (pre) each wave
+//    computes softplus(Delta), Delta*x and the gate for 8 of the 32 tokens of all
+//    64 channels and shares Delta and Delta*x through LDS; (core) each wave runs the
+//    recurrence over the 32 tokens for its 4 states and writes the partial readout
+//    sum_{its 4 n} C*h to LDS; (post) each wave adds the four partials of its 8
+//    tokens, applies D*x and the gate, and stores y. Every (t, d) element-wise
+//    step is done once, every (t, d, n) step once.
+//  * Long sequences with few channel groups are cut into chunks (the tiles-with-
+//    final-state idea of the pages' kernel): pass 1 runs each chunk from a zero state
+//    and writes only its end state and sum of Delta, a carry pass composes them in
+//    chunk order, and pass 2 reruns every chunk from its carried-in state.
+// No MFMA: there is no dense contraction here; the bound is the VALU (one exp per
+// (t, d, n)) with HBM traffic of ~8 bytes per (t, d) in bf16.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- element-wise
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
+__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// softplus(v) = max(v, 0) + log1p(e^-|v|). log1p(e) is taken as log(w) + (e - (w - 1))
+// with w = 1 + e rounded: the second term restores what the rounding of 1 + e lost
+// (w - 1 is exact for w in [1, 2]), so small e keeps full relative accuracy.
+__device__ __forceinline__ float softplus_f(float v) {
+    const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+    const float w = 1.0f + e;
+    const float r = e - (w - 1.0f);
+    const float lp = __builtin_fmaf(fast_log2(w), kLn2, r);
+    return __builtin_fmaxf(v, 0.0f) + lp;
+}
+
+// silu(z) = z / (1 + e^-z); for z -> -inf the exp overflows to inf, rcp gives 0.
+__device__ __forceinline__ float silu_f(float z) {
+    return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // RNE
+}
+__device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_one(uint16_t* p, float v) {
+    *p = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Four consecutive tokens of one row, kept raw in registers between the load
+// (issued one tile ahead) and the use. `vec` = the 4 tokens are in range and the
+// address is aligned (one 8- or 16-byte load); otherwise `n` (<= 4) valid tokens are
+// read one by one and the rest are zero.
+template <typename IO> struct Raw4;
+template <> struct Raw4<uint16_t> {
+    uint32_t w[2];
+    __device__ __forceinline__ void load(const uint16_t* p, bool vec, int n) {
+        if (vec) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t lo = (2 * k < n) ? p[2 * k] : 0u;
+                const uint32_t hi = (2 * k + 1 < n) ? p[2 * k + 1] : 0u;
+                w[k] = lo | (hi << 16);
+            }
+        }
+    }
+    __device__ __forceinline__ void zero() { w[0] = w[1] = 0u; }
+    __device__ __forceinline__ void widen(float* o) const {
+        o[0] = bf16_lo(w[0]); o[1] = bf16_hi(w[0]);
+        o[2] = bf16_lo(w[1]); o[3] = bf16_hi(w[1]);
+    }
+};
+template <> struct Raw4<float> {
+    float v[4];
+    __device__ __forceinline__ void load(const float* p, bool vec, int n) {
+        if (vec) {
+            const float4 a = *reinterpret_cast<const float4*>(p);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = (k < n) ? p[k] : 0.0f;
+        }
+    }
+    __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = 0.0f; }
+    __device__ __forceinline__ void widen(float* o) const {
+        o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+    }
+};
+
+template <typename IO> struct Store4;
+template <> struct Store4<uint16_t> {
+    __device__ __forceinline__ static void store(uint16_t* p, bool vec, int n, const float* v) {
+        if (vec) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]),
+                                                      pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k < n) store_one(p + k, v[k]);
+        }
+    }
+};
+template <> struct Store4<float> {
+    __device__ __forceinline__ static void store(float* p, bool vec, int n, const float* v) {
+        if (vec) {
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k < n) p[k] = v[k];
+        }
+    }
+};
+
+// ------------------------------------------------------------- B/C widening pass
+// bcq[b][p][t][0..3] = (B[b][t][2p], B[b][t][2p+1], C[b][t][2p], C[b][t][2p+1]) in fp32
+// for t < seqlen; zero for the padding tokens up to lpad (a multiple of the tile).
+// One thread per (b, t, state pair p).
+template <typename IO>
+__global__ __launch_bounds__(256) void bc_widen_kernel(const IO* __restrict__ B,
+                                                       const IO* __restrict__ C,
+                                                       float* __restrict__ bcq, int64_t batch,
+                                                       int64_t seqlen, int64_t lpad) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = batch * lpad * 8;
+    if (i >= total) return;
+    const int pr = (int)(i & 7);
+    const int64_t bt = i >> 3;
+    const int64_t b = bt / lpad;
+    const int64_t t = bt - b * lpad;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < seqlen) {
+        const IO* pb = B + (b * seqlen + t) * kDState + 2 * pr;
+        const IO* pc = C + (b * seqlen + t) * kDState + 2 * pr;
+        o = make_float4(to_f32(pb[0]), to_f32(pb[1]), to_f32(pc[0]), to_f32(pc[1]));
+    }
+    *reinterpret_cast<float4*>(bcq + ((b * 8 + pr) * lpad + t) * 4) = o;
+}
+
+// --------------------------------------------------------------------- the scan
+constexpr int kTile = 32;                 // tokens per tile
+constexpr int kLdsRow = kTile + 4;        // padded [channel][token] LDS row (floats)
+constexpr int kBcTile = 8 * kTile * 4;    // floats of widened B/C per tile (8 state pairs)
+
+// One workgroup = CG channels (a multiple of 16) of one batch row x all 16 states,
+// CG*8 threads = CG/8 waves.
+//  core mapping: each 16-lane row holds one state pair p (states 2p, 2p+1) of 16
+//    consecutive channels; lane = channel. B and C of the row's pair come from LDS
+//    with one row-uniform 16-byte read per token.
+//  pre/post mapping: thread t = (channel t/8, token quad t%8) of the 32-token tile, so
+//    the 8 threads of a channel read and write 64 contiguous bytes (bf16).
+// Per tile:
+//  pre : widen x, delta, z (loaded one tile earlier), Delta = softplus(delta + bias),
+//        u = Delta*x -> LDS; keep D*x and silu(z) for post
+//  core: 32 tokens of the recurrence for the lane's (channel, state pair); partial
+//        readouts C*h of the pair -> LDS
+//  post: sum the 8 pairs' partials, add D*x, gate, store y
+// LOCAL = pass 1 of the chunked plan: start from zero, write only the chunk's end
+// state and its sum of Delta. Otherwise: outputs y (and h_final).
+template <typename IO, bool LOCAL, int CG>
+__global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
+    static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
+    constexpr int kRowsPerPair = CG / 16;
+    __shared__ float sD[CG * kLdsRow];
+    __shared__ float sU[CG * kLdsRow];
+    __shared__ float sP[LOCAL ? 4 : 8 * CG * kLdsRow];
+    __shared__ float sBC[2 * kBcTile];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int g = blockIdx.x % p.ngroups;
+    const int c = blockIdx.x / p.ngroups + p.chunk_offset;
+    const int64_t b = g / p.groups_per_batch;
+    const int64_t d0 = (int64_t)(g % p.groups_per_batch) * CG;
+    const int64_t t_beg = (int64_t)c * p.chunk_len;
+    const int64_t t_end = (t_beg + p.chunk_len < p.seqlen) ? t_beg + p.chunk_len : p.seqlen;
+    const int ntiles = (int)((t_end - t_beg + kTile - 1) / kTile);
+
+    // core mapping: 16-lane row r -> state pair pr, channel block
+    const int r = tid >> 4;
+    const int pr = r / kRowsPerPair;
+    const int cc = (r % kRowsPerPair) * 16 + (tid & 15);      // channel within the group
+    const int64_t d = d0 + cc;
+    const bool valid = d < p.dim;
+    const int64_t row = b * p.dim + d;
+    // pre/post mapping: (channel cq, token quad jq)
+    const int cq = tid >> 3;
+    const int jq = tid & 7;
+    const int64_t dq = d0 + cq;
+    const bool validq = dq < p.dim;
+    const int64_t rowq = b * p.dim + dq;
+
+    float a2[2], h[2];
+    {
+        float2 av = make_float2(0.f, 0.f), hv = av;
+        if (valid) {
+            av = *reinterpret_cast<const float2*>(p.A + d * kDState + 2 * pr);
+            if (!LOCAL) {
+                if (p.chunk_state)
+                    hv = *reinterpret_cast<const float2*>(
+                        p.chunk_state + (row * p.nchunks + c) * kDState + 2 * pr);
+                else if (p.h0)
+                    hv = *reinterpret_cast<const float2*>(p.h0 + row * kDState + 2 * pr);
+            }
+        }
+        a2[0] = av.x * kLog2e;
+        a2[1] = av.y * kLog2e;
+        h[0] = hv.x;
+        h[1] = hv.y;
+    }
+    const float bias = (validq && p.bias) ? p.bias[dq] : 0.0f;
+    const float Dd = (validq && p.D) ? p.D[dq] : 0.0f;
+    const IO* xr = static_cast<const IO*>(p.x) + rowq * p.seqlen;
+    const IO* dr = static_cast<const IO*>(p.delta) + rowq * p.seqlen;
+    const IO* zr = (!LOCAL && p.z) ? static_cast<const IO*>(p.z) + rowq * p.seqlen : nullptr;
+    IO* yr = LOCAL ? nullptr : static_cast<IO*>(p.y) + rowq * p.seqlen;
+    // B/C staging: the first 256 threads each move 16 bytes (one token of one pair)
+    const bool bc_mover = tid < 256;
+    const float* bcsrc = p.bcq + ((b * 8 + (tid >> 5)) * p.lpad + (tid & 31)) * 4;
+    float* const bcdst = sBC + tid * 4;
+    float dsum = 0.0f;
+
+    float* const myDq = sD + cq * kLdsRow + 4 * jq;   // pre: this thread's 4 tokens
+    float* const myUq = sU + cq * kLdsRow + 4 * jq;
+    const float* const coreD = sD + cc * kLdsRow;     // core: the lane's channel
+    const float* const coreU = sU + cc * kLdsRow;
+
+    Raw4<IO> rx, rdl, rz;
+    float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto load_tile = [&](int ti) {
+        const int64_t t0 = t_beg + (int64_t)ti * kTile;
+        const int nvalid = (t_end - t0 < kTile) ? (int)(t_end - t0) : kTile;
+        const int nq = nvalid - 4 * jq;
+        const bool vec = p.aligned && nvalid == kTile;
+        if (validq) {
+            rx.load(xr + t0 + 4 * jq, vec, nq);
+            rdl.load(dr + t0 + 4 * jq, vec, nq);
+            if (zr) rz.load(zr + t0 + 4 * jq, vec, nq);
+        }
+        if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
+    };
+    rx.zero();
+    rdl.zero();
+    rz.zero();
+    load_tile(0);
+    if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
+
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int64_t t0 = t_beg + (int64_t)ti * kTile;
+        const int nvalid = (t_end - t0 < kTile) ? (int)(t_end - t0) : kTile;
+        const int nq = nvalid - 4 * jq;            // valid tokens of this thread's 4 (may be <= 0)
+        const bool vec = p.aligned && nvalid == kTile;
+        // ---- pre: widen this tile's raw tokens, then start loading the next tile
+        float xv[4], dv[4], zv[4];
+        rx.widen(xv);
+        rdl.widen(dv);
+        if (!LOCAL) rz.widen(zv);
+        if (ti + 1 < ntiles) load_tile(ti + 1);
+        float dl[4], uu[4], post_a[4], post_g[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float v = dv[k] + bias;
+            float delta = p.softplus ? softplus_f(v) : v;
+            delta = (k < nq) ? delta : 0.0f;   // padding tokens: exp(0) = 1, no input
+            dl[k] = delta;
+            uu[k] = delta * xv[k];
+        }
+        if (!LOCAL) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                post_g[k] = zr ? silu_f(zv[k]) : 1.0f;
+                post_a[k] = Dd * xv[k];
+            }
+        }
+        *reinterpret_cast<float4*>(myDq) = make_float4(dl[0], dl[1], dl[2], dl[3]);
+        *reinterpret_cast<float4*>(myUq) = make_float4(uu[0], uu[1], uu[2], uu[3]);
+        __syncthreads();
+
+        // ---- core: the recurrence over the 32 tokens for (channel cc, states 2pr, 2pr+1).
+        // Every lane of a row reads the same (B0, B1, C0, C1) of a token from LDS, so B
+        // and C arrive in VGPRs and every op below is a plain VOP2 with VGPR operands
+        // (the fast FP32 issue path; SGPR or DPP operands halve it).
+        const float* bct = sBC + (ti & 1) * kBcTile + pr * (kTile * 4);
+        float* const pout = sP + (pr * CG + cc) * kLdsRow;
+#pragma unroll
+        for (int tq = 0; tq < kTile; tq += 4) {
+            const float4 D4 = *reinterpret_cast<const float4*>(coreD + tq);
+            const float4 U4 = *reinterpret_cast<const float4*>(coreU + tq);
+            const float4 q0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
+            const float4 q1 = *reinterpret_cast<const float4*>(bct + (tq + 1) * 4);
+            const float4 q2 = *reinterpret_cast<const float4*>(bct + (tq + 2) * 4);
+            const float4 q3 = *reinterpret_cast<const float4*>(bct + (tq + 3) * 4);
+            float pp[4];
+#define SSM_TOKEN(S, DS, US, Q)                                                       \
+    {                                                                                 \
+        const float e0 = fast_exp2(DS * a2[0]);                                       \
+        const float e1 = fast_exp2(DS * a2[1]);                                       \
+        h[0] = __builtin_fmaf(e0, h[0], Q.x * US);                                    \
+        h[1] = __builtin_fmaf(e1, h[1], Q.y * US);                                    \
+        if (!LOCAL) pp[S] = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                    \
+        else if (pr == 0) dsum += DS;                                                 \
+    }
+            SSM_TOKEN(0, D4.x, U4.x, q0)
+            SSM_TOKEN(1, D4.y, U4.y, q1)
+            SSM_TOKEN(2, D4.z, U4.z, q2)
+            SSM_TOKEN(3, D4.w, U4.w, q3)
+#undef SSM_TOKEN
+            if (!LOCAL)
+                *reinterpret_cast<float4*>(pout + tq) = make_float4(pp[0], pp[1], pp[2], pp[3]);
+        }
+        __syncthreads();
+
+        // ---- post: this thread's 4 tokens: sum the 8 pairs' partials, skip, gate, store
+        if (!LOCAL) {
+            float yv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float4 a = *reinterpret_cast<const float4*>(sP + (q * CG + cq) * kLdsRow + 4 * jq);
+                yv[0] += a.x; yv[1] += a.y; yv[2] += a.z; yv[3] += a.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) yv[k] = (yv[k] + post_a[k]) * post_g[k];
+            if (validq && nq > 0) Store4<IO>::store(yr + t0 + 4 * jq, vec, nq, yv);
+        }
+        // the next tile's B/C into the other LDS buffer (its last readers finished
+        // before the barrier above; its next readers come after the next barrier)
+        if (bc_mover && ti + 1 < ntiles)
+            *reinterpret_cast<float4*>(bcdst + ((ti + 1) & 1) * kBcTile) = rbc;
+    }
+
+    if (!valid) return;
+    if (LOCAL) {
+        *reinterpret_cast<float2*>(p.chunk_state + (row * p.nchunks + c) * kDState + 2 * pr) =
+            make_float2(h[0], h[1]);
+        if (pr == 0) p.chunk_sum[row * p.nchunks + c] = dsum;
+    } else if (p.h_final && c == p.nchunks - 1) {
+        *reinterpret_cast<float2*>(p.h_final + row * kDState + 2 * pr) = make_float2(h[0], h[1]);
+    }
+}
+
+// ------------------------------------------------------------------ chunk carry
+// One thread per (row, n). In chunk order: the carried-in state of chunk c is
+// written over chunk_state[c]; then h <- exp(A*sum_c Delta)*h + local end state of c.
+__global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A,
+                                                    const float* __restrict__ h0,
+                                                    float* __restrict__ chunk_state,
+                                                    const float* __restrict__ chunk_sum,
+                                                    int64_t nrows, int64_t dim, int nchunks) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nrows * kDState) return;
+    const int64_t row = i / kDState;
+    const int n = (int)(i % kDState);
+    const int64_t d = row % dim;
+    const float a2 = A[d * kDState + n] * kLog2e;
+    float h = h0 ? h0[row * kDState + n] : 0.0f;
+    float* st = chunk_state + row * (int64_t)nchunks * kDState + n;
+    const float* sm = chunk_sum + row * (int64_t)nchunks;
+    // chunks 0..K-2 have a local end state and a sum of Delta; the last chunk only
+    // receives its carried-in state
+    for (int c = 0; c < nchunks - 1; ++c) {
+        const float loc = st[(int64_t)c * kDState];
+        const float S = sm[c];
+        st[(int64_t)c * kDState] = h;
+        h = __builtin_fmaf(fast_exp2(a2 * S), h, loc);
+    }
+    st[(int64_t)(nchunks - 1) * kDState] = h;
+}
+
+// ----------------------------------------------------------------- decode step
+// Lane = (channel row, state quad j): a wave covers 16 rows x 16 states, i.e. 1 KB of
+// contiguous state, read and written with 16-byte accesses. The 4 lanes of a quad
+// each evaluate the per-token scalars (cheap next to the state traffic) and reduce
+// the readout with two DPP adds.
+template <typename IO>
+__global__ __launch_bounds__(256) void state_update_kernel(const DecodeParams p) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t grow = tid >> 2;           // b * dim + d
+    const int j = (int)(tid & 3);
+    if (grow >= p.batch * p.dim) return;     // whole quads leave together
+    const int64_t b = grow / p.dim;
+    const int64_t d = grow - b * p.dim;
+
+    float4 hv = *reinterpret_cast<const float4*>(p.state + grow * kDState + 4 * j);
+    const float4 av = *reinterpret_cast<const float4*>(p.A + d * kDState + 4 * j);
+    const IO* xp = static_cast<const IO*>(p.x);
+    const IO* dp = static_cast<const IO*>(p.delta);
+    const IO* Bp = static_cast<const IO*>(p.B) + b * kDState + 4 * j;
+    const IO* Cp = static_cast<const IO*>(p.C) + b * kDState + 4 * j;
+    const float xv = to_f32(xp[grow]);
+    const float v = to_f32(dp[grow]) + (p.bias ? p.bias[d] : 0.0f);
+    const float delta = p.softplus ? softplus_f(v) : v;
+    const float u = delta * xv;
+    float Bv[4], Cv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        Bv[k] = to_f32(Bp[k]);
+        Cv[k] = to_f32(Cp[k]);
+    }
+    float hh[4] = {hv.x, hv.y, hv.z, hv.w};
+    const float aa[4] = {av.x, av.y, av.z, av.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        hh[k] = __builtin_fmaf(fast_exp2(delta * aa[k] * kLog2e), hh[k], u * Bv[k]);
+        acc = __builtin_fmaf(Cv[k], hh[k], acc);
+    }
+    *reinterpret_cast<float4*>(p.state + grow * kDState + 4 * j) =
+        make_float4(hh[0], hh[1], hh[2], hh[3]);
+    // quad sum: lanes j^1 then j^2 (quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E)
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, false));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, false));
+    if (j == 0) {
+        float s = acc + (p.D ? p.D[d] * xv : 0.0f);
+        if (p.z) s *= silu_f(to_f32(static_cast<const IO*>(p.z)[grow]));
+        store_one(static_cast<IO*>(p.y) + grow, s);
+    }
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <typename IO, bool LOCAL>
+hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
+    switch (cg) {
+#define SSM_CASE(N)                                                                          \
+    case N:                                                                                  \
+        hipLaunchKernelGGL((scan_kernel<IO, LOCAL, N>), grid, dim3(N * 8), 0, stream, prm);  \
+        break;
+        SSM_CASE(32)
+        SSM_CASE(48)
+        SSM_CASE(64)
+        SSM_CASE(80)
+        SSM_CASE(96)
+#undef SSM_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_scan_t(const ScanPlan& plan, ScanParams prm, const void* B, const void* C,
+                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    {
+        const int64_t n = prm.batch * prm.lpad * 8;
+        hipLaunchKernelGGL(bc_widen_kernel<IO>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
+                           stream, static_cast<const IO*>(B), static_cast<const IO*>(C),
+                           prm.bcq, prm.batch, prm.seqlen, prm.lpad);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int cg = plan.group_channels;
+    if (plan.nchunks == 1) {
+        prm.chunk_state = nullptr;
+        prm.chunk_offset = 0;
+        if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
+        hipError_t e = launch_scan_kernel<IO, false>(cg, dim3((unsigned)prm.ngroups), stream, prm);
+        if (e == hipSuccess && ev1) e = hipEventRecord(ev1, stream);
+        return e;
+    }
+    // pass 1: chunks 0..K-2 from a zero state -> end states and sums of Delta
+    {
+        ScanParams p1 = prm;
+        p1.chunk_offset = 0;
+        hipError_t e = launch_scan_kernel<IO, true>(
+            cg, dim3((unsigned)(prm.ngroups * (int64_t)(plan.nchunks - 1))), stream, p1);
+        if (e != hipSuccess) return e;
+    }
+    {
+        const int64_t nrows = prm.batch * prm.dim;
+        hipLaunchKernelGGL(carry_kernel, dim3((unsigned)cdiv(nrows * kDState, 256)), dim3(256),
+                           0, stream, prm.A, prm.h0, prm.chunk_state, prm.chunk_sum, nrows,
+                           prm.dim, plan.nchunks);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    prm.chunk_offset = 0;
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
+    hipError_t e = launch_scan_kernel<IO, false>(
+        cg, dim3((unsigned)(prm.ngroups * (int64_t)plan.nchunks)), stream, prm);
+    if (e == hipSuccess && ev1) e = hipEventRecord(ev1, stream);
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* B, const void* C,
+                       bool bf16, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
+    return bf16 ? launch_scan_t<uint16_t>(plan, prm, B, C, stream, ev_begin, ev_end)
+                : launch_scan_t<float>(plan, prm, B, C, stream, ev_begin, ev_end);
+}
+
+hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream) {
+    const int64_t threads = prm.batch * prm.dim * 4;
+    const dim3 grid((unsigned)cdiv(threads, 256));
+    if (bf16)
+        hipLaunchKernelGGL(state_update_kernel<uint16_t>, grid, dim3(256), 0, stream, prm);
+    else
+        hipLaunchKernelGGL(state_update_kernel<float>, grid, dim3(256), 0, stream, prm);
+    return hipGetLastError();
+}
+
+}  // namespace ssm
