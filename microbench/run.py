@@ -12,7 +12,8 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PROBES = ["copy_and_alu", "issue_latency", "valu_forms", "lds_bandwidth", "scan_access_pattern"]
+PROBES = ["copy_and_alu", "issue_latency", "valu_forms", "dual_issue", "lds_bandwidth",
+          "scan_access_pattern", "core_mix"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
