@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_ABI_VERSION 2
 
 typedef enum {
     SSM_OK = 0,
@@ -64,7 +64,8 @@ typedef enum {
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
-/* Plan selection, for tests and tuning. Pass NULL for the library's choice. */
+/* Scan direction and output mode, plus plan selection for tests and tuning.
+ * Pass NULL for: causal scan, y overwritten, the library's plan. */
 typedef struct {
     int64_t chunk_len;  /* tokens per chunk in the chunked plan; 0 = library choice.
                            Must be a positive multiple of 32 when set.                 */
@@ -78,6 +79,16 @@ typedef struct {
     void* timing_begin; /* hipEvent_t or NULL: recorded on `stream` right before the
                            launch of the scan kernel that writes y                     */
     void* timing_end;   /* hipEvent_t or NULL: recorded right after that launch        */
+    int32_t reverse;    /* 0 = causal scan, t = 0..L-1. 1 = anti-causal scan, t = L-1..0:
+                           h_t = exp(Delta_t*A)*h_{t+1} + Delta_t*B_t*x_t with h_L = h0,
+                           y read from h_t as in the causal scan, h_final = h_0. This is
+                           the causal scan of the time-reversed sequence, reversed back;
+                           the second direction of a bidirectional layer (sivaro, FAQ on
+                           bidirectional context).                                       */
+    int32_t accumulate; /* 0 = y is written. 1 = y += this scan's output (y is read first,
+                           the sum rounded once to io_dtype): two calls, causal then
+                           anti-causal with accumulate = 1, give a bidirectional layer's
+                           summed output.                                                 */
 } ssm_scan_options;
 
 /*
@@ -85,11 +96,16 @@ typedef struct {
  * not NULL). Returns 0 for an invalid shape. The caller allocates it (any device
  * allocation, 16-byte aligned) and may reuse it across calls on the same stream.
  * Layout, with Lp = seqlen rounded up to a multiple of 32 and K chunks:
- *   [0, batch*4*Lp*32 bytes)  B and C widened to fp32, per state quad q:
- *                             [batch][q][Lp][B[4q..4q+3], C[4q..4q+3]]
+ *   [0, batch*8*Lp*16 bytes)  B and C widened to fp32, per state pair p = 0..7:
+ *                             [batch][p][Lp][B[2p], B[2p+1], C[2p], C[2p+1]]
+ *                             (zeros for the padding tokens t >= seqlen)
  *   then (256-byte aligned, chunked plan only) [batch*dim][K][16] fp32: after the
- *   call, the state entering each chunk (h0 or zeros for chunk 0);
- *   then (256-byte aligned) [batch*dim][K] fp32: the sum of Delta over each chunk.
+ *   call, the state entering each chunk in scan order (for the first chunk in scan
+ *   order: h0, or zeros);
+ *   then (256-byte aligned) [batch*dim][K] fp32: the sum of Delta over each chunk
+ *   (not written for the last chunk in scan order);
+ *   then (256-byte aligned) [K] int32: for packed sequences, 1 where a sequence
+ *   begins (in scan order) inside the chunk.
  */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                 ssm_dtype io_dtype, const ssm_scan_options* opts);
@@ -108,7 +124,8 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   delta_bias [dim] fp32 or NULL (zero)
  *   delta_softplus  1: Delta = softplus(delta + bias); 0: Delta = delta + bias
  *   h0         [batch][dim][dstate] fp32 or NULL (zero initial state)
- *   y          [batch][dim][seqlen] io_dtype out; must not overlap any other buffer
+ *   y          [batch][dim][seqlen] io_dtype out (also read first when
+ *              opts->accumulate = 1); must not overlap any other buffer
  *   h_final    [batch][dim][dstate] fp32 out (the state after the last token) or
  *              NULL. It may be exactly h0 (in-place resume) but not partly overlap it.
  *   workspace  device buffer of at least ssm_scan_workspace_bytes(...) bytes
@@ -121,6 +138,42 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
                         void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
                         int64_t dstate, ssm_dtype io_dtype, void* workspace,
                         size_t workspace_bytes, const ssm_scan_options* opts, void* stream);
+
+/*
+ * Packed (variable-length) sequences: several sequences laid end to end along the
+ * token axis of one row, each scanned on its own -- the state starts from that
+ * sequence's initial state at its first token and nothing crosses a boundary.
+ * (Training on packed sequences needs this: sivaro, "Problem 3: Ecosystem maturity".)
+ *
+ *   x, delta, z, y  [dim][total]        io_dtype (z may be NULL)
+ *   B, C            [total][dstate]     io_dtype
+ *   cu_seqlens      [nseq+1] int32, device: sequence i is tokens
+ *                   cu_seqlens[i] .. cu_seqlens[i+1]-1. It must hold 0 = cu[0] <=
+ *                   cu[1] <= ... <= cu[nseq] = total (empty sequences allowed); this
+ *                   is not checked (it lives on the device). If it does not hold the
+ *                   outputs are unspecified, but nothing outside the buffers given
+ *                   here is read or written.
+ *   h0              [nseq][dim][dstate] fp32 or NULL: initial state of each sequence
+ *   h_final         [nseq][dim][dstate] fp32 out or NULL: final state of each sequence
+ *                   (an empty sequence's final state is its initial state). May be
+ *                   exactly h0.
+ *   A, D, delta_bias, delta_softplus, opts (including reverse: each sequence is
+ *   scanned from its last token to its first) as for ssm_scan_fwd.
+ * total >= 0 (0: only h_final is written), nseq >= 1, dim >= 1, dstate == 16.
+ * The workspace is ssm_scan_varlen_workspace_bytes(...) bytes (0 when total == 0),
+ * laid out as for ssm_scan_fwd with batch = 1 and seqlen = total.
+ */
+size_t ssm_scan_varlen_workspace_bytes(int64_t total, int64_t dim, int64_t dstate,
+                                       ssm_dtype io_dtype, const ssm_scan_options* opts);
+
+ssm_status ssm_scan_varlen_fwd(const void* x, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, int delta_softplus,
+                               const int32_t* cu_seqlens, int64_t nseq, const float* h0,
+                               void* y, float* h_final, int64_t total, int64_t dim,
+                               int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                               size_t workspace_bytes, const ssm_scan_options* opts,
+                               void* stream);
 
 /*
  * One recurrent decode step: one token for every (batch, channel), the state

@@ -133,6 +133,52 @@ class Oracle:
             h0_rows=None if h0 is None else f64(h0).reshape(b * d, N), nthreads=nthreads)
         return y.reshape(b, d, L), hf.reshape(b, d, N)
 
+    # ---- reverse-time and packed (varlen) scans ---------------------------
+    def scan_reverse(self, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                     delta_softplus=True, h0=None, nthreads=1):
+        """The scan run backwards in time: h_t = exp(Delta_t A) h_{t+1} + Delta_t B_t x_t,
+        h_L = h0. By definition the forward scan of the time-reversed inputs, with the
+        outputs reversed back; h_final is the state after token 0."""
+        rx = f64(x)[:, :, ::-1]
+        rd = f64(delta)[:, :, ::-1]
+        rz = None if z is None else f64(z)[:, :, ::-1]
+        rB = f64(B)[:, ::-1]
+        rC = f64(C)[:, ::-1]
+        y, hf = self.scan(rx, rd, A, rB, rC, D=D, z=rz, delta_bias=delta_bias,
+                          delta_softplus=delta_softplus, h0=h0, nthreads=nthreads)
+        return np.ascontiguousarray(y[:, :, ::-1]), hf
+
+    def scan_varlen(self, x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None,
+                    delta_softplus=True, h0=None, reverse=False, nthreads=1):
+        """Packed sequences: x, delta, z are [dim][total], B, C [total][N]; sequence i is
+        tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 and starts from h0[i] (zeros when h0 is
+        None). By definition each sequence is scanned on its own. Returns y [dim][total]
+        and the final state of every sequence [nseq][dim][N]."""
+        x = f64(x)
+        dim, total = x.shape
+        N = f64(A).shape[1]
+        cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+        nseq = len(cu) - 1
+        assert cu[0] == 0 and cu[-1] == total and all(a <= b for a, b in zip(cu, cu[1:]))
+        dl, Bf, Cf = f64(delta), f64(B), f64(C)
+        zf = None if z is None else f64(z)
+        h0f = None if h0 is None else f64(h0)
+        y = np.zeros((dim, total))
+        hf = np.zeros((nseq, dim, N))
+        fn = self.scan_reverse if reverse else self.scan
+        for i in range(nseq):
+            a, b = cu[i], cu[i + 1]
+            start = None if h0f is None else h0f[i][None]
+            if b == a:
+                hf[i] = 0.0 if start is None else start[0]
+                continue
+            yi, hi = fn(x[None, :, a:b], dl[None, :, a:b], A, Bf[None, a:b], Cf[None, a:b], D=D,
+                        z=None if zf is None else zf[None, :, a:b], delta_bias=delta_bias,
+                        delta_softplus=delta_softplus, h0=start, nthreads=nthreads)
+            y[:, a:b] = yi[0]
+            hf[i] = hi[0]
+        return y, hf
+
     # ---- decode step ----------------------------------------------------
     def step(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
              delta_softplus=True):

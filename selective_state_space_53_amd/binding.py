@@ -21,14 +21,16 @@ if not os.path.exists(_LIB_PATH):
 SSM_OK, SSM_ERR_INVALID_ARGUMENT, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE_TOO_SMALL, \
     SSM_ERR_HIP = range(5)
 SSM_F32, SSM_BF16 = 0, 1
-EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
-           "ssm_status_string", "ssm_last_error", "ssm_abi_version")
+EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_scan_varlen_workspace_bytes",
+           "ssm_scan_varlen_fwd", "ssm_state_update", "ssm_status_string", "ssm_last_error",
+           "ssm_abi_version")
 
 
 class ScanOptions(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("plan", ctypes.c_int32),
                 ("group_channels", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
-                ("timing_end", ctypes.c_void_p)]
+                ("timing_end", ctypes.c_void_p), ("reverse", ctypes.c_int32),
+                ("accumulate", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -42,6 +44,13 @@ lib.ssm_scan_fwd.restype = ctypes.c_int
 lib.ssm_scan_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                              _i64, _i64, _i64, _i64, ctypes.c_int, _vp, ctypes.c_size_t,
                              ctypes.POINTER(ScanOptions), _vp]
+lib.ssm_scan_varlen_workspace_bytes.restype = ctypes.c_size_t
+lib.ssm_scan_varlen_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int,
+                                                ctypes.POINTER(ScanOptions)]
+lib.ssm_scan_varlen_fwd.restype = ctypes.c_int
+lib.ssm_scan_varlen_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                    _i64, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp,
+                                    ctypes.c_size_t, ctypes.POINTER(ScanOptions), _vp]
 lib.ssm_state_update.restype = ctypes.c_int
 lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                  _i64, _i64, _i64, ctypes.c_int, _vp]
@@ -91,11 +100,14 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
     return t
 
 
-def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0):
-    if plan == 0 and chunk_len == 0 and events is None and group_channels == 0:
+def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0,
+             reverse=False, accumulate=False):
+    if (plan == 0 and chunk_len == 0 and events is None and group_channels == 0
+            and not reverse and not accumulate):
         return None
     ev0, ev1 = (None, None) if events is None else events
-    return ctypes.byref(ScanOptions(chunk_len, plan, group_channels, ev0, ev1))
+    return ctypes.byref(ScanOptions(chunk_len, plan, group_channels, ev0, ev1, int(bool(reverse)),
+                                    int(bool(accumulate))))
 
 
 def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
@@ -104,11 +116,19 @@ def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk
                                         _options(plan, chunk_len, None, group_channels))
 
 
+def ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype, plan=0, chunk_len=0,
+                                    group_channels=0) -> int:
+    return lib.ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype,
+                                               _options(plan, chunk_len, None, group_channels))
+
+
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                  h0=None, return_final_state=False, y=None, h_final=None, workspace=None,
-                 plan=0, chunk_len=0, stream=None, timing_events=None, group_channels=0):
+                 plan=0, chunk_len=0, stream=None, timing_events=None, group_channels=0,
+                 reverse=False, accumulate=False):
     """x, delta, z: [batch][dim][seqlen]; B, C: [batch][seqlen][16]; A: [dim][16];
     D, delta_bias: [dim]; h0: [batch][dim][16]. Returns y (and h_final).
+    reverse: anti-causal scan; accumulate: add into the given y instead of writing it.
     timing_events: optional (begin, end) pair of raw hipEvent_t handles (ints) that
     the library records around the launch of the scan kernel that writes y."""
     _dev(x, "x")
@@ -126,12 +146,14 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     code = _dtype_code(x)
     dev = x.device
     if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the y to add into")
         y = torch.empty_like(x)
     _dev(y, "y", io, x.shape)
     if return_final_state and h_final is None:
         h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _dev(h_final, "h_final", torch.float32, (batch, dim, N))
-    opts = _options(plan, chunk_len, timing_events, group_channels)
+    opts = _options(plan, chunk_len, timing_events, group_channels, reverse, accumulate)
     ws_bytes = lib.ssm_scan_workspace_bytes(batch, seqlen, dim, N, code, opts)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -141,6 +163,53 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
             _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, N,
             code, _ptr(workspace), 0 if workspace is None else workspace.numel(), opts, s))
+    return (y, h_final) if return_final_state else y
+
+
+def ssm_scan_varlen_fwd(x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None,
+                        delta_softplus=True, h0=None, return_final_state=False, y=None,
+                        h_final=None, workspace=None, plan=0, chunk_len=0, stream=None,
+                        timing_events=None, group_channels=0, reverse=False,
+                        accumulate=False):
+    """Packed sequences. x, delta, z: [dim][total]; B, C: [total][16]; cu_seqlens: int32
+    [nseq+1] on the device; h0: [nseq][dim][16]. Returns y (and h_final [nseq][dim][16])."""
+    _dev(x, "x")
+    io = x.dtype
+    dim, total = x.shape
+    N = A.shape[-1]
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least 2 entries")
+    nseq = cu_seqlens.numel() - 1
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(A, "A", torch.float32, (dim, N))
+    _dev(B, "B", io, (total, N))
+    _dev(C, "C", io, (total, N))
+    _dev(D, "D", torch.float32, (dim,))
+    _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    _dev(h0, "h0", torch.float32, (nseq, dim, N))
+    code = _dtype_code(x)
+    dev = x.device
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the y to add into")
+        y = torch.empty_like(x)
+    _dev(y, "y", io, x.shape)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((nseq, dim, N), dtype=torch.float32, device=dev)
+    _dev(h_final, "h_final", torch.float32, (nseq, dim, N))
+    opts = _options(plan, chunk_len, timing_events, group_channels, reverse, accumulate)
+    ws_bytes = lib.ssm_scan_varlen_workspace_bytes(total, dim, N, code, opts)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        _check(lib.ssm_scan_varlen_fwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(cu_seqlens), nseq, _ptr(h0), _ptr(y), _ptr(h_final),
+            total, dim, N, code, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+            opts, s))
     return (y, h_final) if return_final_state else y
 
 

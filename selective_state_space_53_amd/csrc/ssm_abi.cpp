@@ -62,33 +62,75 @@ Region region(const char* name, const void* p, int64_t bytes) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// LDS bytes of one scan workgroup of cg channels (must match the kernel's arrays).
-int64_t scan_lds_bytes(int cg) { return (int64_t)(10 * cg * 36 + 2 * 1024) * 4; }
+// LDS bytes of one scan workgroup of cg channels (must match the kernel's arrays):
+// Delta, Delta*x and (not in pass 1) the 8 partial readouts, [cg][36] floats each,
+// plus two tiles of widened B/C.
+int64_t scan_lds_bytes(int cg, bool local) {
+    return (int64_t)((local ? 2 : 10) * cg * 36 + (local ? 4 : 0) + 2 * 1024) * 4;
+}
 
-int choose_group_channels(int64_t batch, int64_t dim) {
-    static const int kCands[] = {96, 80, 64, 48, 32};
-    const int64_t kCUs = 256, kLds = 160 * 1024;
-    int best = 32;
-    double best_t = 1e300;
-    int64_t best_busy = -1;
-    for (int cg : kCands) {
-        const int64_t groups = batch * ((dim + cg - 1) / cg);
-        int64_t k = kLds / scan_lds_bytes(cg);                    // workgroups per CU
-        const int64_t per_cu = (groups + kCUs - 1) / kCUs;
-        if (k > per_cu) k = per_cu;
-        if (k < 1) k = 1;
-        const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
-        int64_t per_simd = (k * (cg / 8) + 3) / 4;               // waves on the busiest SIMD
-        if (per_simd < 2) per_simd = 2;
-        const double t = (double)rounds * (double)per_simd;
-        const int64_t busy = groups < kCUs ? groups : kCUs;
-        if (t < best_t - 1e-9 || (t < best_t + 1e-9 && busy > best_busy)) {
-            best = cg;
-            best_t = t;
-            best_busy = busy;
-        }
+// ---- launch cost model -------------------------------------------------------------
+// SIMD cycles per wave per (token, state pair) of the recurrence, by waves resident on
+// the SIMD: one wave cannot hide the exp/FMA latencies, more than three add little
+// (measured on gfx950 with the same instruction mix: microbench/core_mix.hip).
+double wave_cost(int64_t waves_per_simd) {
+    static const double kCost[] = {0.0, 55.5, 36.5, 31.0, 30.7};
+    return waves_per_simd <= 4 ? kCost[waves_per_simd < 1 ? 1 : waves_per_simd] : 30.5;
+}
+
+constexpr int64_t kCUs = 256;
+constexpr int64_t kLdsPerCU = 160 * 1024;
+// waves per SIMD that the registers allow: the kernel that writes y uses <= 112 VGPRs,
+// pass 1 <= 88 (512 per lane and SIMD)
+constexpr int64_t kMaxWavesFull = 4, kMaxWavesLocal = 5;
+
+// Relative time of one pass: `groups` workgroups of cg channels, `tiles` tiles each.
+double pass_cost(int64_t groups, int64_t tiles, int cg, bool local) {
+    const int64_t waves = cg / 8;
+    int64_t k = kLdsPerCU / scan_lds_bytes(cg, local);                  // by LDS
+    const int64_t kw = 4 * (local ? kMaxWavesLocal : kMaxWavesFull) / waves;  // by registers
+    if (kw < k) k = kw;
+    const int64_t per_cu = (groups + kCUs - 1) / kCUs;
+    if (k > per_cu) k = per_cu;
+    if (k < 1) k = 1;
+    const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
+    const int64_t w = (k * waves + 3) / 4;                               // busiest SIMD
+    // pass 1 skips the readout and the output stage; a workgroup's set-up costs about
+    // one tile
+    return (double)rounds * (double)(tiles + 1) * (double)w * wave_cost(w) * (local ? 0.85 : 1.0);
+}
+
+struct PlanChoice {
+    int cg;
+    int64_t nchunks, chunk_len;
+    double cost;
+    int64_t busy;  // CUs with a workgroup of the pass that writes y
+};
+
+// lower modelled time; on a tie, fewer chunks, then more busy CUs
+bool better(const PlanChoice& a, const PlanChoice& b) {
+    if (b.cg == 0) return true;
+    if (a.cost < b.cost * (1 - 1e-9)) return true;
+    if (a.cost > b.cost * (1 + 1e-9)) return false;
+    if (a.nchunks != b.nchunks) return a.nchunks < b.nchunks;
+    return a.busy > b.busy;
+}
+
+// Cost of (cg, chunk_len): single pass when chunk_len >= seqlen, else pass 1 over all
+// chunks but one, the carry, and pass 2 over every chunk.
+PlanChoice plan_cost(int64_t batch, int64_t seqlen, int64_t dim, int cg, int64_t chunk_len) {
+    const int64_t groups = batch * ((dim + cg - 1) / cg);
+    const int64_t tile = ssm::kTokenTile;
+    if (chunk_len >= seqlen) {
+        return PlanChoice{cg, 1, seqlen, pass_cost(groups, (seqlen + tile - 1) / tile, cg, false),
+                          groups < kCUs ? groups : kCUs};
     }
-    return best;
+    const int64_t k = (seqlen + chunk_len - 1) / chunk_len;
+    const int64_t tiles = chunk_len / tile;
+    // two more launches (pass 1 and the carry), each worth about 150 units (~6 us)
+    const double c = pass_cost(groups * (k - 1), tiles, cg, true) +
+                     pass_cost(groups * k, tiles, cg, false) + (double)k * 2.0 + 300.0;
+    return PlanChoice{cg, k, chunk_len, c, groups * k < kCUs ? groups * k : kCUs};
 }
 
 // Plan for a shape. Shared by the workspace query and the call, so both agree.
@@ -125,6 +167,12 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
             return fail(SSM_ERR_INVALID_ARGUMENT,
                         "ssm_scan_options.chunk_len=%lld must be a multiple of %d",
                         (long long)opts->chunk_len, ssm::kTokenTile);
+        if (opts->reverse != 0 && opts->reverse != 1)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.reverse=%d not 0 or 1",
+                        (int)opts->reverse);
+        if (opts->accumulate != 0 && opts->accumulate != 1)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.accumulate=%d not 0 or 1",
+                        (int)opts->accumulate);
         req_plan = opts->plan;
         req_chunk = opts->chunk_len;
     }
@@ -132,49 +180,55 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
         return fail(SSM_ERR_INVALID_ARGUMENT, "batch*dim too large");
     const int64_t lpad = (seqlen + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
 
-    // Channels per workgroup (single pass): the choice with the shortest estimated
-    // makespan on 256 CUs. A workgroup of cg channels runs cg/8 waves; a CU holds as
-    // many workgroups as its 160 KB of LDS allows; a SIMD's time is proportional to
-    // the waves it holds, except that a lone wave issues at half rate (so 1 wave costs
-    // as much as 2). Ties go to more busy CUs, then to larger groups.
-    const int cg_single = req_cg ? req_cg : choose_group_channels(batch, dim);
-    const int64_t groups_single = batch * ((dim + cg_single - 1) / cg_single);
-
-    // Single pass when there are enough channel groups to occupy the chip, or the
-    // sequence is short; otherwise cut the sequence so that groups x chunks ~ 2048.
-    bool chunked;
-    if (req_plan == 1)
-        chunked = false;
-    else if (req_plan == 2)
-        chunked = true;
-    else
-        chunked = groups_single < 128 && seqlen >= 4096;
-    const int cg = chunked ? (req_cg ? req_cg : (dim >= 96 ? 96 : 32)) : cg_single;
-    const int64_t ngroups = batch * ((dim + cg - 1) / cg);
-    int64_t chunk_len = seqlen, nchunks = 1;
-    if (chunked) {
-        chunk_len = req_chunk;
-        if (chunk_len == 0) {
-            int64_t k = (2048 + ngroups - 1) / ngroups;
-            if (k < 2) k = 2;
-            chunk_len = (seqlen + k - 1) / k;
-            chunk_len = (chunk_len + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
+    // Channels per workgroup and chunking: the choice with the lowest modelled time
+    // (pass_cost above) among group sizes 32..96 and chunk counts 1 (single pass), 2,
+    // 3, 4, 6, 8, 12, ... A requested group size, plan or chunk length restricts the
+    // search. Ties go to fewer chunks, then to larger groups.
+    static const int kCands[] = {96, 80, 64, 48, 32};
+    PlanChoice best{0, 0, 0, 1e300, 0};
+    for (int c : kCands) {
+        if (req_cg && c != req_cg) continue;
+        if (req_plan != 2) {
+            const PlanChoice pc = plan_cost(batch, seqlen, dim, c, seqlen);
+            if (better(pc, best)) best = pc;
         }
-        nchunks = (seqlen + chunk_len - 1) / chunk_len;
-        if (nchunks <= 1) {
-            nchunks = 1;
-            chunk_len = seqlen;
+        if (req_plan == 1) continue;
+        if (req_chunk > 0) {
+            if (req_chunk < seqlen) {
+                const PlanChoice pc = plan_cost(batch, seqlen, dim, c, req_chunk);
+                if (better(pc, best)) best = pc;
+            } else if (req_plan == 2 && best.cg == 0) {
+                best = plan_cost(batch, seqlen, dim, c, seqlen);
+            }
+            continue;
+        }
+        for (int64_t kk = 2; kk <= 4096; kk = kk < 4 ? kk + 1 : kk + kk / 2) {
+            int64_t cl = (seqlen + kk - 1) / kk;
+            cl = (cl + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
+            if (cl >= seqlen) {
+                if (req_plan == 2 && best.cg == 0) best = plan_cost(batch, seqlen, dim, c, seqlen);
+                continue;
+            }
+            const PlanChoice pc = plan_cost(batch, seqlen, dim, c, cl);
+            if (better(pc, best)) best = pc;
+            if (cl <= ssm::kTokenTile) break;
         }
     }
+    if (best.cg == 0) best = plan_cost(batch, seqlen, dim, req_cg ? req_cg : 32, seqlen);
+    const int cg = best.cg;
+    const int64_t ngroups = batch * ((dim + cg - 1) / cg);
+    const int64_t nchunks = best.nchunks;
+    const int64_t chunk_len = best.chunk_len;
     if (ngroups * nchunks >= (int64_t(1) << 31))
         return fail(SSM_ERR_INVALID_ARGUMENT, "too many chunks (%lld)", (long long)nchunks);
-    int64_t bcq_bytes, st_bytes = 0, sum_bytes = 0;
+    int64_t bcq_bytes, st_bytes = 0, sum_bytes = 0, flag_bytes = 0;
     if (!bytes4(batch, lpad, 4 * 8, 4, &bcq_bytes))
         return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
     if (nchunks > 1) {
         if (!bytes4(batch * dim, nchunks, ssm::kDState, 4, &st_bytes) ||
             !bytes4(batch * dim, nchunks, 1, 4, &sum_bytes))
             return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
+        flag_bytes = nchunks * 4;
     }
     plan->group_channels = cg;
     plan->ngroups = ngroups;
@@ -183,7 +237,130 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     plan->ws_bcq = 0;
     plan->ws_state = align_up((size_t)bcq_bytes, 256);
     plan->ws_sum = align_up(plan->ws_state + (size_t)st_bytes, 256);
-    plan->ws_total = align_up(plan->ws_sum + (size_t)sum_bytes, 256);
+    plan->ws_flag = align_up(plan->ws_sum + (size_t)sum_bytes, 256);
+    plan->ws_total = align_up(plan->ws_flag + (size_t)flag_bytes, 256);
+    return SSM_OK;
+}
+
+ssm_status scan_impl(const void* x, const void* delta, const float* A, const void* B,
+                     const void* C, const float* D, const void* z, const float* delta_bias,
+                     int delta_softplus, const int32_t* cu_seqlens, int64_t nseq,
+                     const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen,
+                     int64_t dim, int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                     size_t workspace_bytes, const ssm_scan_options* opts, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    ssm::ScanPlan plan;
+    ssm_status st = make_plan(batch, seqlen, dim, dstate, io_dtype, opts, &plan);
+    if (st != SSM_OK) return st;
+    if (delta_softplus != 0 && delta_softplus != 1)
+        return fail(SSM_ERR_INVALID_ARGUMENT, "delta_softplus must be 0 or 1");
+    if (!x || !delta || !A || !B || !C || !y)
+        return fail(SSM_ERR_INVALID_ARGUMENT,
+                    "x, delta, A, B, C and y are required (got x=%p delta=%p A=%p B=%p "
+                    "C=%p y=%p)",
+                    x, delta, (const void*)A, B, C, y);
+    const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
+    const int64_t io = batch * dim * seqlen * elem;
+    const int64_t bc = batch * seqlen * dstate * elem;
+    // per-row states: one per batch row, or one per packed sequence
+    const int64_t nstates = packed ? nseq : batch;
+    int64_t st_b;
+    if (!bytes4(nstates, dim, dstate, 4, &st_b))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "state size overflows");
+    struct {
+        const char* name;
+        const void* p;
+        uintptr_t align;
+    } al[] = {{"x", x, 16},       {"delta", delta, 16}, {"z", z, 16},
+              {"y", y, 16},       {"B", B, 16},         {"C", C, 16},
+              {"h0", h0, 16},     {"h_final", h_final, 16},
+              {"A", A, 16},       {"D", D, 4},          {"delta_bias", delta_bias, 4},
+              {"cu_seqlens", cu_seqlens, 4},            {"workspace", workspace, 16}};
+    for (auto& a : al)
+        if (a.p && !aligned(a.p, a.align))
+            return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
+                        (unsigned)a.align);
+    if (plan.ws_total > 0 && (!workspace || workspace_bytes < plan.ws_total))
+        return fail(SSM_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace needs %zu bytes (got %zu at %p)", plan.ws_total,
+                    workspace_bytes, workspace);
+    const Region ry = region("y", y, io);
+    const Region rhf = region("h_final", h_final, st_b);
+    const Region rws = region("workspace", workspace, (int64_t)plan.ws_total);
+    const Region inputs[] = {region("x", x, io),
+                             region("delta", delta, io),
+                             region("z", z, io),
+                             region("B", B, bc),
+                             region("C", C, bc),
+                             region("A", A, dim * dstate * 4),
+                             region("D", D, dim * 4),
+                             region("delta_bias", delta_bias, dim * 4),
+                             region("cu_seqlens", cu_seqlens, (nseq + 1) * 4),
+                             region("h0", h0, st_b)};
+    const Region& rh0 = inputs[9];
+    for (const Region& r : inputs) {
+        if (overlaps(ry, r))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps %s", r.name);
+        if (overlaps(rws, r))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+        if (h_final && overlaps(rhf, r)) {
+            const bool same_h0 = (&r == &rh0) && (const void*)h_final == h0;
+            if (!same_h0)
+                return fail(SSM_ERR_INVALID_ARGUMENT,
+                            "h_final overlaps %s (only h_final == h0 exactly is allowed)",
+                            r.name);
+        }
+    }
+    if (h_final && overlaps(ry, rhf))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps h_final");
+    if (overlaps(rws, ry)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps y");
+    if (h_final && overlaps(rws, rhf))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps h_final");
+
+    ssm::ScanParams prm{};
+    char* ws = static_cast<char*>(workspace);
+    prm.x = x;
+    prm.delta = delta;
+    prm.z = z;
+    prm.y = y;
+    prm.A = A;
+    prm.D = D;
+    prm.bias = delta_bias;
+    prm.h0 = h0;
+    prm.h_final = h_final;
+    prm.bcq = reinterpret_cast<float*>(ws + plan.ws_bcq);
+    prm.chunk_state = plan.nchunks > 1 ? reinterpret_cast<float*>(ws + plan.ws_state) : nullptr;
+    prm.chunk_sum = plan.nchunks > 1 ? reinterpret_cast<float*>(ws + plan.ws_sum) : nullptr;
+    prm.chunk_flag = plan.nchunks > 1 ? reinterpret_cast<int32_t*>(ws + plan.ws_flag) : nullptr;
+    prm.cu = cu_seqlens;
+    prm.nseq = (int32_t)nseq;
+    prm.batch = batch;
+    prm.seqlen = seqlen;
+    prm.dim = dim;
+    prm.lpad = (seqlen + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
+    prm.chunk_len = plan.chunk_len;
+    prm.nchunks = plan.nchunks;
+    prm.groups_per_batch = (int32_t)((dim + plan.group_channels - 1) / plan.group_channels);
+    prm.ngroups = (int32_t)(batch * prm.groups_per_batch);
+    prm.chunk_offset = 0;
+    prm.softplus = delta_softplus;
+    prm.aligned = ((seqlen * elem) % 16) == 0;
+    prm.reverse = opts ? opts->reverse : 0;
+    prm.accumulate = opts ? opts->accumulate : 0;
+    if (getenv("SSMSCAN_LOG"))
+        fprintf(stderr,
+                "[ssmscan] scan b=%lld L=%lld d=%lld %s%s%s%s: %s, %d channels/group, %lld "
+                "groups, chunks=%d x %lld\n",
+                (long long)batch, (long long)seqlen, (long long)dim,
+                io_dtype == SSM_BF16 ? "bf16" : "f32", packed ? " packed" : "",
+                prm.reverse ? " reverse" : "", prm.accumulate ? " accumulate" : "",
+                plan.nchunks > 1 ? "chunked" : "single pass", plan.group_channels,
+                (long long)plan.ngroups, plan.nchunks, (long long)plan.chunk_len);
+    hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->timing_begin) : nullptr;
+    hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->timing_end) : nullptr;
+    const hipError_t e = ssm::launch_scan(plan, prm, B, C, io_dtype == SSM_BF16,
+                                          static_cast<hipStream_t>(stream), ev0, ev1);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return SSM_OK;
 }
 
@@ -220,106 +397,59 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
                         int64_t dstate, ssm_dtype io_dtype, void* workspace,
                         size_t workspace_bytes, const ssm_scan_options* opts, void* stream) {
     try {
+        return scan_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, 0, h0, y,
+                         h_final, batch, seqlen, dim, dstate, io_dtype, workspace,
+                         workspace_bytes, opts, stream);
+    } catch (...) {
+        return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
+    }
+}
+
+size_t ssm_scan_varlen_workspace_bytes(int64_t total, int64_t dim, int64_t dstate,
+                                       ssm_dtype io_dtype, const ssm_scan_options* opts) {
+    if (total == 0) return 0;
+    return ssm_scan_workspace_bytes(1, total, dim, dstate, io_dtype, opts);
+}
+
+ssm_status ssm_scan_varlen_fwd(const void* x, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, int delta_softplus,
+                               const int32_t* cu_seqlens, int64_t nseq, const float* h0,
+                               void* y, float* h_final, int64_t total, int64_t dim,
+                               int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                               size_t workspace_bytes, const ssm_scan_options* opts,
+                               void* stream) {
+    try {
+        if (!cu_seqlens)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "cu_seqlens is required");
+        if (nseq < 1 || nseq >= (int64_t(1) << 30))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "nseq=%lld must be in [1, 2^30)",
+                        (long long)nseq);
+        if (total < 0 || total >= (int64_t(1) << 31))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "total=%lld must be in [0, 2^31)",
+                        (long long)total);
+        if (total > 0)
+            return scan_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, cu_seqlens,
+                             nseq, h0, y, h_final, 1, total, dim, dstate, io_dtype, workspace,
+                             workspace_bytes, opts, stream);
+        // no tokens: every sequence is empty and its final state is its initial state
         ssm::ScanPlan plan;
-        ssm_status st = make_plan(batch, seqlen, dim, dstate, io_dtype, opts, &plan);
+        ssm_status st = make_plan(1, 1, dim, dstate, io_dtype, opts, &plan);
         if (st != SSM_OK) return st;
         if (delta_softplus != 0 && delta_softplus != 1)
             return fail(SSM_ERR_INVALID_ARGUMENT, "delta_softplus must be 0 or 1");
-        if (!x || !delta || !A || !B || !C || !y)
+        if (!h_final) return SSM_OK;
+        int64_t st_b;
+        if (!bytes4(nseq, dim, dstate, 4, &st_b))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "state size overflows");
+        if (!aligned(h_final, 16) || (h0 && !aligned(h0, 16)))
+            return fail(SSM_ERR_UNSUPPORTED, "h0 and h_final must be 16-byte aligned");
+        if (h0 && (const void*)h0 != (const void*)h_final &&
+            overlaps(region("h_final", h_final, st_b), region("h0", h0, st_b)))
             return fail(SSM_ERR_INVALID_ARGUMENT,
-                        "x, delta, A, B, C and y are required (got x=%p delta=%p A=%p B=%p "
-                        "C=%p y=%p)",
-                        x, delta, (const void*)A, B, C, y);
-        const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
-        const int64_t io = batch * dim * seqlen * elem;
-        const int64_t bc = batch * seqlen * dstate * elem;
-        const int64_t st_b = batch * dim * dstate * 4;
-        struct {
-            const char* name;
-            const void* p;
-            uintptr_t align;
-        } al[] = {{"x", x, 16},       {"delta", delta, 16}, {"z", z, 16},
-                  {"y", y, 16},       {"B", B, 16},         {"C", C, 16},
-                  {"h0", h0, 16},     {"h_final", h_final, 16},
-                  {"A", A, 16},       {"D", D, 4},          {"delta_bias", delta_bias, 4},
-                  {"workspace", workspace, 16}};
-        for (auto& a : al)
-            if (a.p && !aligned(a.p, a.align))
-                return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
-                            (unsigned)a.align);
-        if (plan.ws_total > 0 && (!workspace || workspace_bytes < plan.ws_total))
-            return fail(SSM_ERR_WORKSPACE_TOO_SMALL,
-                        "workspace needs %zu bytes (got %zu at %p)", plan.ws_total,
-                        workspace_bytes, workspace);
-        const Region ry = region("y", y, io);
-        const Region rhf = region("h_final", h_final, st_b);
-        const Region rws = region("workspace", workspace, (int64_t)plan.ws_total);
-        const Region inputs[] = {region("x", x, io),
-                                 region("delta", delta, io),
-                                 region("z", z, io),
-                                 region("B", B, bc),
-                                 region("C", C, bc),
-                                 region("A", A, dim * dstate * 4),
-                                 region("D", D, dim * 4),
-                                 region("delta_bias", delta_bias, dim * 4),
-                                 region("h0", h0, st_b)};
-        for (const Region& r : inputs) {
-            if (overlaps(ry, r))
-                return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps %s", r.name);
-            if (overlaps(rws, r))
-                return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
-            if (h_final && overlaps(rhf, r)) {
-                const bool same_h0 = (r.name == inputs[8].name) && (const void*)h_final == h0;
-                if (!same_h0)
-                    return fail(SSM_ERR_INVALID_ARGUMENT,
-                                "h_final overlaps %s (only h_final == h0 exactly is allowed)",
-                                r.name);
-            }
-        }
-        if (h_final && overlaps(ry, rhf))
-            return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps h_final");
-        if (overlaps(rws, ry)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps y");
-        if (h_final && overlaps(rws, rhf))
-            return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps h_final");
-
-        ssm::ScanParams prm{};
-        char* ws = static_cast<char*>(workspace);
-        prm.x = x;
-        prm.delta = delta;
-        prm.z = z;
-        prm.y = y;
-        prm.A = A;
-        prm.D = D;
-        prm.bias = delta_bias;
-        prm.h0 = h0;
-        prm.h_final = h_final;
-        prm.bcq = reinterpret_cast<float*>(ws + plan.ws_bcq);
-        prm.chunk_state = plan.nchunks > 1 ? reinterpret_cast<float*>(ws + plan.ws_state) : nullptr;
-        prm.chunk_sum = plan.nchunks > 1 ? reinterpret_cast<float*>(ws + plan.ws_sum) : nullptr;
-        prm.batch = batch;
-        prm.seqlen = seqlen;
-        prm.dim = dim;
-        prm.lpad = (seqlen + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
-        prm.chunk_len = plan.chunk_len;
-        prm.nchunks = plan.nchunks;
-        prm.groups_per_batch =
-            (int32_t)((dim + plan.group_channels - 1) / plan.group_channels);
-        prm.ngroups = (int32_t)(batch * prm.groups_per_batch);
-        prm.chunk_offset = 0;
-        prm.softplus = delta_softplus;
-        prm.aligned = ((seqlen * elem) % 16) == 0;
-        if (getenv("SSMSCAN_LOG"))
-            fprintf(stderr,
-                    "[ssmscan] scan b=%lld L=%lld d=%lld %s: %s, %d channels/group, %lld "
-                    "groups, chunks=%d x %lld\n",
-                    (long long)batch, (long long)seqlen, (long long)dim,
-                    io_dtype == SSM_BF16 ? "bf16" : "f32",
-                    plan.nchunks > 1 ? "chunked" : "single pass", plan.group_channels,
-                    (long long)plan.ngroups, plan.nchunks, (long long)plan.chunk_len);
-        hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->timing_begin) : nullptr;
-        hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->timing_end) : nullptr;
-        const hipError_t e = ssm::launch_scan(plan, prm, B, C, io_dtype == SSM_BF16,
-                                              static_cast<hipStream_t>(stream), ev0, ev1);
+                        "h_final overlaps h0 (only h_final == h0 exactly is allowed)");
+        const hipError_t e = ssm::launch_copy_state(h0, h_final, st_b / 4,
+                                                    static_cast<hipStream_t>(stream));
         if (e != hipSuccess)
             return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
         return SSM_OK;

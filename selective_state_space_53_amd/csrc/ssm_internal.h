@@ -18,6 +18,7 @@ struct ScanPlan {
     size_t ws_bcq = 0;      // workspace byte offsets / sizes
     size_t ws_state = 0;
     size_t ws_sum = 0;
+    size_t ws_flag = 0;
     size_t ws_total = 0;
 };
 
@@ -34,9 +35,12 @@ struct ScanParams {
     float* bcq;          // [batch][8][lpad][4] fp32: B and C widened, per state pair
     float* chunk_state;  // [batch*dim][nchunks][16] (chunked plan) or null
     float* chunk_sum;    // [batch*dim][nchunks]
+    int32_t* chunk_flag; // [nchunks]: 1 = a sequence begins inside the chunk (packed input)
+    const int32_t* cu;   // packed sequences: [nseq+1] token offsets, or null (batch rows)
     int64_t batch, seqlen, dim, lpad, chunk_len;
     int32_t nchunks, ngroups, groups_per_batch, chunk_offset;
-    int32_t softplus, aligned;
+    int32_t nseq;
+    int32_t softplus, aligned, reverse, accumulate;
 };
 
 struct DecodeParams {
@@ -59,5 +63,7 @@ struct DecodeParams {
 hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* B, const void* C,
                        bool bf16, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream);
+// h_final[i] = h0 ? h0[i] : 0 for i < n (packed input with no tokens: every sequence is empty)
+hipError_t launch_copy_state(const float* h0, float* h_final, int64_t n, hipStream_t stream);
 
 }  // namespace ssm

@@ -183,6 +183,18 @@ constexpr int kTile = 32;                 // tokens per tile
 constexpr int kLdsRow = kTile + 4;        // padded [channel][token] LDS row (floats)
 constexpr int kBcTile = 8 * kTile * 4;    // floats of widened B/C per tile (8 state pairs)
 
+// Index of the packed sequence that holds token t: the largest s in [0, nseq) with
+// cu[s] <= t (0 when there is none). Reads only cu[0..nseq-1], whatever cu holds.
+__device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int64_t t) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 // One workgroup = CG channels (a multiple of 16) of one batch row x all 16 states,
 // CG*8 threads = CG/8 waves.
 //  core mapping: each 16-lane row holds one state pair p (states 2p, 2p+1) of 16
@@ -195,10 +207,16 @@ constexpr int kBcTile = 8 * kTile * 4;    // floats of widened B/C per tile (8 s
 //        u = Delta*x -> LDS; keep D*x and silu(z) for post
 //  core: 32 tokens of the recurrence for the lane's (channel, state pair); partial
 //        readouts C*h of the pair -> LDS
-//  post: sum the 8 pairs' partials, add D*x, gate, store y
+//  post: sum the 8 pairs' partials, add D*x, gate, store (or add into) y
 // LOCAL = pass 1 of the chunked plan: start from zero, write only the chunk's end
-// state and its sum of Delta. Otherwise: outputs y (and h_final).
-template <typename IO, bool LOCAL, int CG>
+// state and its sum of Delta. Otherwise: outputs y (and final states).
+// REV = anti-causal: tiles, and tokens inside a tile, are taken from the last to the
+// first; the tiles stay where they are in memory, so loads and stores are the same.
+// PACKED = packed sequences (p.cu set): the state is reset to the sequence's initial state
+// before its first token (in the direction of the scan) and saved after its last.
+// Those events depend on the token only, so every branch on them is uniform; tiles
+// without an event take the same unrolled path as unpacked input.
+template <typename IO, bool LOCAL, bool REV, bool PACKED, int CG>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
     constexpr int kRowsPerPair = CG / 16;
@@ -208,7 +226,6 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     __shared__ float sBC[2 * kBcTile];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int g = blockIdx.x % p.ngroups;
     const int c = blockIdx.x / p.ngroups + p.chunk_offset;
     const int64_t b = g / p.groups_per_batch;
@@ -216,6 +233,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     const int64_t t_beg = (int64_t)c * p.chunk_len;
     const int64_t t_end = (t_beg + p.chunk_len < p.seqlen) ? t_beg + p.chunk_len : p.seqlen;
     const int ntiles = (int)((t_end - t_beg + kTile - 1) / kTile);
+    constexpr bool packed = PACKED;   // p.cu is set
 
     // core mapping: 16-lane row r -> state pair pr, channel block
     const int r = tid >> 4;
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                 if (p.chunk_state)
                     hv = *reinterpret_cast<const float2*>(
                         p.chunk_state + (row * p.nchunks + c) * kDState + 2 * pr);
-                else if (p.h0)
+                else if (p.h0 && !packed)
                     hv = *reinterpret_cast<const float2*>(p.h0 + row * kDState + 2 * pr);
             }
         }
@@ -261,6 +279,46 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     float* const bcdst = sBC + tid * 4;
     float dsum = 0.0f;
 
+    // ---- packed sequences: s is the sequence of the next token to be scanned, [lo, hi)
+    // its tokens. Past the last sequence lo = hi = -1, which matches no token.
+    int s = 0;
+    int64_t lo = 0, hi = 0;
+    bool reset_seen = false;
+    // final state of sequence i: the state, or (empty sequence) its initial state
+    auto save_final = [&](int i, bool empty) {
+        if (LOCAL || !p.h_final || !valid) return;
+        float2 v = make_float2(h[0], h[1]);
+        if (empty)
+            v = p.h0 ? *reinterpret_cast<const float2*>(p.h0 + ((int64_t)i * p.dim + d) * kDState + 2 * pr)
+                     : make_float2(0.f, 0.f);
+        *reinterpret_cast<float2*>(p.h_final + ((int64_t)i * p.dim + d) * kDState + 2 * pr) = v;
+    };
+    // step to the next non-empty sequence in scan order, saving the empty ones passed
+    auto next_seq = [&]() {
+        for (;;) {
+            s += REV ? -1 : 1;
+            if (s < 0 || s >= p.nseq) {
+                lo = hi = -1;
+                return;
+            }
+            lo = p.cu[s];
+            hi = p.cu[s + 1];
+            if (lo < hi) return;
+            save_final(s, true);
+        }
+    };
+    if (packed) {
+        s = seq_of(p.cu, p.nseq, REV ? t_end - 1 : t_beg);
+        lo = p.cu[s];
+        hi = p.cu[s + 1];
+        // the workgroup that scans the first token also saves the empty sequences
+        // that come before it in scan order
+        if (!REV && t_beg == 0)
+            for (int i = 0; i < s; ++i) save_final(i, true);
+        if (REV && t_end == p.seqlen)
+            for (int i = s + 1; i < p.nseq; ++i) save_final(i, true);
+    }
+
     float* const myDq = sD + cq * kLdsRow + 4 * jq;   // pre: this thread's 4 tokens
     float* const myUq = sU + cq * kLdsRow + 4 * jq;
     const float* const coreD = sD + cc * kLdsRow;     // core: the lane's channel
@@ -268,6 +326,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
 
     Raw4<IO> rx, rdl, rz;
     float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto tile_of = [&](int it) { return REV ? ntiles - 1 - it : it; };
     auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kTile;
         const int nvalid = (t_end - t0 < kTile) ? (int)(t_end - t0) : kTile;
@@ -283,10 +342,11 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     rx.zero();
     rdl.zero();
     rz.zero();
-    load_tile(0);
+    load_tile(tile_of(0));
     if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
 
-    for (int ti = 0; ti < ntiles; ++ti) {
+    for (int it = 0; it < ntiles; ++it) {
+        const int ti = tile_of(it);
         const int64_t t0 = t_beg + (int64_t)ti * kTile;
         const int nvalid = (t_end - t0 < kTile) ? (int)(t_end - t0) : kTile;
         const int nq = nvalid - 4 * jq;            // valid tokens of this thread's 4 (may be <= 0)
@@ -296,7 +356,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         rx.widen(xv);
         rdl.widen(dv);
         if (!LOCAL) rz.widen(zv);
-        if (ti + 1 < ntiles) load_tile(ti + 1);
+        if (it + 1 < ntiles) load_tile(tile_of(it + 1));
         float dl[4], uu[4], post_a[4], post_g[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -321,34 +381,75 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // Every lane of a row reads the same (B0, B1, C0, C1) of a token from LDS, so B
         // and C arrive in VGPRs and every op below is a plain VOP2 with VGPR operands
         // (the fast FP32 issue path; SGPR or DPP operands halve it).
-        const float* bct = sBC + (ti & 1) * kBcTile + pr * (kTile * 4);
+        const float* bct = sBC + (it & 1) * kBcTile + pr * (kTile * 4);
         float* const pout = sP + (pr * CG + cc) * kLdsRow;
-#pragma unroll
-        for (int tq = 0; tq < kTile; tq += 4) {
-            const float4 D4 = *reinterpret_cast<const float4*>(coreD + tq);
-            const float4 U4 = *reinterpret_cast<const float4*>(coreU + tq);
-            const float4 q0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
-            const float4 q1 = *reinterpret_cast<const float4*>(bct + (tq + 1) * 4);
-            const float4 q2 = *reinterpret_cast<const float4*>(bct + (tq + 2) * 4);
-            const float4 q3 = *reinterpret_cast<const float4*>(bct + (tq + 3) * 4);
-            float pp[4];
-#define SSM_TOKEN(S, DS, US, Q)                                                       \
+#define SSM_TOKEN(OUT, DS, US, Q)                                                     \
     {                                                                                 \
         const float e0 = fast_exp2(DS * a2[0]);                                       \
         const float e1 = fast_exp2(DS * a2[1]);                                       \
         h[0] = __builtin_fmaf(e0, h[0], Q.x * US);                                    \
         h[1] = __builtin_fmaf(e1, h[1], Q.y * US);                                    \
-        if (!LOCAL) pp[S] = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                    \
+        if (!LOCAL) OUT = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                      \
         else if (pr == 0) dsum += DS;                                                 \
     }
-            SSM_TOKEN(0, D4.x, U4.x, q0)
-            SSM_TOKEN(1, D4.y, U4.y, q1)
-            SSM_TOKEN(2, D4.z, U4.z, q2)
-            SSM_TOKEN(3, D4.w, U4.w, q3)
-#undef SSM_TOKEN
-            if (!LOCAL)
-                *reinterpret_cast<float4*>(pout + tq) = make_float4(pp[0], pp[1], pp[2], pp[3]);
+        // quiet tile: no sequence starts or ends inside it (always, for batch rows)
+        const int64_t tlast = t0 + nvalid - 1;
+        const bool quiet = !packed || (REV ? (hi - 1 != tlast && lo < t0)
+                                           : (lo != t0 && hi > tlast + 1));
+        if (quiet) {
+#pragma unroll
+            for (int gq = 0; gq < kTile; gq += 4) {
+                const int tq = REV ? kTile - 4 - gq : gq;
+                const float4 D4 = *reinterpret_cast<const float4*>(coreD + tq);
+                const float4 U4 = *reinterpret_cast<const float4*>(coreU + tq);
+                const float4 q0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
+                const float4 q1 = *reinterpret_cast<const float4*>(bct + (tq + 1) * 4);
+                const float4 q2 = *reinterpret_cast<const float4*>(bct + (tq + 2) * 4);
+                const float4 q3 = *reinterpret_cast<const float4*>(bct + (tq + 3) * 4);
+                float pp[4];
+                if (!REV) {
+                    SSM_TOKEN(pp[0], D4.x, U4.x, q0)
+                    SSM_TOKEN(pp[1], D4.y, U4.y, q1)
+                    SSM_TOKEN(pp[2], D4.z, U4.z, q2)
+                    SSM_TOKEN(pp[3], D4.w, U4.w, q3)
+                } else {
+                    SSM_TOKEN(pp[3], D4.w, U4.w, q3)
+                    SSM_TOKEN(pp[2], D4.z, U4.z, q2)
+                    SSM_TOKEN(pp[1], D4.y, U4.y, q1)
+                    SSM_TOKEN(pp[0], D4.x, U4.x, q0)
+                }
+                if (!LOCAL)
+                    *reinterpret_cast<float4*>(pout + tq) =
+                        make_float4(pp[0], pp[1], pp[2], pp[3]);
+            }
+        } else {
+            // token by token, with the sequence events (padding tokens have none)
+            for (int kk = 0; kk < kTile; ++kk) {
+                const int k = REV ? kTile - 1 - kk : kk;
+                const int64_t t = t0 + k;
+                const bool real = k < nvalid;
+                if (real && t == (REV ? hi - 1 : lo)) {     // first token of sequence s
+                    float2 hv = make_float2(0.f, 0.f);
+                    if (p.h0 && valid)
+                        hv = *reinterpret_cast<const float2*>(
+                            p.h0 + ((int64_t)s * p.dim + d) * kDState + 2 * pr);
+                    h[0] = hv.x;
+                    h[1] = hv.y;
+                    reset_seen = true;
+                }
+                const float ds = coreD[k];
+                const float us = coreU[k];
+                const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
+                float pk = 0.0f;
+                SSM_TOKEN(pk, ds, us, q)
+                if (!LOCAL) pout[k] = pk;
+                if (real && t == (REV ? lo : hi - 1)) {     // last token of sequence s
+                    save_final(s, false);
+                    next_seq();
+                }
+            }
         }
+#undef SSM_TOKEN
         __syncthreads();
 
         // ---- post: this thread's 4 tokens: sum the 8 pairs' partials, skip, gate, store
@@ -361,50 +462,72 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k) yv[k] = (yv[k] + post_a[k]) * post_g[k];
-            if (validq && nq > 0) Store4<IO>::store(yr + t0 + 4 * jq, vec, nq, yv);
+            if (validq && nq > 0) {
+                if (p.accumulate) {
+                    Raw4<IO> old;
+                    old.load(yr + t0 + 4 * jq, vec, nq);
+                    float ov[4];
+                    old.widen(ov);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) yv[k] += ov[k];
+                }
+                Store4<IO>::store(yr + t0 + 4 * jq, vec, nq, yv);
+            }
         }
         // the next tile's B/C into the other LDS buffer (its last readers finished
         // before the barrier above; its next readers come after the next barrier)
-        if (bc_mover && ti + 1 < ntiles)
-            *reinterpret_cast<float4*>(bcdst + ((ti + 1) & 1) * kBcTile) = rbc;
+        if (bc_mover && it + 1 < ntiles)
+            *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile) = rbc;
     }
 
-    if (!valid) return;
     if (LOCAL) {
+        if (packed && g == 0 && tid == 0) p.chunk_flag[c] = reset_seen ? 1 : 0;
+        if (!valid) return;
         *reinterpret_cast<float2*>(p.chunk_state + (row * p.nchunks + c) * kDState + 2 * pr) =
             make_float2(h[0], h[1]);
         if (pr == 0) p.chunk_sum[row * p.nchunks + c] = dsum;
-    } else if (p.h_final && c == p.nchunks - 1) {
+    } else if (!packed && valid && p.h_final && c == (REV ? 0 : p.nchunks - 1)) {
         *reinterpret_cast<float2*>(p.h_final + row * kDState + 2 * pr) = make_float2(h[0], h[1]);
     }
 }
 
 // ------------------------------------------------------------------ chunk carry
-// One thread per (row, n). In chunk order: the carried-in state of chunk c is
-// written over chunk_state[c]; then h <- exp(A*sum_c Delta)*h + local end state of c.
+// One thread per (row, n). In scan order: the carried-in state of chunk c is written
+// over chunk_state[c]; then h <- exp(A*sum_c Delta)*h + local end state of c, or just
+// the local end state when a packed sequence begins inside chunk c (the state after
+// the chunk then does not depend on what came before it).
 __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A,
                                                     const float* __restrict__ h0,
                                                     float* __restrict__ chunk_state,
                                                     const float* __restrict__ chunk_sum,
-                                                    int64_t nrows, int64_t dim, int nchunks) {
+                                                    const int32_t* __restrict__ chunk_flag,
+                                                    int64_t nrows, int64_t dim, int nchunks,
+                                                    int reverse) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nrows * kDState) return;
     const int64_t row = i / kDState;
     const int n = (int)(i % kDState);
     const int64_t d = row % dim;
     const float a2 = A[d * kDState + n] * kLog2e;
-    float h = h0 ? h0[row * kDState + n] : 0.0f;
+    float h = (h0 && !chunk_flag) ? h0[row * kDState + n] : 0.0f;
     float* st = chunk_state + row * (int64_t)nchunks * kDState + n;
     const float* sm = chunk_sum + row * (int64_t)nchunks;
-    // chunks 0..K-2 have a local end state and a sum of Delta; the last chunk only
-    // receives its carried-in state
-    for (int c = 0; c < nchunks - 1; ++c) {
+    // every chunk but the last in scan order has a local end state and a sum of
+    // Delta; the last only receives its carried-in state
+    for (int j = 0; j < nchunks - 1; ++j) {
+        const int c = reverse ? nchunks - 1 - j : j;
         const float loc = st[(int64_t)c * kDState];
         const float S = sm[c];
         st[(int64_t)c * kDState] = h;
-        h = __builtin_fmaf(fast_exp2(a2 * S), h, loc);
+        h = (chunk_flag && chunk_flag[c]) ? loc : __builtin_fmaf(fast_exp2(a2 * S), h, loc);
     }
-    st[(int64_t)(nchunks - 1) * kDState] = h;
+    st[(int64_t)(reverse ? 0 : nchunks - 1) * kDState] = h;
+}
+
+__global__ __launch_bounds__(256) void copy_state_kernel(const float* h0, float* out,
+                                                         int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = h0 ? h0[i] : 0.0f;
 }
 
 // ----------------------------------------------------------------- decode step
@@ -461,12 +584,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(const DecodeParams p)
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename IO, bool LOCAL>
+template <typename IO, bool LOCAL, bool REV, bool PACKED>
 hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
     switch (cg) {
-#define SSM_CASE(N)                                                                          \
-    case N:                                                                                  \
-        hipLaunchKernelGGL((scan_kernel<IO, LOCAL, N>), grid, dim3(N * 8), 0, stream, prm);  \
+#define SSM_CASE(N)                                                                  \
+    case N:                                                                          \
+        hipLaunchKernelGGL((scan_kernel<IO, LOCAL, REV, PACKED, N>), grid, dim3(N * 8), 0, \
+                           stream, prm);                                             \
         break;
         SSM_CASE(32)
         SSM_CASE(48)
@@ -478,6 +602,15 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
             return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename IO, bool LOCAL>
+hipError_t launch_scan_dir(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
+    if (prm.cu)
+        return prm.reverse ? launch_scan_kernel<IO, LOCAL, true, true>(cg, grid, stream, prm)
+                           : launch_scan_kernel<IO, LOCAL, false, true>(cg, grid, stream, prm);
+    return prm.reverse ? launch_scan_kernel<IO, LOCAL, true, false>(cg, grid, stream, prm)
+                       : launch_scan_kernel<IO, LOCAL, false, false>(cg, grid, stream, prm);
 }
 
 template <typename IO>
@@ -496,29 +629,31 @@ hipError_t launch_scan_t(const ScanPlan& plan, ScanParams prm, const void* B, co
         prm.chunk_state = nullptr;
         prm.chunk_offset = 0;
         if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
-        hipError_t e = launch_scan_kernel<IO, false>(cg, dim3((unsigned)prm.ngroups), stream, prm);
+        hipError_t e = launch_scan_dir<IO, false>(cg, dim3((unsigned)prm.ngroups), stream, prm);
         if (e == hipSuccess && ev1) e = hipEventRecord(ev1, stream);
         return e;
     }
-    // pass 1: chunks 0..K-2 from a zero state -> end states and sums of Delta
+    // pass 1: every chunk but the last in scan order, from a zero state -> end states
+    // and sums of Delta (and, for packed input, whether a sequence begins in the chunk)
     {
         ScanParams p1 = prm;
-        p1.chunk_offset = 0;
-        hipError_t e = launch_scan_kernel<IO, true>(
+        p1.chunk_offset = prm.reverse ? 1 : 0;
+        hipError_t e = launch_scan_dir<IO, true>(
             cg, dim3((unsigned)(prm.ngroups * (int64_t)(plan.nchunks - 1))), stream, p1);
         if (e != hipSuccess) return e;
     }
     {
         const int64_t nrows = prm.batch * prm.dim;
         hipLaunchKernelGGL(carry_kernel, dim3((unsigned)cdiv(nrows * kDState, 256)), dim3(256),
-                           0, stream, prm.A, prm.h0, prm.chunk_state, prm.chunk_sum, nrows,
-                           prm.dim, plan.nchunks);
+                           0, stream, prm.A, prm.cu ? nullptr : prm.h0, prm.chunk_state,
+                           prm.chunk_sum, prm.cu ? prm.chunk_flag : nullptr, nrows, prm.dim,
+                           plan.nchunks, prm.reverse);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     prm.chunk_offset = 0;
     if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
-    hipError_t e = launch_scan_kernel<IO, false>(
+    hipError_t e = launch_scan_dir<IO, false>(
         cg, dim3((unsigned)(prm.ngroups * (int64_t)plan.nchunks)), stream, prm);
     if (e == hipSuccess && ev1) e = hipEventRecord(ev1, stream);
     return e;
@@ -530,6 +665,13 @@ hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* 
                        bool bf16, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
     return bf16 ? launch_scan_t<uint16_t>(plan, prm, B, C, stream, ev_begin, ev_end)
                 : launch_scan_t<float>(plan, prm, B, C, stream, ev_begin, ev_end);
+}
+
+hipError_t launch_copy_state(const float* h0, float* h_final, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, h0,
+                       h_final, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream) {

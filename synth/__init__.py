@@ -186,6 +186,41 @@ def decode_token(cfg: DecodeConfig, step: int, device="cpu", seed: int | None = 
     }
 
 
+def length_mix(total: int, lo: int, hi: int, seed: int, empties: int = 0) -> list:
+    """Sequence lengths for packed input: log-uniform integers in [lo, hi] until
+    `total` tokens are used (the last one cut to fit), then `empties` zero-length
+    sequences inserted at seeded positions."""
+    g = _gen("cpu", seed, STREAM_STATE, 99)
+    lens = []
+    used = 0
+    while used < total:
+        u = float(torch.rand(1, generator=g, dtype=torch.float64))
+        n = int(round(math.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))))
+        n = max(1, min(n, total - used))
+        lens.append(n)
+        used += n
+    for _ in range(empties):
+        pos = int(torch.randint(0, len(lens) + 1, (1,), generator=g))
+        lens.insert(pos, 0)
+    return lens
+
+
+def cu_seqlens(lens, device="cpu") -> torch.Tensor:
+    """int32 offsets [0, l0, l0+l1, ...] of packed sequences."""
+    out = [0]
+    for n in lens:
+        out.append(out[-1] + int(n))
+    return torch.tensor(out, dtype=torch.int32, device=device)
+
+
+def packed_inputs(cfg: ScanConfig, total: int, device="cpu", seed: int | None = None) -> dict:
+    """Inputs of one packed call with `total` tokens: x, delta, z [dim][total];
+    B, C [total][dstate]; the same distributions as scan_inputs (drawn as one row)."""
+    one = scan_inputs(shrink(cfg, batch=1, seqlen=total), device, seed)
+    return {k: (v[0] if k in ("x", "delta", "z", "B", "C") and v is not None else v)
+            for k, v in one.items()}
+
+
 def shrink(cfg: ScanConfig, **kw) -> ScanConfig:
     """A copy of `cfg` with some sizes replaced (same distributions)."""
     d = dict(cfg.__dict__)

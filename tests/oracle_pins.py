@@ -313,6 +313,162 @@ def pin_elementwise(orc):
         assert abs((orc.silu(v) - orc.silu(-v)) - v) <= 1e-14 * max(1.0, abs(v)), v
 
 
+# ---------------------------------------------------------------------------
+# P11: the anti-causal (reverse-time) scan.
+# ---------------------------------------------------------------------------
+def pin_reverse_lti_convolution(orc):
+    """Delta, B, C constant: the reverse scan is the anti-causal convolution
+    y_t = sum_{s>=t} K_{s-t} x_s + D x_t, i.e. numpy.convolve on the reversed input."""
+    rng = np.random.default_rng(31)
+    dim, L, N = 2, 257, 6
+    A = -rng.uniform(0.2, 3.0, size=(dim, N))
+    delta_c = np.array([0.11, 0.43])
+    Bc = rng.standard_normal(N)
+    Cc = rng.standard_normal(N)
+    D = np.array([-0.75, 2.0])
+    x = rng.standard_normal((1, dim, L))
+    y, _ = orc.scan_reverse(x, np.zeros((1, dim, L)), A, np.tile(Bc, (1, L, 1)),
+                            np.tile(Cc, (1, L, 1)), D=D, delta_bias=delta_c,
+                            delta_softplus=False)
+    k = np.arange(L)
+    for d in range(dim):
+        dl = delta_c[d]
+        K = ((Cc * dl * Bc)[None, :] * np.exp(k[:, None] * dl * A[d][None, :])).sum(axis=1)
+        ref = np.convolve(x[0, d][::-1], K)[:L][::-1] + D[d] * x[0, d]
+        assert _rel(y[0, d], ref) < 1e-12, _rel(y[0, d], ref)
+        # y_t must not depend on x_s for s < t: the last output sees only the last input
+        assert abs(y[0, d, -1] - (K[0] + D[d]) * x[0, d, -1]) < 1e-12 * max(1, abs(y[0, d, -1]))
+
+
+def brute_force_reverse(x, dr, A, B, C, D, z, bias, softplus, h0):
+    """Reverse recurrence h_t = exp(Delta_t A) h_{t+1} + Delta_t B_t x_t, h_L = h0,
+    unrolled: with R_k = sum_{u>=k} Delta_u,
+    h_t = sum_{s>=t} exp(A (R_t - R_s)) Delta_s B_s x_s + exp(A R_t) h0,
+    y_t = (C_t . h_t + D x_t) silu(z_t); the final state is h_0."""
+    batch, dim, L = x.shape
+    N = A.shape[1]
+    v = dr + (0 if bias is None else bias[None, :, None])
+    delta = np.logaddexp(0.0, v) if softplus else v
+    y = np.zeros_like(x)
+    hf = np.zeros((batch, dim, N))
+    for b in range(batch):
+        for d in range(dim):
+            R = np.concatenate([np.cumsum(delta[b, d][::-1])[::-1], [0.0]])
+            for t in range(L):
+                hs = np.zeros(N)
+                for s in range(t, L):
+                    hs += np.exp(A[d] * (R[t] - R[s])) * delta[b, d, s] * B[b, s] * x[b, d, s]
+                if h0 is not None:
+                    hs += np.exp(A[d] * R[t]) * h0[b, d]
+                val = float(np.dot(C[b, t], hs))
+                if D is not None:
+                    val += D[d] * x[b, d, t]
+                if z is not None:
+                    zz = z[b, d, t]
+                    val *= zz / (1.0 + np.exp(-zz))
+                y[b, d, t] = val
+                if t == 0:
+                    hf[b, d] = hs
+    return y, hf
+
+
+def pin_reverse_brute_force(orc):
+    rng = np.random.default_rng(32)
+    batch, dim, L, N = 2, 2, 33, 4
+    A = -rng.uniform(0.1, 3.0, size=(dim, N))
+    x = rng.standard_normal((batch, dim, L))
+    dr = rng.normal(0, 0.5, size=(batch, dim, L))
+    bias = rng.normal(-1.0, 0.5, size=dim)
+    z = rng.standard_normal((batch, dim, L)) * 2
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    D = rng.standard_normal(dim)
+    h0 = rng.standard_normal((batch, dim, N))
+    for use_z, use_h0 in [(True, True), (False, False)]:
+        zz = z if use_z else None
+        hh = h0 if use_h0 else None
+        y, hf = orc.scan_reverse(x, dr, A, B, C, D=D, z=zz, delta_bias=bias, h0=hh)
+        y_ref, hf_ref = brute_force_reverse(x, dr, A, B, C, D, zz, bias, True, hh)
+        for b in range(batch):
+            for d in range(dim):
+                assert _rel(y[b, d], y_ref[b, d]) < 1e-11, (b, d)
+        assert _rel(hf, hf_ref) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# P12: packed (variable-length) sequences.
+# ---------------------------------------------------------------------------
+def _packed_problem(seed, lens, dim=3, N=5):
+    rng = np.random.default_rng(seed)
+    total = int(sum(lens))
+    return dict(
+        x=rng.standard_normal((dim, total)),
+        delta=rng.normal(0, 0.5, size=(dim, total)),
+        A=-rng.uniform(0.1, 3.0, size=(dim, N)),
+        B=rng.standard_normal((total, N)),
+        C=rng.standard_normal((total, N)),
+        D=rng.standard_normal(dim),
+        z=rng.standard_normal((dim, total)),
+        delta_bias=rng.normal(-1.0, 0.5, size=dim),
+    ), np.concatenate([[0], np.cumsum(lens)]).astype(np.int64), rng.standard_normal(
+        (len(lens), dim, N))
+
+
+def pin_varlen_brute_force(orc):
+    """Ragged lengths with empty and one-token sequences: each sequence against the
+    brute-force closed forms (forward and reverse), starting from its own h0; an
+    empty sequence's final state is its h0."""
+    lens = [5, 0, 1, 17, 0, 0, 9, 2]
+    p, cu, h0 = _packed_problem(33, lens)
+    for reverse, bf in [(False, brute_force), (True, brute_force_reverse)]:
+        y, hf = orc.scan_varlen(cu_seqlens=cu, h0=h0, reverse=reverse, **p)
+        for i in range(len(lens)):
+            a, b = int(cu[i]), int(cu[i + 1])
+            if a == b:
+                assert np.array_equal(hf[i], h0[i])
+                continue
+            yr, hr = bf(p["x"][None, :, a:b], p["delta"][None, :, a:b], p["A"],
+                        p["B"][None, a:b], p["C"][None, a:b], p["D"], p["z"][None, :, a:b],
+                        p["delta_bias"], True, h0[i][None])
+            assert _rel(y[:, a:b], yr[0]) < 1e-11, (reverse, i)
+            assert _rel(hf[i], hr[0]) < 1e-11, (reverse, i)
+
+
+def pin_varlen_equals_batched(orc):
+    """Equal lengths: packing is a relayout of a batch ([dim][b*L] <-> [b][dim][L])."""
+    batch, L = 3, 21
+    p, cu, h0 = _packed_problem(34, [L] * batch)
+    dim = p["x"].shape[0]
+    bt = {k: (v.reshape(dim, batch, L).transpose(1, 0, 2) if k in ("x", "delta", "z")
+              else v.reshape(batch, L, -1) if k in ("B", "C") else v) for k, v in p.items()}
+    for reverse in (False, True):
+        fn = orc.scan_reverse if reverse else orc.scan
+        yb, hb = fn(h0=h0, **bt)
+        y, hf = orc.scan_varlen(cu_seqlens=cu, h0=h0, reverse=reverse, **p)
+        assert np.array_equal(y, yb.transpose(1, 0, 2).reshape(dim, batch * L))
+        assert np.array_equal(hf, hb)
+
+
+def pin_varlen_isolation(orc):
+    """Nothing crosses a boundary: changing one sequence's inputs changes its own
+    outputs and leaves every other sequence's outputs bit-identical."""
+    lens = [7, 12, 1, 9]
+    p, cu, _ = _packed_problem(35, lens)
+    for reverse in (False, True):
+        y, hf = orc.scan_varlen(cu_seqlens=cu, reverse=reverse, **p)
+        q = {k: v.copy() for k, v in p.items()}
+        a, b = int(cu[1]), int(cu[2])
+        q["x"][:, a:b] += 1.0
+        q["B"][a:b] *= -1.0
+        y2, hf2 = orc.scan_varlen(cu_seqlens=cu, reverse=reverse, **q)
+        assert np.array_equal(y2[:, :a], y[:, :a]) and np.array_equal(y2[:, b:], y[:, b:])
+        assert not np.array_equal(y2[:, a:b], y[:, a:b])
+        assert np.array_equal(hf2[[0, 2, 3]], hf[[0, 2, 3]])
+        assert not np.array_equal(hf2[1], hf[1])
+
+
 ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response,
             pin_free_decay, pin_brute_force, pin_chunked_equals_unchunked,
-            pin_decode_equals_scan, pin_linearity_and_causality, pin_elementwise]
+            pin_decode_equals_scan, pin_linearity_and_causality, pin_elementwise,
+            pin_reverse_lti_convolution, pin_reverse_brute_force, pin_varlen_brute_force,
+            pin_varlen_equals_batched, pin_varlen_isolation]

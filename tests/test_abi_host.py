@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(b):
 
 
 def test_version_and_strings(b):
-    assert b.ssm_abi_version() == 1
+    assert b.ssm_abi_version() == 2
     assert b.ssm_status_string(0) == "ok"
     assert b.ssm_status_string(3) == "workspace too small"
     assert b.ssm_status_string(99) == "unknown status"
@@ -76,6 +76,8 @@ def test_scan_rejects(b, kw, status):
 
 def test_scan_rejects_bad_options(b):
     assert scan(b, opts=ctypes.byref(b.ScanOptions(48, 2, 0))) == 1   # not a multiple of 32
+    assert scan(b, opts=ctypes.byref(b.ScanOptions(0, 0, 0, None, None, 2, 0))) == 1  # reverse
+    assert scan(b, opts=ctypes.byref(b.ScanOptions(0, 0, 0, None, None, 0, -1))) == 1  # accumulate
     assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 3, 0))) == 1   # unknown plan
     assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 2, 40))) == 1  # group size
     assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 2, 112))) == 1
@@ -85,7 +87,7 @@ def test_scan_rejects_bad_options(b):
 def test_workspace_query(b):
     # single pass: B and C widened to fp32, per state quad, tokens padded to 32
     assert b.ssm_scan_workspace_bytes(4, 2048, 5120, 16, 1) == 4 * 2048 * 32 * 4
-    assert b.ssm_scan_workspace_bytes(1, 100, 16, 16, 0) == 128 * 32 * 4
+    assert b.ssm_scan_workspace_bytes(1, 100, 16, 16, 0, plan=1) == 128 * 32 * 4
     # forced chunking adds one state (16 fp32) and one sum per (row, chunk)
     ws = b.ssm_scan_workspace_bytes(2, 1000, 70, 16, 1, plan=2, chunk_len=64)
     k = 16
@@ -94,7 +96,7 @@ def test_workspace_query(b):
     sm = 2 * 70 * k * 4
     def up(v):
         return (v + 255) // 256 * 256
-    assert ws == up(up(up(bcq) + st) + sm)
+    assert ws == up(up(up(up(bcq) + st) + sm) + k * 4)
     assert b.ssm_scan_workspace_bytes(0, 10, 10, 16, 1) == 0
     assert b.ssm_scan_workspace_bytes(1, 10, 10, 8, 1) == 0
 
@@ -112,3 +114,37 @@ def test_state_update_rejects(b, kw, status):
     st = b.lib.ssm_state_update(p["state"], p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"],
                                 p["z"], p["bias"], 1, p["y"], batch, 32, dstate, io, None)
     assert st == status
+
+
+def varlen(b, total=100, dim=64, nseq=3, io=1, ws_bytes=None, **over):
+    p = dict(P, cu=0x7e0000000000)
+    p.update(over)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return b.lib.ssm_scan_varlen_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                     p["bias"], 1, p["cu"], nseq, p["h0"], p["y"], p["hf"], total,
+                                     dim, 16, io, p["ws"], ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), 1), (dict(nseq=0), 1), (dict(total=-1), 1), (dict(total=1 << 31), 1),
+    (dict(cu=0x7e0000000002), 2), (dict(dim=0), 1), (dict(ws=None), 3),
+    (dict(hf=P["h0"] + 16), 1), (dict(y=P["x"]), 1), (dict(h0=P["h0"] + 4), 2),
+    (dict(total=0, hf=P["h0"] + 16), 1), (dict(total=0, hf=P["hf"] + 4), 2),
+    (dict(total=0, dim=0), 1),
+])
+def test_varlen_rejects(b, kw, status):
+    assert varlen(b, **kw) == status
+    assert b.ssm_last_error() != ""
+
+
+def test_varlen_workspace_query(b):
+    assert b.ssm_scan_varlen_workspace_bytes(0, 64, 16, 1) == 0
+    assert (b.ssm_scan_varlen_workspace_bytes(1000, 64, 16, 1, plan=2, chunk_len=64)
+            == b.ssm_scan_workspace_bytes(1, 1000, 64, 16, 1, plan=2, chunk_len=64))
+    # chunked: B/C staging, chunk states, chunk sums, one flag per chunk
+    ws = b.ssm_scan_workspace_bytes(1, 1000, 64, 16, 1, plan=2, chunk_len=64)
+    def up(v):
+        return (v + 255) // 256 * 256
+    k = 16
+    assert ws == up(up(up(up(1024 * 32 * 4) + 64 * k * 16 * 4) + 64 * k * 4) + k * 4)

@@ -1,0 +1,226 @@
+"""GPU parity of the anti-causal scan (opts.reverse), the bidirectional sum
+(opts.accumulate) and packed variable-length sequences (ssm_scan_varlen_fwd),
+through the C ABI, against the fp64 oracle.
+
+Small shapes with ragged tails are checked on every row in the single-pass and
+the chunked plan; the Mamba-2.8B layer shape is checked on sampled rows in the
+launch configuration the benchmark uses; integer-exact inputs check the state
+resets at sequence boundaries bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_53_amd import binding  # noqa: F401  (fails loudly if unbuilt)
+
+
+VARIANTS = [dict(use_z=True, use_D=True), dict(use_z=False, use_D=False)]
+PLANS = [(1, 0), (2, 64), (2, 96)]
+
+
+def _h0(shape, seed):
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(shape, generator=gen).to(DEV)
+
+
+# ------------------------------------------------------------------ reverse scan
+@pytest.mark.parametrize("shape", [(1, 256, 16, "f32"), (2, 1000, 200, "bf16"),
+                                   (1, 333, 70, "bf16"), (3, 1, 5, "f32"), (1, 33, 65, "f32"),
+                                   (1, 4103, 130, "bf16")],
+                         ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
+@pytest.mark.parametrize("plan,chunk", PLANS, ids=["single", "c64", "c96"])
+def test_reverse_all_rows(shape, plan, chunk):
+    batch, L, dim, io = shape
+    cfg = synth.ScanConfig("rev", batch, L, dim, io=io, seed=700 + L)
+    say("case reverse", shape, plan, chunk)
+    inp = synth.scan_inputs(cfg, DEV)
+    h0 = _h0((batch, dim, 16), L)
+    for var in VARIANTS:
+        y, hf = parity.gpu_scan(inp, h0=h0, plan=plan, chunk_len=chunk, reverse=True, **var)
+        torch.cuda.synchronize()
+        yr, hr = oracle.Oracle().scan_reverse(
+            inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+            D=inp["D"] if var["use_D"] else None, z=inp["z"] if var["use_z"] else None,
+            delta_bias=inp["delta_bias"], h0=h0, nthreads=parity.threads())
+        ey, eh = parity.rowwise_err(y, yr), parity.rowwise_err(hf, hr)
+        say(f"  {var}: y {ey:.3e} h {eh:.3e}")
+        assert ey <= parity.TOL[io] and eh <= parity.TOL[io]
+
+
+@pytest.mark.parametrize("name,nrows", [("m2p8", 64), ("long", 4)])
+def test_reverse_full_size_sampled_rows(name, nrows):
+    cfg = synth.CONFIGS[name]
+    say("case reverse full size", name)
+    inp = synth.scan_inputs(cfg, DEV)
+    y, hf = parity.gpu_scan(inp, reverse=True)
+    torch.cuda.synchronize()
+    rb, rd = parity.sample_rows(cfg.batch, cfg.dim, nrows, seed=cfg.seed + 1)
+    yr, hr = parity.oracle_reverse_rows(inp, rb, rd)
+    sel = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
+    ey, eh = parity.rowwise_err(y[sel], yr), parity.rowwise_err(hf[sel], hr)
+    say(f"{name} reverse: rows {len(rb)} y {ey:.3e} h {eh:.3e}")
+    assert ey <= parity.TOL[cfg.io] and eh <= parity.TOL[cfg.io]
+
+
+@pytest.mark.parametrize("shape", [(1, 256, 16, "f32"), (2, 1000, 200, "bf16")],
+                         ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
+@pytest.mark.parametrize("plan,chunk", [(1, 0), (2, 64)], ids=["single", "c64"])
+def test_bidirectional_sum(shape, plan, chunk):
+    """Causal scan, then the anti-causal scan added into the same y: the sum of the
+    two oracle outputs (each direction rounded to io_dtype once on the GPU)."""
+    batch, L, dim, io = shape
+    cfg = synth.ScanConfig("bidir", batch, L, dim, io=io, seed=800 + L)
+    say("case bidirectional", shape, plan, chunk)
+    inp = synth.scan_inputs(cfg, DEV)
+    y = parity.gpu_scan(inp, final=False, plan=plan, chunk_len=chunk)
+    from selective_state_space_53_amd import binding
+    binding.ssm_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                         z=inp["z"], delta_bias=inp["delta_bias"], y=y, plan=plan,
+                         chunk_len=chunk, reverse=True, accumulate=True)
+    torch.cuda.synchronize()
+    orc = oracle.Oracle()
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
+    kw = dict(D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], nthreads=parity.threads())
+    yf, _ = orc.scan(*args, **kw)
+    yb, _ = orc.scan_reverse(*args, **kw)
+    e = parity.rowwise_err(y, yf + yb)
+    say(f"  bidirectional y err {e:.3e}")
+    assert e <= parity.TOL[io]
+
+
+# ------------------------------------------------------------- packed sequences
+PACKED = [
+    # (lengths, dim, io)
+    ([5, 0, 1, 17, 0, 0, 40, 2, 31, 32, 33, 1], 70, "f32"),
+    ([300, 1, 1, 64, 0, 700, 3], 160, "bf16"),
+    ([1] * 37, 32, "f32"),
+    ([4103], 130, "bf16"),
+    ([0, 0, 1000, 0], 96, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=lambda c: "n{}_T{}_d{}_{}".format(
+    len(c[0]), sum(c[0]), c[1], c[2]))
+@pytest.mark.parametrize("plan,chunk", PLANS, ids=["single", "c64", "c96"])
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_packed_all_rows(case, plan, chunk, reverse):
+    lens, dim, io = case
+    total = sum(lens)
+    cfg = synth.ScanConfig("packed", 1, total, dim, io=io, seed=900 + total)
+    say("case packed", len(lens), total, dim, io, plan, chunk, reverse)
+    inp = synth.packed_inputs(cfg, total, DEV)
+    cu = synth.cu_seqlens(lens, DEV)
+    h0 = _h0((len(lens), dim, 16), total)
+    for var, use_h0 in [(VARIANTS[0], True), (VARIANTS[1], False)]:
+        hh = h0 if use_h0 else None
+        y, hf = parity.gpu_varlen(inp, cu, h0=hh, plan=plan, chunk_len=chunk, reverse=reverse,
+                                  **var)
+        torch.cuda.synchronize()
+        yr, hr = parity.oracle_varlen(inp, cu, h0=hh, reverse=reverse, **var)
+        ey, eh = parity.rowwise_err(y, yr), parity.rowwise_err(hf, hr)
+        say(f"  {var} h0={use_h0}: y {ey:.3e} h {eh:.3e}")
+        assert ey <= parity.TOL[io] and eh <= parity.TOL[io]
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_packed_full_size_sampled_channels(reverse):
+    """The Mamba-2.8B layer (dim 5120) over 8192 packed tokens with a log-uniform
+    length mix (16..2048) and empty sequences, in the library's own plan."""
+    cfg = synth.CONFIGS["m2p8"]
+    total = cfg.batch * cfg.seqlen
+    lens = synth.length_mix(total, 16, 2048, seed=cfg.seed, empties=3)
+    say("case packed full size", len(lens), total, reverse)
+    inp = synth.packed_inputs(cfg, total, DEV)
+    cu = synth.cu_seqlens(lens, DEV)
+    h0 = _h0((len(lens), cfg.dim, 16), 11)
+    y, hf = parity.gpu_varlen(inp, cu, h0=h0, reverse=reverse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    ch = np.unique(np.concatenate([[0, 79, 80, cfg.dim - 1], rng.integers(0, cfg.dim, 40)]))
+    yr, hr = parity.oracle_varlen(inp, cu, h0=h0, reverse=reverse, channels=ch)
+    sel = torch.as_tensor(ch, device=DEV)
+    ey, eh = parity.rowwise_err(y[sel], yr), parity.rowwise_err(hf[:, sel], hr)
+    say(f"  packed m2p8 reverse={reverse}: channels {len(ch)} y {ey:.3e} h {eh:.3e}")
+    assert ey <= parity.TOL[cfg.io] and eh <= parity.TOL[cfg.io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_packed_integer_exact(io, reverse):
+    """A = 0, Delta = 1 (softplus off): integer state sums, exact in fp32 and bf16,
+    so every reset at a sequence boundary is checked bit for bit -- boundaries on
+    and next to tile (32) and chunk (64) edges, empty and one-token sequences."""
+    lens = [31, 1, 32, 0, 33, 64, 63, 65, 1, 0, 96, 127, 5]
+    total = sum(lens)
+    dim = 40
+    rng = np.random.default_rng(3 if reverse else 4)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    x = np.zeros((dim, total))
+    for d in range(dim):
+        idx = rng.choice(total, size=12, replace=False)
+        x[d, idx] = rng.choice([-1.0, 1.0], size=12)
+    inp = {
+        "x": torch.tensor(x, dtype=dt, device=DEV),
+        "delta": torch.ones((dim, total), dtype=dt, device=DEV),
+        "z": None,
+        "B": torch.tensor(rng.integers(-1, 2, size=(total, 16)), dtype=dt, device=DEV),
+        "C": torch.tensor(rng.integers(-1, 2, size=(total, 16)), dtype=dt, device=DEV),
+        "A": torch.zeros((dim, 16), dtype=torch.float32, device=DEV),
+        "D": torch.tensor(rng.integers(-2, 3, size=dim), dtype=torch.float32, device=DEV),
+        "delta_bias": None,
+    }
+    cu = synth.cu_seqlens(lens, DEV)
+    h0 = torch.tensor(rng.integers(-3, 4, size=(len(lens), dim, 16)), dtype=torch.float32,
+                      device=DEV)
+    from selective_state_space_53_amd import binding
+    for plan, chunk in PLANS:
+        say("case packed integer", io, reverse, plan, chunk)
+        y, hf = binding.ssm_scan_varlen_fwd(
+            inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], cu, D=inp["D"],
+            delta_softplus=False, h0=h0, return_final_state=True, plan=plan, chunk_len=chunk,
+            reverse=reverse)
+        torch.cuda.synchronize()
+        yr, hr = oracle.Oracle().scan_varlen(
+            inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+            oracle.f64(cu).astype(np.int64), D=inp["D"], delta_softplus=False, h0=h0,
+            reverse=reverse)
+        assert np.array_equal(oracle.f64(y), yr)
+        assert np.array_equal(oracle.f64(hf), hr)
+
+
+def test_packed_no_tokens():
+    """total = 0: every sequence is empty; h_final = h0 (or zeros), also in place."""
+    from selective_state_space_53_amd import binding
+    dim, nseq = 24, 3
+    x = torch.empty((dim, 0), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((0, 16), dtype=torch.bfloat16, device=DEV)
+    A = -torch.ones((dim, 16), device=DEV)
+    cu = torch.zeros(nseq + 1, dtype=torch.int32, device=DEV)
+    h0 = _h0((nseq, dim, 16), 1)
+    _, hf = binding.ssm_scan_varlen_fwd(x, x, A, B, B, cu, h0=h0, return_final_state=True)
+    _, hz = binding.ssm_scan_varlen_fwd(x, x, A, B, B, cu, return_final_state=True)
+    keep = h0.clone()
+    binding.ssm_scan_varlen_fwd(x, x, A, B, B, cu, h0=h0, h_final=h0, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(hf, keep) and torch.equal(h0, keep)
+    assert torch.count_nonzero(hz) == 0

@@ -59,3 +59,43 @@ def test_mutant_is_caught(tmp_path, name, old, new):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
+
+
+# Mistakes planted in the Python compositions of oracle/__init__.py (the reverse
+# scan and packed sequences are built there from the C scan).
+PY_MUTANTS = [
+    ("rev_B_not_reversed", "rB = f64(B)[:, ::-1]", "rB = f64(B)"),
+    ("rev_C_not_reversed", "rC = f64(C)[:, ::-1]", "rC = f64(C)"),
+    ("rev_z_not_reversed", "rz = None if z is None else f64(z)[:, :, ::-1]",
+     "rz = None if z is None else f64(z)"),
+    ("rev_output_not_reversed", "return np.ascontiguousarray(y[:, :, ::-1]), hf",
+     "return np.ascontiguousarray(y), hf"),
+    ("varlen_h0_of_previous_seq", "start = None if h0f is None else h0f[i][None]",
+     "start = None if h0f is None else h0f[max(i - 1, 0)][None]"),
+    ("varlen_state_carried_across", "start = None if h0f is None else h0f[i][None]",
+     "start = hf[i - 1][None] if i > 0 else None"),
+    ("varlen_empty_final_zero", "hf[i] = 0.0 if start is None else start[0]", "hf[i] = 0.0"),
+    ("varlen_C_from_row_start", "Cf[None, a:b]", "Cf[None, 0:b - a]"),
+    ("varlen_reverse_ignored", "fn = self.scan_reverse if reverse else self.scan",
+     "fn = self.scan"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_is_caught(tmp_path, name, old, new):
+    import importlib.util
+    src = open(os.path.join(SRC_DIR, "__init__.py")).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    path = tmp_path / f"oracle_{name}.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"oracle_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    orc = mod.Oracle(oracle.build(force=False))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
