@@ -194,6 +194,51 @@ ssm_status ssm_state_update(float* state, const void* x, const void* delta, cons
                             int64_t batch, int64_t dim, int64_t dstate, ssm_dtype io_dtype,
                             void* stream);
 
+/*
+ * Causal depthwise convolution of width 4 per channel, then SiLU: the local mixing
+ * the Mamba block applies to the projected input before the selective scan
+ * (sivaro, "The Architecture in Practice": a channel-wise Conv1d with d_conv = 4
+ * and a SiLU after it). The printed layer has no padding; the reading taken here is
+ * causal left padding by width-1, so the output is as long as the input and never
+ * looks ahead:
+ *
+ *   y[b,d,t] = act(bias[d] + sum_{k<width} weight[d,k] * x[b,d,t-(width-1)+k])
+ *
+ * where inputs before t = 0 come from conv_state (zeros when NULL) and act is SiLU
+ * (activation = 1) or the identity (0). The conv output feeds the projections that
+ * give Delta, B and C, so it is written out rather than fused into the scan.
+ *
+ *   x              [batch][dim][seqlen] io_dtype
+ *   weight         [dim][width] fp32 (16-byte aligned)
+ *   bias           [dim] fp32 or NULL
+ *   conv_state     [batch][dim][width-1] io_dtype or NULL: the width-1 inputs before
+ *                  x[.,.,0], oldest first (the state a previous call returned)
+ *   y              [batch][dim][seqlen] io_dtype out; overlaps nothing
+ *   conv_state_out [batch][dim][width-1] io_dtype out or NULL: the last width-1
+ *                  inputs of [conv_state, x] (for a following call or decode);
+ *                  overlaps nothing (not even conv_state)
+ * batch, seqlen, dim >= 1; width must be 4. x and y 16-byte aligned; conv states
+ * aligned to their element.
+ */
+ssm_status ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                                 const void* conv_state, void* y, void* conv_state_out,
+                                 int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                                 int activation, ssm_dtype io_dtype, void* stream);
+
+/*
+ * One decode token through the same convolution, with the rolling state updated in
+ * place: y = act(bias + sum_k weight[.,k] * [conv_state, x][k]), then conv_state =
+ * its last width-2 entries followed by x.
+ *
+ *   conv_state  [batch][dim][width-1] io_dtype, in/out
+ *   x, y        [batch][dim] io_dtype (y out; overlaps nothing)
+ *   weight, bias, width, activation as for ssm_causal_conv1d_fwd
+ */
+ssm_status ssm_causal_conv1d_update(void* conv_state, const void* x, const float* weight,
+                                    const float* bias, void* y, int64_t batch, int64_t dim,
+                                    int64_t width, int activation, ssm_dtype io_dtype,
+                                    void* stream);
+
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* ssm_status_string(ssm_status s);
 /* Thread-local detail of the last non-OK status returned on this thread ("" if none). */

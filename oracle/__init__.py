@@ -4,10 +4,11 @@ Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of `bench.py`
 may import this package. The product path (the HIP library and its binding) never
 does: it shares no code with it and fails loudly when its own library is missing.
 
-The arithmetic lives in `ssm_oracle.c` (plain C, fp64, one sequential loop per
-row; see `ssm_oracle.h` for the recurrence and where each part of it comes from
-on the pages). This module only builds that file with gcc, widens inputs exactly
-to fp64 and calls it through ctypes.
+The scan's arithmetic lives in `ssm_oracle.c` (plain C, fp64, one sequential loop
+per row; see `ssm_oracle.h` for the recurrence and where each part of it comes
+from on the pages). This module builds that file with gcc, widens inputs exactly
+to fp64 and calls it through ctypes; the reverse-time and packed scans are defined
+here from it, and the causal convolution before the scan is plain numpy in fp64.
 
 Every oracle function is pinned by CPU tests against things other than itself
 (closed forms, library routines, brute force, invariants): see tests/test_oracle_pins.py.
@@ -178,6 +179,47 @@ class Oracle:
             y[:, a:b] = yi[0]
             hf[i] = hi[0]
         return y, hf
+
+    # ---- causal depthwise convolution + SiLU (the step before the scan) ----
+    @staticmethod
+    def conv1d(x, weight, bias=None, state=None, silu=True):
+        """Causal depthwise convolution of width K per channel, then SiLU:
+            out[b,d,t] = silu(bias[d] + sum_{k<K} weight[d,k] * x[b,d,t-(K-1)+k])
+        (the channel-wise Conv1d with groups = channels and the SiLU after it in the
+        Mamba block: sivaro, "The Architecture in Practice"). Inputs before t = 0 come
+        from `state` [b][d][K-1] (oldest first), zeros when None -- the left padding
+        that keeps the layer causal and the output as long as the input.
+        Returns (out [b][d][L], new state = the last K-1 inputs of [state, x])."""
+        x = f64(x)
+        w = f64(weight)
+        b_, d_, L = x.shape
+        K = w.shape[1]
+        st = np.zeros((b_, d_, K - 1)) if state is None else f64(state)
+        xp = np.concatenate([st, x], axis=2)            # xp[..., j] = x[..., j - (K-1)]
+        acc = np.zeros((b_, d_, L))
+        if bias is not None:
+            acc += f64(bias)[None, :, None]
+        for k in range(K):
+            acc += w[None, :, k, None] * xp[:, :, k:k + L]
+        out = acc / (1.0 + np.exp(-acc)) if silu else acc
+        return out, np.ascontiguousarray(xp[:, :, L:])
+
+    @staticmethod
+    def conv1d_step(state, x, weight, bias=None, silu=True):
+        """One decode token: state [b][d][K-1] holds the last K-1 inputs (oldest first),
+        x [b][d]. Returns (out [b][d], state shifted by one with x appended)."""
+        st = f64(state)
+        x = f64(x)
+        w = f64(weight)
+        K = w.shape[1]
+        window = np.concatenate([st, x[:, :, None]], axis=2)   # the last K inputs
+        acc = np.zeros(x.shape)
+        if bias is not None:
+            acc += f64(bias)[None, :]
+        for k in range(K):
+            acc += w[None, :, k] * window[:, :, k]
+        out = acc / (1.0 + np.exp(-acc)) if silu else acc
+        return out, np.ascontiguousarray(window[:, :, 1:])
 
     # ---- decode step ----------------------------------------------------
     def step(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None,

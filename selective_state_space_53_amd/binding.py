@@ -22,8 +22,8 @@ SSM_OK, SSM_ERR_INVALID_ARGUMENT, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE_TOO_SMA
     SSM_ERR_HIP = range(5)
 SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_scan_varlen_workspace_bytes",
-           "ssm_scan_varlen_fwd", "ssm_state_update", "ssm_status_string", "ssm_last_error",
-           "ssm_abi_version")
+           "ssm_scan_varlen_fwd", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
+           "ssm_state_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
 
 class ScanOptions(ctypes.Structure):
@@ -51,6 +51,12 @@ lib.ssm_scan_varlen_fwd.restype = ctypes.c_int
 lib.ssm_scan_varlen_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                     _i64, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp,
                                     ctypes.c_size_t, ctypes.POINTER(ScanOptions), _vp]
+lib.ssm_causal_conv1d_fwd.restype = ctypes.c_int
+lib.ssm_causal_conv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                      ctypes.c_int, ctypes.c_int, _vp]
+lib.ssm_causal_conv1d_update.restype = ctypes.c_int
+lib.ssm_causal_conv1d_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int,
+                                         ctypes.c_int, _vp]
 lib.ssm_state_update.restype = ctypes.c_int
 lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                  _i64, _i64, _i64, ctypes.c_int, _vp]
@@ -211,6 +217,53 @@ def ssm_scan_varlen_fwd(x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bia
             total, dim, N, code, _ptr(workspace), 0 if workspace is None else workspace.numel(),
             opts, s))
     return (y, h_final) if return_final_state else y
+
+
+def ssm_causal_conv1d_fwd(x, weight, bias=None, conv_state=None, activation=True,
+                          return_state=False, y=None, conv_state_out=None, stream=None):
+    """x: [batch][dim][seqlen]; weight: [dim][4] fp32; bias: [dim] fp32; conv_state:
+    [batch][dim][3] (x's dtype). Returns y (and the new conv state)."""
+    _dev(x, "x")
+    io = x.dtype
+    batch, dim, seqlen = x.shape
+    width = weight.shape[-1]
+    _dev(weight, "weight", torch.float32, (dim, width))
+    _dev(bias, "bias", torch.float32, (dim,))
+    _dev(conv_state, "conv_state", io, (batch, dim, width - 1))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", io, x.shape)
+    if return_state and conv_state_out is None:
+        conv_state_out = torch.empty((batch, dim, width - 1), dtype=io, device=x.device)
+    _dev(conv_state_out, "conv_state_out", io, (batch, dim, width - 1))
+    with torch.cuda.device(x.device):
+        s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib.ssm_causal_conv1d_fwd(
+            _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(y), _ptr(conv_state_out),
+            batch, seqlen, dim, width, int(bool(activation)), _dtype_code(x), s))
+    return (y, conv_state_out) if return_state else y
+
+
+def ssm_causal_conv1d_update(conv_state, x, weight, bias=None, activation=True, y=None,
+                             stream=None):
+    """conv_state: [batch][dim][3] (x's dtype), updated in place; x: [batch][dim].
+    Returns y [batch][dim]."""
+    _dev(x, "x")
+    io = x.dtype
+    batch, dim = x.shape
+    width = weight.shape[-1]
+    _dev(weight, "weight", torch.float32, (dim, width))
+    _dev(bias, "bias", torch.float32, (dim,))
+    _dev(conv_state, "conv_state", io, (batch, dim, width - 1))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", io, x.shape)
+    with torch.cuda.device(x.device):
+        s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib.ssm_causal_conv1d_update(
+            _ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias), _ptr(y), batch, dim, width,
+            int(bool(activation)), _dtype_code(x), s))
+    return y
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -23,6 +23,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+KERNEL_SOURCES = ["ssm_kernels.hip", "ssm_conv.hip"]
 
 
 def _run(cmd, verbose):
@@ -40,22 +41,25 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, save_temps: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
-    k_obj = os.path.join(BUILD_DIR, "ssm_kernels.o")
     a_obj = os.path.join(BUILD_DIR, "ssm_abi.o")
     extra = []
     if save_temps:
         extra = ["--save-temps"]
+    k_objs = []
     cwd = os.getcwd()
     try:
         os.chdir(BUILD_DIR)  # --save-temps writes next to the working directory
-        _run(["hipcc", "-c", *DEVICE_FLAGS, *inc, *extra,
-              os.path.join(CSRC, "ssm_kernels.hip"), "-o", k_obj], verbose)
+        for src in KERNEL_SOURCES:
+            obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+            _run(["hipcc", "-c", *DEVICE_FLAGS, *inc, *extra, os.path.join(CSRC, src), "-o", obj],
+                 verbose)
+            k_objs.append(obj)
     finally:
         os.chdir(cwd)
     _run(["hipcc", "-c", *HOST_FLAGS, *inc, os.path.join(CSRC, "ssm_abi.cpp"), "-o", a_obj],
          verbose)
     tmp = LIB + ".tmp"
-    _run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", k_obj, a_obj, "-o", tmp],
+    _run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *k_objs, a_obj, "-o", tmp],
          verbose)
     os.replace(tmp, LIB)
     return LIB

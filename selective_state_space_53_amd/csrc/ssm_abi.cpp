@@ -458,6 +458,137 @@ ssm_status ssm_scan_varlen_fwd(const void* x, const void* delta, const float* A,
     }
 }
 
+ssm_status ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                                 const void* conv_state, void* y, void* conv_state_out,
+                                 int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                                 int activation, ssm_dtype io_dtype, void* stream) {
+    try {
+        if (io_dtype != SSM_F32 && io_dtype != SSM_BF16)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "io_dtype %d is not SSM_F32 or SSM_BF16",
+                        (int)io_dtype);
+        if (batch <= 0 || seqlen <= 0 || dim <= 0 || width <= 0)
+            return fail(SSM_ERR_INVALID_ARGUMENT,
+                        "sizes must be >= 1 (batch=%lld seqlen=%lld dim=%lld width=%lld)",
+                        (long long)batch, (long long)seqlen, (long long)dim, (long long)width);
+        if (width != 4)
+            return fail(SSM_ERR_UNSUPPORTED, "width=%lld: only width 4 is supported",
+                        (long long)width);
+        if (activation != 0 && activation != 1)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "activation must be 0 (none) or 1 (SiLU)");
+        if (!x || !weight || !y)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "x, weight and y are required");
+        const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
+        int64_t io, stb;
+        if (!bytes4(batch, dim, seqlen, elem, &io) || !bytes4(batch, dim, width - 1, elem, &stb))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "tensor size overflows");
+        struct {
+            const char* name;
+            const void* p;
+            uintptr_t align;
+        } al[] = {{"x", x, 16}, {"y", y, 16}, {"weight", weight, 16}, {"bias", bias, 4},
+                  {"conv_state", conv_state, 2}, {"conv_state_out", conv_state_out, 2}};
+        for (auto& a : al)
+            if (a.p && !aligned(a.p, a.align))
+                return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
+                            (unsigned)a.align);
+        const Region outs[] = {region("y", y, io), region("conv_state_out", conv_state_out, stb)};
+        const Region ins[] = {region("x", x, io), region("weight", weight, dim * width * 4),
+                              region("bias", bias, dim * 4),
+                              region("conv_state", conv_state, stb)};
+        for (const Region& o : outs)
+            for (const Region& r : ins)
+                if (overlaps(o, r))
+                    return fail(SSM_ERR_INVALID_ARGUMENT, "%s overlaps %s", o.name, r.name);
+        if (overlaps(outs[0], outs[1]))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps conv_state_out");
+        ssm::ConvParams prm{};
+        prm.x = x;
+        prm.w = weight;
+        prm.bias = bias;
+        prm.state_in = conv_state;
+        prm.y = y;
+        prm.state_out = conv_state_out;
+        prm.rows = batch * dim;
+        prm.seqlen = seqlen;
+        prm.dim = dim;
+        prm.silu = activation;
+        prm.aligned = ((seqlen * elem) % 16) == 0;
+        const hipError_t e = ssm::launch_conv1d_fwd(prm, io_dtype == SSM_BF16,
+                                                    static_cast<hipStream_t>(stream));
+        if (e != hipSuccess)
+            return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        return SSM_OK;
+    } catch (...) {
+        return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
+    }
+}
+
+ssm_status ssm_causal_conv1d_update(void* conv_state, const void* x, const float* weight,
+                                    const float* bias, void* y, int64_t batch, int64_t dim,
+                                    int64_t width, int activation, ssm_dtype io_dtype,
+                                    void* stream) {
+    try {
+        if (io_dtype != SSM_F32 && io_dtype != SSM_BF16)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "io_dtype %d is not SSM_F32 or SSM_BF16",
+                        (int)io_dtype);
+        if (batch <= 0 || dim <= 0 || width <= 0)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (batch=%lld dim=%lld "
+                        "width=%lld)", (long long)batch, (long long)dim, (long long)width);
+        if (width != 4)
+            return fail(SSM_ERR_UNSUPPORTED, "width=%lld: only width 4 is supported",
+                        (long long)width);
+        if (activation != 0 && activation != 1)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "activation must be 0 (none) or 1 (SiLU)");
+        if (!conv_state || !x || !weight || !y)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "conv_state, x, weight and y are required");
+        const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
+        int64_t io, stb;
+        if (!bytes4(batch, dim, 1, elem, &io) || !bytes4(batch, dim, width - 1, elem, &stb))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "tensor size overflows");
+        struct {
+            const char* name;
+            const void* p;
+            uintptr_t align;
+        } al[] = {{"x", x, 2}, {"y", y, 2}, {"weight", weight, 16}, {"bias", bias, 4},
+                  {"conv_state", conv_state, 2}};
+        for (auto& a : al)
+            if (a.p && !aligned(a.p, a.align))
+                return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
+                            (unsigned)a.align);
+        if (elem == 4 && (!aligned(x, 4) || !aligned(y, 4) || !aligned(conv_state, 4)))
+            return fail(SSM_ERR_UNSUPPORTED, "fp32 buffers must be 4-byte aligned");
+        const Region outs[] = {region("y", y, io), region("conv_state", conv_state, stb)};
+        const Region ins[] = {region("x", x, io), region("weight", weight, dim * width * 4),
+                              region("bias", bias, dim * 4)};
+        for (const Region& o : outs)
+            for (const Region& r : ins)
+                if (overlaps(o, r))
+                    return fail(SSM_ERR_INVALID_ARGUMENT, "%s overlaps %s", o.name, r.name);
+        if (overlaps(outs[0], outs[1]))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps conv_state");
+        ssm::ConvParams prm{};
+        prm.x = x;
+        prm.w = weight;
+        prm.bias = bias;
+        prm.y = y;
+        prm.state_out = conv_state;
+        prm.rows = batch * dim;
+        prm.seqlen = 1;
+        prm.dim = dim;
+        prm.silu = activation;
+        // whole groups of 8 rows use full-width accesses when every buffer is 16-byte
+        // aligned (then 8 rows of x, y and state start on 16-byte boundaries)
+        prm.aligned = aligned(x, 16) && aligned(y, 16) && aligned(conv_state, 16);
+        const hipError_t e = ssm::launch_conv1d_update(prm, io_dtype == SSM_BF16,
+                                                       static_cast<hipStream_t>(stream));
+        if (e != hipSuccess)
+            return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        return SSM_OK;
+    } catch (...) {
+        return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
+    }
+}
+
 ssm_status ssm_state_update(float* state, const void* x, const void* delta, const float* A,
                             const void* B, const void* C, const float* D, const void* z,
                             const float* delta_bias, int delta_softplus, void* y,

@@ -58,6 +58,17 @@ struct DecodeParams {
     int32_t softplus;
 };
 
+struct ConvParams {
+    const void* x;          // [rows][seqlen] (decode: [rows])
+    const float* w;         // [dim][4]
+    const float* bias;      // [dim] or null
+    const void* state_in;   // [rows][3] or null (zeros)
+    void* y;                // like x
+    void* state_out;        // [rows][3] or null; the decode update reads and writes it
+    int64_t rows, seqlen, dim;
+    int32_t silu, aligned;
+};
+
 // ev_begin / ev_end (may be null) are recorded around the launch of the scan kernel
 // that writes y.
 hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* B, const void* C,
@@ -65,5 +76,7 @@ hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* 
 hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream);
 // h_final[i] = h0 ? h0[i] : 0 for i < n (packed input with no tokens: every sequence is empty)
 hipError_t launch_copy_state(const float* h0, float* h_final, int64_t n, hipStream_t stream);
+hipError_t launch_conv1d_fwd(const ConvParams& prm, bool bf16, hipStream_t stream);
+hipError_t launch_conv1d_update(const ConvParams& prm, bool bf16, hipStream_t stream);
 
 }  // namespace ssm

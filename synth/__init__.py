@@ -221,6 +221,20 @@ def packed_inputs(cfg: ScanConfig, total: int, device="cpu", seed: int | None = 
             for k, v in one.items()}
 
 
+def conv_params(dim: int, width: int, seed: int):
+    """Weights [dim][width] ~ N(0, 0.5^2) and bias [dim] ~ N(0, 0.2^2) in fp32 for the
+    causal convolution in front of the scan, drawn on the CPU."""
+    g = _gen("cpu", seed, STREAM_DT, 7)
+    w = (torch.randn((dim, width), generator=g, dtype=torch.float32) * 0.5).contiguous()
+    b = torch.randn(dim, generator=g, dtype=torch.float32) * 0.2
+    return w, b
+
+
+def conv_state(batch: int, dim: int, width: int, dtype, device="cpu", seed: int = 0):
+    """A conv state [batch][dim][width-1] ~ N(0, 1) in `dtype` (the inputs before t = 0)."""
+    return _normal((batch, dim, width - 1), 1.0, dtype, device, seed, STREAM_STATE, 11)
+
+
 def shrink(cfg: ScanConfig, **kw) -> ScanConfig:
     """A copy of `cfg` with some sizes replaced (same distributions)."""
     d = dict(cfg.__dict__)

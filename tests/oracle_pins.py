@@ -467,8 +467,88 @@ def pin_varlen_isolation(orc):
         assert not np.array_equal(hf2[1], hf[1])
 
 
+# ---------------------------------------------------------------------------
+# P13: the causal depthwise convolution + SiLU in front of the scan.
+# ---------------------------------------------------------------------------
+def _conv_problem(seed, batch=2, dim=3, L=40, K=4):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((batch, dim, L)), rng.standard_normal((dim, K)) * 0.5,
+            rng.standard_normal(dim) * 0.3, rng.standard_normal((batch, dim, K - 1)))
+
+
+def pin_conv_library(orc):
+    """torch.nn.functional.conv1d (fp64, CPU) with groups = channels and K-1 zeros of
+    padding on both sides, keeping the first L outputs, then torch's SiLU; and with a
+    state, the same conv over [state, x] without padding."""
+    import torch
+    import torch.nn.functional as F
+    x, w, b, st = _conv_problem(41)
+    dim, K = w.shape
+    tw = torch.tensor(w)[:, None, :]
+    ref = F.conv1d(torch.tensor(x), tw, torch.tensor(b), padding=K - 1, groups=dim)
+    ref = F.silu(ref[..., :x.shape[2]]).numpy()
+    y, _ = orc.conv1d(x, w, b)
+    assert _rel(y, ref) < 1e-14, _rel(y, ref)
+    ref = F.silu(F.conv1d(torch.tensor(np.concatenate([st, x], axis=2)), tw, torch.tensor(b),
+                          groups=dim)).numpy()
+    y, _ = orc.conv1d(x, w, b, state=st)
+    assert _rel(y, ref) < 1e-14
+
+
+def pin_conv_np_convolve(orc):
+    """Without SiLU and bias, each row is numpy.convolve with the reversed taps (Conv1d
+    is a cross-correlation), truncated to the causal part."""
+    x, w, _, _ = _conv_problem(42, batch=1, dim=2, L=33)
+    y, _ = orc.conv1d(x, w, None, silu=False)
+    for d in range(2):
+        ref = np.convolve(x[0, d], w[d][::-1])[:33]
+        assert _rel(y[0, d], ref) < 1e-14
+
+
+def pin_conv_impulse(orc):
+    """A unit impulse at t0: the pre-activation is bias + weight[K-1-(t-t0)] for
+    0 <= t - t0 < K and bias elsewhere (the newest input meets the last tap)."""
+    dim, L, K, t0 = 2, 12, 4, 5
+    w = np.array([[1.0, 2.0, 3.0, 4.0], [-0.5, 0.25, -2.0, 8.0]])
+    b = np.array([0.125, -1.0])
+    x = np.zeros((1, dim, L))
+    x[0, :, t0] = 1.0
+    y, st = orc.conv1d(x, w, b, silu=False)
+    for d in range(dim):
+        for t in range(L):
+            want = b[d] + (w[d, K - 1 - (t - t0)] if 0 <= t - t0 < K else 0.0)
+            assert y[0, d, t] == want, (d, t, y[0, d, t], want)
+    assert np.array_equal(st[0], np.zeros((dim, K - 1)))
+
+
+def pin_conv_state_continuation(orc):
+    """Splitting a sequence and carrying the state gives the same bits; a sequence
+    shorter than K-1 keeps the tail of the old state."""
+    x, w, b, st = _conv_problem(43, L=29)
+    y, s_end = orc.conv1d(x, w, b, state=st)
+    for cut in (1, 2, 3, 17):
+        y1, s1 = orc.conv1d(x[:, :, :cut], w, b, state=st)
+        y2, s2 = orc.conv1d(x[:, :, cut:], w, b, state=s1)
+        assert np.array_equal(np.concatenate([y1, y2], axis=2), y), cut
+        assert np.array_equal(s2, s_end), cut
+    _, s1 = orc.conv1d(x[:, :, :1], w, b, state=st)
+    assert np.array_equal(s1, np.concatenate([st[:, :, 1:], x[:, :, :1]], axis=2))
+
+
+def pin_conv_decode_equals_prefill(orc):
+    x, w, b, st = _conv_problem(44, L=9)
+    y, s_end = orc.conv1d(x, w, b, state=st)
+    s = st
+    for t in range(x.shape[2]):
+        yt, s = orc.conv1d_step(s, x[:, :, t], w, b)
+        assert np.array_equal(yt, y[:, :, t]), t
+    assert np.array_equal(s, s_end)
+
+
 ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response,
             pin_free_decay, pin_brute_force, pin_chunked_equals_unchunked,
             pin_decode_equals_scan, pin_linearity_and_causality, pin_elementwise,
             pin_reverse_lti_convolution, pin_reverse_brute_force, pin_varlen_brute_force,
-            pin_varlen_equals_batched, pin_varlen_isolation]
+            pin_varlen_equals_batched, pin_varlen_isolation, pin_conv_library,
+            pin_conv_np_convolve, pin_conv_impulse, pin_conv_state_continuation,
+            pin_conv_decode_equals_prefill]

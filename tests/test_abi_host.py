@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libssmscan.so n
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -148,3 +148,35 @@ def test_varlen_workspace_query(b):
         return (v + 255) // 256 * 256
     k = 16
     assert ws == up(up(up(up(1024 * 32 * 4) + 64 * k * 16 * 4) + 64 * k * 4) + k * 4)
+
+
+def conv(b, batch=2, seqlen=64, dim=64, width=4, act=1, io=1, **over):
+    p = dict(P, cs=P["h0"], cso=P["hf"])
+    p.update(over)
+    return b.lib.ssm_causal_conv1d_fwd(p["x"], p["A"], p["D"], p["cs"], p["y"], p["cso"], batch,
+                                       seqlen, dim, width, act, io, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(seqlen=0), 1), (dict(width=3), 2), (dict(width=0), 1),
+    (dict(act=2), 1), (dict(io=5), 1), (dict(x=None), 1), (dict(A=None), 1), (dict(y=None), 1),
+    (dict(x=P["x"] + 8), 2), (dict(A=P["A"] + 4), 2), (dict(cs=P["h0"] + 1), 2),
+    (dict(y=P["x"]), 1), (dict(cso=P["h0"]), 1), (dict(cso=P["y"] + 64), 1),
+])
+def test_conv_rejects(b, kw, status):
+    assert conv(b, **kw) == status
+    assert b.ssm_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(width=5), 2), (dict(state=None), 1), (dict(y=None), 1),
+    (dict(y=P["x"]), 1), (dict(state=P["x"]), 1), (dict(act=-1), 1),
+])
+def test_conv_update_rejects(b, kw, status):
+    p = dict(P, state=P["hf"])
+    batch = kw.pop("batch", 4)
+    width = kw.pop("width", 4)
+    act = kw.pop("act", 1)
+    p.update(kw)
+    assert b.lib.ssm_causal_conv1d_update(p["state"], p["x"], p["A"], p["D"], p["y"], batch, 32,
+                                          width, act, 1, None) == status

@@ -1,0 +1,119 @@
+"""GPU parity of the causal depthwise convolution + SiLU (ssm_causal_conv1d_fwd)
+and its decode update (ssm_causal_conv1d_update), through the C ABI, against the
+fp64 oracle: every row of small ragged shapes, every row of the Mamba-2.8B layer
+shape, and prefill-then-decode continuity. Conv states are copies of inputs, so
+they are compared bit for bit."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_53_amd import binding  # noqa: F401  (fails loudly if unbuilt)
+
+
+def _inputs(batch, L, dim, io, seed):
+    cfg = synth.ScanConfig("conv", batch, L, dim, io=io, seed=seed, use_z=False)
+    x = synth.scan_inputs(cfg, DEV)["x"]
+    w, b = synth.conv_params(dim, 4, seed)
+    st = synth.conv_state(batch, dim, 4, cfg.io_dtype, DEV, seed)
+    return x, w.to(DEV), b.to(DEV), st
+
+
+SHAPES = [(2, 1000, 200, "bf16"), (1, 333, 70, "bf16"), (3, 1, 5, "f32"), (1, 2, 7, "bf16"),
+          (1, 3, 9, "f32"), (2, 8, 16, "bf16"), (1, 9, 3, "f32"), (2, 2048, 64, "f32"),
+          (1, 4100, 33, "bf16")]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
+def test_conv_all_rows(shape):
+    from selective_state_space_53_amd import binding
+    batch, L, dim, io = shape
+    x, w, b, st = _inputs(batch, L, dim, io, 40 + L)
+    for use_state, act, use_bias in [(True, True, True), (False, True, False),
+                                     (True, False, True)]:
+        say("case conv", shape, use_state, act, use_bias)
+        y, so = binding.ssm_causal_conv1d_fwd(x, w, b if use_bias else None,
+                                              conv_state=st if use_state else None,
+                                              activation=act, return_state=True)
+        torch.cuda.synchronize()
+        yr, sr = oracle.Oracle.conv1d(x, w, b if use_bias else None,
+                                      state=st if use_state else None, silu=act)
+        e = parity.rowwise_err(y, yr)
+        say(f"  y err {e:.3e}")
+        assert e <= parity.TOL[io]
+        assert np.array_equal(oracle.f64(so), sr)
+
+
+def test_conv_full_size_all_rows():
+    """The Mamba-2.8B layer shape (batch 4, 2048 tokens, d_inner 5120, bf16)."""
+    from selective_state_space_53_amd import binding
+    cfg = synth.CONFIGS["m2p8"]
+    say("case conv full size")
+    x, w, b, st = _inputs(cfg.batch, cfg.seqlen, cfg.dim, cfg.io, cfg.seed)
+    y, so = binding.ssm_causal_conv1d_fwd(x, w, b, conv_state=st, return_state=True)
+    torch.cuda.synchronize()
+    yr, sr = oracle.Oracle.conv1d(x, w, b, state=st)
+    e = parity.rowwise_err(y, yr)
+    say(f"  full size y err {e:.3e}")
+    assert e <= parity.TOL[cfg.io]
+    assert np.array_equal(oracle.f64(so), sr)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_decode_continues_prefill(io):
+    """Prefill L tokens (returning the conv state), then T decode steps: the same as
+    one prefill over L + T tokens; the rolling state ends equal, bit for bit."""
+    from selective_state_space_53_amd import binding
+    batch, L, T, dim = 256 if io == "bf16" else 8, 37, 6, 5120 if io == "bf16" else 96
+    x, w, b, st = _inputs(batch, L + T, dim, io, 77)
+    say("case conv decode", io)
+    y_pre, state = binding.ssm_causal_conv1d_fwd(x[:, :, :L].contiguous(), w, b, conv_state=st,
+                                                 return_state=True)
+    ys = [binding.ssm_causal_conv1d_update(state, x[:, :, L + t].contiguous(), w, b)
+          for t in range(T)]
+    torch.cuda.synchronize()
+    yr, sr = oracle.Oracle.conv1d(x, w, b, state=st)
+    assert parity.rowwise_err(y_pre, yr[:, :, :L]) <= parity.TOL[io]
+    ydec = torch.stack(ys, dim=2)
+    assert parity.rowwise_err(ydec, yr[:, :, L:]) <= parity.TOL[io]
+    assert np.array_equal(oracle.f64(state), sr)
+    # the step oracle agrees with the sequence oracle on the same tokens
+    s = oracle.f64(st)
+    for t in range(L + T):
+        yt, s = oracle.Oracle.conv1d_step(s, x[:, :, t], w, b)
+    assert np.array_equal(s, sr)
+
+
+def test_conv_update_identity_taps():
+    """weight = (0, 0, 0, 1), no bias, no activation: y = x exactly and the state
+    shifts by one token."""
+    from selective_state_space_53_amd import binding
+    batch, dim = 3, 50
+    x, _, _, st = _inputs(batch, 1, dim, "bf16", 5)
+    w = torch.zeros((dim, 4), device=DEV)
+    w[:, 3] = 1.0
+    x0 = x[:, :, 0].contiguous()
+    st0 = st.clone()
+    y = binding.ssm_causal_conv1d_update(st, x0, w, None, activation=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, x0)
+    assert torch.equal(st[:, :, :2], st0[:, :, 1:]) and torch.equal(st[:, :, 2], x0)

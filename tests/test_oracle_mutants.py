@@ -78,6 +78,19 @@ PY_MUTANTS = [
     ("varlen_C_from_row_start", "Cf[None, a:b]", "Cf[None, 0:b - a]"),
     ("varlen_reverse_ignored", "fn = self.scan_reverse if reverse else self.scan",
      "fn = self.scan"),
+    ("conv_taps_reversed", "acc += w[None, :, k, None] * xp[:, :, k:k + L]",
+     "acc += w[None, :, K - 1 - k, None] * xp[:, :, k:k + L]"),
+    ("conv_halo_off_by_one", "acc += w[None, :, k, None] * xp[:, :, k:k + L]",
+     "acc += w[None, :, k, None] * xp[:, :, min(k + 1, K - 1):min(k + 1, K - 1) + L]"),
+    ("conv_bias_dropped", "            acc += f64(bias)[None, :, None]\n", "            pass\n"),
+    ("conv_silu_is_sigmoid", "out = acc / (1.0 + np.exp(-acc)) if silu else acc\n        return out, np.ascontiguousarray(xp",
+     "out = 1.0 / (1.0 + np.exp(-acc)) if silu else acc\n        return out, np.ascontiguousarray(xp"),
+    ("conv_state_ignored", "st = np.zeros((b_, d_, K - 1)) if state is None else f64(state)",
+     "st = np.zeros((b_, d_, K - 1))"),
+    ("conv_state_out_head", "return out, np.ascontiguousarray(xp[:, :, L:])",
+     "return out, np.ascontiguousarray(xp[:, :, :K - 1])"),
+    ("conv_step_no_shift", "return out, np.ascontiguousarray(window[:, :, 1:])",
+     "return out, np.ascontiguousarray(window[:, :, :-1])"),
 ]
 
 
