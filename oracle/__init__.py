@@ -23,7 +23,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_SRCS = [os.path.join(_HERE, "ssm_oracle.c"), os.path.join(_HERE, "ssm_oracle_bwd.c")]
 _LIB_PATH = os.path.join(_HERE, "libssmoracle.so")
 _lib = None
 _lock = threading.Lock()
@@ -33,13 +33,14 @@ _ip = ctypes.POINTER(ctypes.c_int64)
 
 
 def build(force: bool = True, out: str | None = None, extra_flags=()) -> str:
-    """Compile ssm_oracle.c with gcc (no fast-math: IEEE fp64 throughout)."""
+    """Compile the oracle's C files with gcc (no fast-math: IEEE fp64 throughout)."""
     out = out or _LIB_PATH
-    src = _SRC
-    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+    srcs = _SRCS
+    if (not force and os.path.exists(out)
+            and all(os.path.getmtime(out) >= os.path.getmtime(s) for s in srcs)):
         return out
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
-           "-ffp-contract=off", *extra_flags, src, "-o", out, "-lm"]
+           "-ffp-contract=off", *extra_flags, *srcs, "-o", out, "-lm"]
     subprocess.run(cmd, check=True, cwd=_HERE)
     return out
 
@@ -54,6 +55,11 @@ def _load(path: str | None = None):
     lib.ssm_oracle_scan_rows.argtypes = [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _ip, _ip,
         _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, ctypes.c_int]
+    lib.ssm_oracle_scan_bwd_rows.restype = ctypes.c_int
+    lib.ssm_oracle_scan_bwd_rows.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _ip, _ip, ctypes.c_int64, ctypes.c_int64,
+        _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp,
+        _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
     lib.ssm_oracle_step_rows.restype = ctypes.c_int
     lib.ssm_oracle_step_rows.argtypes = [
         ctypes.c_int64, ctypes.c_int64, _ip, _ip, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
@@ -133,6 +139,49 @@ class Oracle:
             delta_bias=delta_bias, delta_softplus=delta_softplus,
             h0_rows=None if h0 is None else f64(h0).reshape(b * d, N), nthreads=nthreads)
         return y.reshape(b, d, L), hf.reshape(b, d, N)
+
+    # ---- gradients ------------------------------------------------------
+    def scan_bwd(self, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                 delta_softplus=True, h0=None, dh_final=None, nthreads=1):
+        """Gradients of sum(dy * y) + sum(dh_final * h_final) for the forward scan with
+        the same arguments (full tensors, [batch][dim][L] layouts). Returns a dict with
+        dx, ddelta, dz ([batch][dim][L]), dA [dim][N], dB, dC [batch][L][N], dD, dbias
+        [dim] and dh0 [batch][dim][N], in fp64; dz / dD are None without z / D."""
+        x = f64(x)
+        b, d, L = x.shape
+        A = f64(A)
+        N = A.shape[1]
+        B = f64(B)
+        C = f64(C)
+        rb = np.repeat(np.arange(b, dtype=np.int64), d)
+        rd = np.tile(np.arange(d, dtype=np.int64), b)
+        R = b * d
+        rows = lambda t: None if t is None else np.ascontiguousarray(f64(t).reshape(R, -1))
+        xz, dl, zz, dyy = rows(x), rows(delta), rows(z), rows(dy)
+        h0r, dhf = rows(h0), rows(dh_final)
+        Df = None if D is None else f64(D)
+        bias = None if delta_bias is None else f64(delta_bias)
+        out = {k: np.empty((R, L)) for k in ("dx", "ddelta")}
+        out["dz"] = np.empty((R, L)) if z is not None else None
+        out["dA"] = np.empty((d, N))
+        out["dB"] = np.empty((b, L, N))
+        out["dC"] = np.empty((b, L, N))
+        out["dD"] = np.empty(d) if D is not None else None
+        out["dbias"] = np.empty(d)
+        out["dh0"] = np.empty((R, N))
+        rc = self._l.ssm_oracle_scan_bwd_rows(
+            R, L, N, _ptr_i(rb), _ptr_i(rd), b, d, _ptr(xz), _ptr(dl), _ptr(zz), _ptr(A),
+            _ptr(B), _ptr(C), _ptr(Df), _ptr(bias), int(bool(delta_softplus)), _ptr(h0r),
+            _ptr(dyy), _ptr(dhf), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dz"]),
+            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+            _ptr(out["dbias"]), _ptr(out["dh0"]), int(nthreads))
+        if rc != 0:
+            raise RuntimeError("ssm_oracle_scan_bwd_rows failed")
+        for k in ("dx", "ddelta", "dz"):
+            if out[k] is not None:
+                out[k] = out[k].reshape(b, d, L)
+        out["dh0"] = out["dh0"].reshape(b, d, N)
+        return out
 
     # ---- reverse-time and packed (varlen) scans ---------------------------
     def scan_reverse(self, x, delta, A, B, C, D=None, z=None, delta_bias=None,

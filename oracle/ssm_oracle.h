@@ -89,6 +89,35 @@ int ssm_oracle_step_rows(int64_t nrows, int64_t dstate,
                          const double* C, const double* D, const double* delta_bias,
                          int delta_softplus, double* y);
 
+/*
+ * Gradients of the scan (reverse mode; the pages give none, so this is the
+ * derivative of the definition above). With q_t = sum_n C_t[n] h_t[n] + D x_t the
+ * output before the gate, a_t[n] = exp(Delta_t A[n]), u_t = Delta_t x_t and
+ * G_t = dLoss/dh_t, for t = L-1 down to 0:
+ *   dq_t     = dy_t * silu(z_t)                 (dy_t without z)
+ *   dz_t     = dy_t * q_t * silu'(z_t),   silu'(z) = s (1 + z (1 - s)), s = sigma(z)
+ *   G_t[n]   = a_{t+1}[n] G_{t+1}[n] + dq_t C_t[n]     (the first term is dh_final at t = L-1)
+ *   dC_t[n] += dq_t h_t[n]          dB_t[n] += G_t[n] u_t     (summed over channels)
+ *   dx_t     = dq_t D + Delta_t sum_n G_t[n] B_t[n]
+ *   dDelta_t = x_t sum_n G_t[n] B_t[n] + sum_n G_t[n] h_{t-1}[n] a_t[n] A[n]
+ *   ddelta_t = dDelta_t * sigma(v_t)    (softplus' ; 1 without softplus),  dbias += ddelta_t
+ *   dA[n]   += G_t[n] h_{t-1}[n] a_t[n] Delta_t     dD += dq_t x_t
+ *   dh0[n]   = a_0[n] G_0[n]
+ * Shapes as for ssm_oracle_scan_rows; dy [nrows][seqlen]; dh_final [nrows][dstate] or
+ * NULL; outputs dx, ddelta, dz (when z is given) [nrows][seqlen]; dA [dim][dstate],
+ * dD (when D is given), dbias [dim] and dB, dC [batch][seqlen][dstate] are the sums over
+ * the given rows (overwritten); dh0 [nrows][dstate] or NULL. Returns 0 or -1.
+ */
+int ssm_oracle_scan_bwd_rows(int64_t nrows, int64_t seqlen, int64_t dstate,
+                             const int64_t* row_b, const int64_t* row_d, int64_t batch,
+                             int64_t dim, const double* x, const double* delta,
+                             const double* z, const double* A, const double* B,
+                             const double* C, const double* D, const double* delta_bias,
+                             int delta_softplus, const double* h0, const double* dy,
+                             const double* dh_final, double* dx, double* ddelta, double* dz,
+                             double* dA, double* dB, double* dC, double* dD, double* dbias,
+                             double* dh0, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -545,10 +545,140 @@ def pin_conv_decode_equals_prefill(orc):
     assert np.array_equal(s, s_end)
 
 
+# ---------------------------------------------------------------------------
+# P14: gradients (the backward scan).
+# ---------------------------------------------------------------------------
+def _bwd_problem(seed, batch=2, dim=3, L=23, N=4):
+    rng = np.random.default_rng(seed)
+    return dict(
+        x=rng.standard_normal((batch, dim, L)),
+        delta=rng.normal(0, 0.5, size=(batch, dim, L)),
+        A=-rng.uniform(0.1, 2.0, size=(dim, N)),
+        B=rng.standard_normal((batch, L, N)),
+        C=rng.standard_normal((batch, L, N)),
+        D=rng.standard_normal(dim),
+        z=rng.standard_normal((batch, dim, L)),
+        delta_bias=rng.normal(-0.5, 0.5, size=dim),
+        h0=rng.standard_normal((batch, dim, N)),
+    ), rng.standard_normal((batch, dim, L)), rng.standard_normal((batch, dim, N))
+
+
+def _torch_forward(x, delta, A, B, C, D, z, delta_bias, softplus, h0):
+    """The forward written a second time, in torch fp64 ops (softplus as logaddexp,
+    silu as torch's), so that torch.autograd can differentiate it."""
+    import torch
+    import torch.nn.functional as F
+    b, d, L = x.shape
+    v = delta + (0 if delta_bias is None else delta_bias[None, :, None])
+    dl = torch.logaddexp(v, torch.zeros_like(v)) if softplus else v
+    h = h0 if h0 is not None else torch.zeros((b, d, A.shape[1]), dtype=x.dtype)
+    ys = []
+    for t in range(L):
+        h = torch.exp(dl[:, :, t, None] * A[None]) * h + \
+            (dl[:, :, t] * x[:, :, t])[..., None] * B[:, None, t, :]
+        s = (C[:, None, t, :] * h).sum(-1)
+        if D is not None:
+            s = s + D[None, :] * x[:, :, t]
+        if z is not None:
+            s = s * F.silu(z[:, :, t])
+        ys.append(s)
+    return torch.stack(ys, dim=-1), h
+
+
+def pin_bwd_autograd(orc):
+    """Every gradient against torch.autograd of the torch forward, with and without
+    the gate, skip, bias, softplus, initial and final states."""
+    import torch
+    p, dy, dhf = _bwd_problem(51)
+    for use_z, use_D, sp, use_h, use_dhf in [(True, True, True, True, True),
+                                             (False, False, True, False, False),
+                                             (True, False, False, True, False)]:
+        q = dict(p)
+        if not sp:
+            q["delta"] = np.abs(p["delta"]) * 0.3
+            q["delta_bias"] = None
+        names = ["x", "delta", "A", "B", "C"] + (["D"] if use_D else []) + \
+                (["z"] if use_z else []) + (["delta_bias"] if sp else []) + \
+                (["h0"] if use_h else [])
+        tt = {k: torch.tensor(q[k], requires_grad=True) for k in names}
+        y, hf = _torch_forward(tt["x"], tt["delta"], tt["A"], tt["B"], tt["C"], tt.get("D"),
+                               tt.get("z"), tt.get("delta_bias"), sp, tt.get("h0"))
+        loss = (y * torch.tensor(dy)).sum()
+        if use_dhf:
+            loss = loss + (hf * torch.tensor(dhf)).sum()
+        loss.backward()
+        g = orc.scan_bwd(q["x"], q["delta"], q["A"], q["B"], q["C"], dy,
+                         D=q["D"] if use_D else None, z=q["z"] if use_z else None,
+                         delta_bias=q["delta_bias"] if sp else None, delta_softplus=sp,
+                         h0=q["h0"] if use_h else None, dh_final=dhf if use_dhf else None)
+        pairs = [("dx", "x"), ("ddelta", "delta"), ("dA", "A"), ("dB", "B"), ("dC", "C")]
+        pairs += [("dD", "D")] if use_D else []
+        pairs += [("dz", "z")] if use_z else []
+        pairs += [("dbias", "delta_bias")] if sp else []
+        pairs += [("dh0", "h0")] if use_h else []
+        for gk, tk in pairs:
+            ref = tt[tk].grad.numpy()
+            assert _rel(g[gk], ref) < 1e-11, (gk, _rel(g[gk], ref))
+
+
+def pin_bwd_finite_differences(orc):
+    """Directional derivatives of the (pinned) forward oracle by central differences:
+    sum(grad * V) against (loss(P + eps V) - loss(P - eps V)) / (2 eps) for a random
+    direction V of every input P."""
+    p, dy, dhf = _bwd_problem(52, batch=2, dim=2, L=17, N=3)
+    rng = np.random.default_rng(53)
+
+    def loss(q):
+        y, hf = orc.scan(q["x"], q["delta"], q["A"], q["B"], q["C"], D=q["D"], z=q["z"],
+                         delta_bias=q["delta_bias"], h0=q["h0"])
+        return float(np.sum(y * dy) + np.sum(hf * dhf))
+
+    g = orc.scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dy, D=p["D"], z=p["z"],
+                     delta_bias=p["delta_bias"], h0=p["h0"], dh_final=dhf)
+    for gk, pk in [("dx", "x"), ("ddelta", "delta"), ("dz", "z"), ("dA", "A"), ("dB", "B"),
+                   ("dC", "C"), ("dD", "D"), ("dbias", "delta_bias"), ("dh0", "h0")]:
+        V = rng.standard_normal(p[pk].shape)
+        eps = 1e-6
+        qp = dict(p)
+        qm = dict(p)
+        qp[pk] = p[pk] + eps * V
+        qm[pk] = p[pk] - eps * V
+        fd = (loss(qp) - loss(qm)) / (2 * eps)
+        an = float(np.sum(g[gk] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gk, fd, an)
+
+
+def pin_bwd_cumsum_closed_form(orc):
+    """A = 0, constant Delta, no gate: h_t = Delta sum_{s<=t} x_s B_s, so with
+    R_s = sum_{t>=s} dy_t C_t (numpy reverse cumsum): dx_s = D dy_s + Delta B_s . R_s,
+    dB_s = sum_d Delta x_s R_s, dC_t = sum_d dy_t h_t, dA = sum_t Delta R_t h_{t-1}."""
+    rng = np.random.default_rng(54)
+    b, d, L, N = 2, 3, 19, 4
+    x = rng.standard_normal((b, d, L))
+    dl = np.array([0.3, 0.7, 1.1])
+    B = rng.standard_normal((b, L, N))
+    C = rng.standard_normal((b, L, N))
+    D = rng.standard_normal(d)
+    dy = rng.standard_normal((b, d, L))
+    g = orc.scan_bwd(x, np.zeros((b, d, L)), np.zeros((d, N)), B, C, dy, D=D, delta_bias=dl,
+                     delta_softplus=False)
+    R = np.cumsum((dy[..., None] * C[:, None])[:, :, ::-1], axis=2)[:, :, ::-1]  # [b,d,L,N]
+    h = np.cumsum(dl[None, :, None, None] * x[..., None] * B[:, None], axis=2)     # h_t
+    hprev = np.concatenate([np.zeros((b, d, 1, N)), h[:, :, :-1]], axis=2)
+    dx = D[None, :, None] * dy + dl[None, :, None] * np.einsum("bln,bdln->bdl", B, R)
+    dB = np.einsum("bdl,bdln->bln", dl[None, :, None] * x, R)
+    dC = np.einsum("bdl,bdln->bln", dy, h)
+    dA = np.einsum("bdln,bdln->dn", R, hprev) * dl[:, None]
+    assert _rel(g["dx"], dx) < 1e-12 and _rel(g["dB"], dB) < 1e-12
+    assert _rel(g["dC"], dC) < 1e-12 and _rel(g["dA"], dA) < 1e-12
+    assert _rel(g["dD"], np.einsum("bdl,bdl->d", dy, x)) < 1e-12
+
+
 ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response,
             pin_free_decay, pin_brute_force, pin_chunked_equals_unchunked,
             pin_decode_equals_scan, pin_linearity_and_causality, pin_elementwise,
             pin_reverse_lti_convolution, pin_reverse_brute_force, pin_varlen_brute_force,
             pin_varlen_equals_batched, pin_varlen_isolation, pin_conv_library,
             pin_conv_np_convolve, pin_conv_impulse, pin_conv_state_continuation,
-            pin_conv_decode_equals_prefill]
+            pin_conv_decode_equals_prefill, pin_bwd_autograd, pin_bwd_finite_differences,
+            pin_bwd_cumsum_closed_form]

@@ -39,18 +39,65 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_mutant_is_caught(tmp_path, name, old, new):
-    src = open(os.path.join(SRC_DIR, "ssm_oracle.c")).read()
+# the same, in the gradient file
+BWD_MUTANTS = [
+    ("bwd_decay_of_same_token", "G[n] = Gc[n] + dq * Ct[n];",
+     "G[n] = Gc[n] * a[t * N + n] + dq * Ct[n];"),
+    ("bwd_carry_skips_decay", "Gc[n] = a[t * N + n] * G[n];", "Gc[n] = G[n];"),
+    ("bwd_dC_uses_prev_state", "j->dC[(b * L + t) * N + n] += dq * H[(t + 1) * N + n];",
+     "j->dC[(b * L + t) * N + n] += dq * H[t * N + n];"),
+    ("bwd_dB_drops_delta", "j->dB[(b * L + t) * N + n] += G[n] * (dl[t] * xr[t]);",
+     "j->dB[(b * L + t) * N + n] += G[n] * xr[t];"),
+    ("bwd_no_softplus_grad", "j->ddelta[r * L + t] = ddel * sg[t];",
+     "j->ddelta[r * L + t] = ddel;"),
+    ("bwd_dA_drops_delta", "j->dA[d * N + n] += gh * dl[t];", "j->dA[d * N + n] += gh;"),
+    ("bwd_dz_drops_q", "j->dz[r * L + t] = dyt * q[t] * (sz * (1.0 + zt * (1.0 - sz)));",
+     "j->dz[r * L + t] = dyt * (sz * (1.0 + zt * (1.0 - sz)));"),
+    ("bwd_dsilu_is_sigmoid", "j->dz[r * L + t] = dyt * q[t] * (sz * (1.0 + zt * (1.0 - sz)));",
+     "j->dz[r * L + t] = dyt * q[t] * sz;"),
+    ("bwd_dx_drops_skip", "j->dx[r * L + t] = j->D ? dq * j->D[d] : 0.0;",
+     "j->dx[r * L + t] = 0.0;"),
+    ("bwd_dx_drops_delta", "j->dx[r * L + t] += du * dl[t];", "j->dx[r * L + t] += du;"),
+    ("bwd_ddelta_drops_input_path", "ddel += du * xr[t];", "ddel += 0.0 * xr[t];"),
+    ("bwd_dh0_undecayed", "j->dh0[r * N + n] = Gc[n];", "j->dh0[r * N + n] = G[n];"),
+    ("bwd_dh_final_ignored", "Gc[n] = j->dh_final ? j->dh_final[r * N + n] : 0.0;",
+     "Gc[n] = 0.0;"),
+]
+
+SOURCES = ["ssm_oracle.c", "ssm_oracle_bwd.c"]
+
+
+def _mutant(tmp_path, name, fname, old, new):
+    src = open(os.path.join(SRC_DIR, fname)).read()
     assert src.count(old) == 1, f"mutation site for {name} not unique/present"
     d = tmp_path / name
     d.mkdir()
     shutil.copy(os.path.join(SRC_DIR, "ssm_oracle.h"), d / "ssm_oracle.h")
-    (d / "ssm_oracle.c").write_text(src.replace(old, new))
+    for f in SOURCES:
+        text = open(os.path.join(SRC_DIR, f)).read()
+        (d / f).write_text(src.replace(old, new) if f == fname else text)
     so = d / "libmut.so"
     subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
-                    "-ffp-contract=off", str(d / "ssm_oracle.c"), "-o", str(so), "-lm"],
+                    "-ffp-contract=off", *[str(d / f) for f in SOURCES], "-o", str(so), "-lm"],
                    check=True)
+    return so
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_bwd_mutant_is_caught(tmp_path, name, old, new):
+    orc = oracle.Oracle(str(_mutant(tmp_path, name, "ssm_oracle_bwd.c", old, new)))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    so = _mutant(tmp_path, name, "ssm_oracle.c", old, new)
     orc = oracle.Oracle(str(so))
     failed = []
     for pin in oracle_pins.ALL_PINS:
