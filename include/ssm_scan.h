@@ -89,6 +89,8 @@ typedef struct {
                            the sum rounded once to io_dtype): two calls, causal then
                            anti-causal with accumulate = 1, give a bidirectional layer's
                            summed output.                                                 */
+    int32_t bwd_group_channels; /* ssm_scan_bwd: channels per backward workgroup, 0 =
+                           library choice, else 32, 48 or 64                              */
 } ssm_scan_options;
 
 /*
@@ -137,6 +139,55 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
                         const float* delta_bias, int delta_softplus, const float* h0,
                         void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
                         int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                        size_t workspace_bytes, const ssm_scan_options* opts, void* stream);
+
+/*
+ * Backward selective scan (training): the gradients of a loss through
+ * ssm_scan_fwd, given dy = dLoss/dy and optionally dh_final = dLoss/dh_final. The
+ * pages say Mamba trains with parallel scans ("Mamba: Linear-Time Sequence Modeling
+ * with Selective State Spaces", key points; aidatadrop, "The Magic of Selective
+ * Scan") but give no gradients; these are the reverse-mode derivatives of the
+ * recurrence above. With a_t = exp(Delta_t A), u_t = Delta_t x_t, q_t = the output
+ * before the gate and G_t = dLoss/dh_t, for t = L-1 down to 0:
+ *   dq_t = dy_t silu(z_t)       dz_t = dy_t q_t silu'(z_t)
+ *   G_t  = a_{t+1} G_{t+1} + dq_t C_t          (a_L G_L = dh_final)
+ *   dB_t = sum_d G_t u_t        dC_t = sum_d dq_t h_t
+ *   dx_t = dq_t D + Delta_t (G_t . B_t)
+ *   ddelta_t = (x_t (G_t . B_t) + sum_n G_t h_{t-1} a_t A) * softplus'(v_t)
+ *   dA = sum_{b,t} G_t h_{t-1} a_t Delta_t   dD = sum dq_t x_t   ddelta_bias = sum ddelta
+ *   dh0 = a_0 G_0
+ * The states are recomputed from checkpoints the call writes into its workspace (a
+ * forward pass that keeps the state before every 16th token), so the forward's
+ * outputs are not needed.
+ *
+ *   x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0: as for ssm_scan_fwd
+ *   dy           [batch][dim][seqlen] io_dtype
+ *   dh_final     [batch][dim][dstate] fp32 or NULL (zero)
+ *   dx, ddelta   [batch][dim][seqlen] io_dtype out (ddelta is the gradient of the raw
+ *                delta, before bias and softplus)
+ *   dz           [batch][dim][seqlen] io_dtype out: required when z is given, else NULL
+ *   dA           [dim][dstate] fp32 out
+ *   dB, dC       [batch][seqlen][dstate] fp32 out
+ *   dD           [dim] fp32 out or NULL (needs D)
+ *   ddelta_bias  [dim] fp32 out or NULL (needs delta_bias)
+ *   dh0          [batch][dim][dstate] fp32 out or NULL
+ *   workspace    ssm_scan_bwd_workspace_bytes(...) bytes
+ *   opts         as for ssm_scan_fwd (the plan of the checkpoint pass); reverse and
+ *                accumulate must be 0 (SSM_ERR_UNSUPPORTED otherwise)
+ * Every output overlaps nothing. Sums over channels and batch rows are finished in a
+ * fixed order, so results are deterministic. timing events, when given, bracket the
+ * backward kernel itself.
+ */
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    ssm_dtype io_dtype, const ssm_scan_options* opts);
+
+ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z,
+                        const float* delta_bias, int delta_softplus, const float* h0,
+                        const void* dy, const float* dh_final, void* dx, void* ddelta,
+                        void* dz, float* dA, float* dB, float* dC, float* dD,
+                        float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
+                        int64_t dim, int64_t dstate, ssm_dtype io_dtype, void* workspace,
                         size_t workspace_bytes, const ssm_scan_options* opts, void* stream);
 
 /*

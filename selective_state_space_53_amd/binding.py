@@ -21,7 +21,8 @@ if not os.path.exists(_LIB_PATH):
 SSM_OK, SSM_ERR_INVALID_ARGUMENT, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE_TOO_SMALL, \
     SSM_ERR_HIP = range(5)
 SSM_F32, SSM_BF16 = 0, 1
-EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_scan_varlen_workspace_bytes",
+EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_scan_bwd_workspace_bytes",
+           "ssm_scan_bwd", "ssm_scan_varlen_workspace_bytes",
            "ssm_scan_varlen_fwd", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
            "ssm_state_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
@@ -30,7 +31,7 @@ class ScanOptions(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("plan", ctypes.c_int32),
                 ("group_channels", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
                 ("timing_end", ctypes.c_void_p), ("reverse", ctypes.c_int32),
-                ("accumulate", ctypes.c_int32)]
+                ("accumulate", ctypes.c_int32), ("bwd_group_channels", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -44,6 +45,13 @@ lib.ssm_scan_fwd.restype = ctypes.c_int
 lib.ssm_scan_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                              _i64, _i64, _i64, _i64, ctypes.c_int, _vp, ctypes.c_size_t,
                              ctypes.POINTER(ScanOptions), _vp]
+lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+lib.ssm_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
+                                             ctypes.POINTER(ScanOptions)]
+lib.ssm_scan_bwd.restype = ctypes.c_int
+lib.ssm_scan_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                             ctypes.c_int, _vp, ctypes.c_size_t, ctypes.POINTER(ScanOptions), _vp]
 lib.ssm_scan_varlen_workspace_bytes.restype = ctypes.c_size_t
 lib.ssm_scan_varlen_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int,
                                                 ctypes.POINTER(ScanOptions)]
@@ -107,19 +115,26 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 
 def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0,
-             reverse=False, accumulate=False):
+             reverse=False, accumulate=False, bwd_group_channels: int = 0):
     if (plan == 0 and chunk_len == 0 and events is None and group_channels == 0
-            and not reverse and not accumulate):
+            and not reverse and not accumulate and bwd_group_channels == 0):
         return None
     ev0, ev1 = (None, None) if events is None else events
     return ctypes.byref(ScanOptions(chunk_len, plan, group_channels, ev0, ev1, int(bool(reverse)),
-                                    int(bool(accumulate))))
+                                    int(bool(accumulate)), bwd_group_channels))
 
 
 def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
                              group_channels=0) -> int:
     return lib.ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype,
                                         _options(plan, chunk_len, None, group_channels))
+
+
+def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
+                                 group_channels=0, bwd_group_channels=0) -> int:
+    return lib.ssm_scan_bwd_workspace_bytes(
+        batch, seqlen, dim, dstate, io_dtype,
+        _options(plan, chunk_len, None, group_channels, bwd_group_channels=bwd_group_channels))
 
 
 def ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype, plan=0, chunk_len=0,
@@ -170,6 +185,54 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
             int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, N,
             code, _ptr(workspace), 0 if workspace is None else workspace.numel(), opts, s))
     return (y, h_final) if return_final_state else y
+
+
+def ssm_scan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 h0=None, dh_final=None, want_dh0=False, workspace=None, plan=0, chunk_len=0,
+                 stream=None, timing_events=None, group_channels=0, bwd_group_channels=0):
+    """Gradients of the forward scan with the same arguments, given dy [batch][dim][L]
+    (and dh_final [batch][dim][16]). Returns a dict: dx, ddelta, dz (x's dtype), dA,
+    dB, dC, dD, ddelta_bias, dh0 (fp32; None where the input is absent / not asked)."""
+    _dev(x, "x")
+    io = x.dtype
+    batch, dim, seqlen = x.shape
+    N = A.shape[-1]
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(dy, "dy", io, x.shape)
+    _dev(A, "A", torch.float32, (dim, N))
+    _dev(B, "B", io, (batch, seqlen, N))
+    _dev(C, "C", io, (batch, seqlen, N))
+    _dev(D, "D", torch.float32, (dim,))
+    _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    _dev(h0, "h0", torch.float32, (batch, dim, N))
+    _dev(dh_final, "dh_final", torch.float32, (batch, dim, N))
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {
+        "dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+        "dz": torch.empty_like(x) if z is not None else None,
+        "dA": torch.empty((dim, N), **f32), "dB": torch.empty((batch, seqlen, N), **f32),
+        "dC": torch.empty((batch, seqlen, N), **f32),
+        "dD": torch.empty((dim,), **f32) if D is not None else None,
+        "ddelta_bias": torch.empty((dim,), **f32) if delta_bias is not None else None,
+        "dh0": torch.empty((batch, dim, N), **f32) if want_dh0 else None,
+    }
+    code = _dtype_code(x)
+    opts = _options(plan, chunk_len, timing_events, group_channels,
+                    bwd_group_channels=bwd_group_channels)
+    ws_bytes = lib.ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, N, code, opts)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        _check(lib.ssm_scan_bwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(g["dx"]),
+            _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+            _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, seqlen, dim, N, code,
+            _ptr(workspace), workspace.numel(), opts, s))
+    return g
 
 
 def ssm_scan_varlen_fwd(x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None,

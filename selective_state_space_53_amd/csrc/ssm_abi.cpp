@@ -364,9 +364,238 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
     return SSM_OK;
 }
 
+// ---- backward ---------------------------------------------------------------------
+constexpr int kBwdTile = 16;
+
+// LDS bytes of one backward workgroup of cg channels (must match scan_bwd_kernel):
+// Delta, u, dq [cg][20]; two [8][cg][20] partial arrays; two B/C tiles; row sums.
+int64_t bwd_lds_bytes(int cg) { return (int64_t)(396 * cg + 1024) * 4; }
+
+int choose_bwd_group(int64_t batch, int64_t dim) {
+    static const int kCands[] = {64, 48, 32};
+    int best = 32;
+    double best_c = 1e300;
+    for (int cg : kCands) {
+        const int64_t groups = batch * ((dim + cg - 1) / cg);
+        int64_t k = kLdsPerCU / bwd_lds_bytes(cg);
+        const int64_t kw = 4 * 3 / (cg / 8);        // <= 168 VGPRs: 3 waves per SIMD
+        if (kw < k) k = kw;
+        const int64_t per_cu = (groups + kCUs - 1) / kCUs;
+        if (k > per_cu) k = per_cu;
+        if (k < 1) k = 1;
+        const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
+        const int64_t w = (k * (cg / 8) + 3) / 4;
+        const double c = (double)rounds * (double)w * wave_cost(w);
+        if (c < best_c * (1 - 1e-9)) {
+            best = cg;
+            best_c = c;
+        }
+    }
+    return best;
+}
+
+struct BwdPlan {
+    ssm::ScanPlan fwd;      // the checkpoint pass
+    int cg;
+    int64_t nckpt;
+    size_t ws_ckpt, ws_bc, ws_A, ws_D, ws_bias, ws_total;
+};
+
+ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                         ssm_dtype io_dtype, const ssm_scan_options* opts, BwdPlan* bp) {
+    if (opts && (opts->reverse || opts->accumulate))
+        return fail(SSM_ERR_UNSUPPORTED,
+                    "the backward scan supports the causal scan without accumulate only");
+    ssm_status st = make_plan(batch, seqlen, dim, dstate, io_dtype, opts, &bp->fwd);
+    if (st != SSM_OK) return st;
+    const int req = opts ? opts->bwd_group_channels : 0;
+    if (req != 0 && req != 32 && req != 48 && req != 64)
+        return fail(SSM_ERR_INVALID_ARGUMENT,
+                    "ssm_scan_options.bwd_group_channels=%d not in {0, 32, 48, 64}", req);
+    bp->cg = req ? req : choose_bwd_group(batch, dim);
+    const int64_t gpb = (dim + bp->cg - 1) / bp->cg;
+    bp->nckpt = (seqlen + kBwdTile - 1) / kBwdTile;
+    int64_t ck, bc, pa, pd;
+    if (!bytes4(batch * dim, bp->nckpt, ssm::kDState, 4, &ck) ||
+        !bytes4(batch * gpb, seqlen, 32, 4, &bc) || !bytes4(batch * dim, ssm::kDState, 1, 4, &pa) ||
+        !bytes4(batch * dim, 1, 1, 4, &pd))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
+    bp->ws_ckpt = align_up(bp->fwd.ws_total, 256);
+    bp->ws_bc = align_up(bp->ws_ckpt + (size_t)ck, 256);
+    bp->ws_A = align_up(bp->ws_bc + (size_t)bc, 256);
+    bp->ws_D = align_up(bp->ws_A + (size_t)pa, 256);
+    bp->ws_bias = align_up(bp->ws_D + (size_t)pd, 256);
+    bp->ws_total = align_up(bp->ws_bias + (size_t)pd, 256);
+    return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    ssm_dtype io_dtype, const ssm_scan_options* opts) {
+    BwdPlan bp;
+    if (make_bwd_plan(batch, seqlen, dim, dstate, io_dtype, opts, &bp) != SSM_OK) return 0;
+    return bp.ws_total;
+}
+
+ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z,
+                        const float* delta_bias, int delta_softplus, const float* h0,
+                        const void* dy, const float* dh_final, void* dx, void* ddelta,
+                        void* dz, float* dA, float* dB, float* dC, float* dD,
+                        float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
+                        int64_t dim, int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                        size_t workspace_bytes, const ssm_scan_options* opts, void* stream) {
+    try {
+        BwdPlan bp;
+        ssm_status st = make_bwd_plan(batch, seqlen, dim, dstate, io_dtype, opts, &bp);
+        if (st != SSM_OK) return st;
+        if (delta_softplus != 0 && delta_softplus != 1)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "delta_softplus must be 0 or 1");
+        if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC)
+            return fail(SSM_ERR_INVALID_ARGUMENT,
+                        "x, delta, A, B, C, dy, dx, ddelta, dA, dB and dC are required");
+        if ((z != nullptr) != (dz != nullptr))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "dz is required exactly when z is given");
+        if (dD && !D) return fail(SSM_ERR_INVALID_ARGUMENT, "dD needs D");
+        if (ddelta_bias && !delta_bias)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "ddelta_bias needs delta_bias");
+        const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
+        const int64_t io = batch * dim * seqlen * elem;
+        const int64_t bc = batch * seqlen * dstate * elem;
+        const int64_t bc32 = batch * seqlen * dstate * 4;
+        const int64_t stb = batch * dim * dstate * 4;
+        struct {
+            const char* name;
+            const void* p;
+            uintptr_t align;
+        } al[] = {{"x", x, 16},           {"delta", delta, 16}, {"z", z, 16},
+                  {"dy", dy, 16},         {"B", B, 16},         {"C", C, 16},
+                  {"A", A, 16},           {"D", D, 4},          {"delta_bias", delta_bias, 4},
+                  {"h0", h0, 16},         {"dh_final", dh_final, 16},
+                  {"dx", dx, 16},         {"ddelta", ddelta, 16}, {"dz", dz, 16},
+                  {"dA", dA, 16},         {"dB", dB, 16},       {"dC", dC, 16},
+                  {"dD", dD, 4},          {"ddelta_bias", ddelta_bias, 4},
+                  {"dh0", dh0, 16},       {"workspace", workspace, 16}};
+        for (auto& a : al)
+            if (a.p && !aligned(a.p, a.align))
+                return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
+                            (unsigned)a.align);
+        if (!workspace || workspace_bytes < bp.ws_total)
+            return fail(SSM_ERR_WORKSPACE_TOO_SMALL,
+                        "workspace needs %zu bytes (got %zu at %p)", bp.ws_total,
+                        workspace_bytes, workspace);
+        const Region regs[] = {
+            region("x", x, io),           region("delta", delta, io),
+            region("z", z, io),           region("dy", dy, io),
+            region("B", B, bc),           region("C", C, bc),
+            region("A", A, dim * dstate * 4), region("D", D, dim * 4),
+            region("delta_bias", delta_bias, dim * 4), region("h0", h0, stb),
+            region("dh_final", dh_final, stb),
+            // outputs from here on: each may overlap nothing
+            region("dx", dx, io),         region("ddelta", ddelta, io),
+            region("dz", dz, io),         region("dA", dA, dim * dstate * 4),
+            region("dB", dB, bc32),       region("dC", dC, bc32),
+            region("dD", dD, dim * 4),    region("ddelta_bias", ddelta_bias, dim * 4),
+            region("dh0", dh0, stb),      region("workspace", workspace, (int64_t)bp.ws_total)};
+        constexpr int kFirstOut = 11;
+        constexpr int kN = sizeof(regs) / sizeof(regs[0]);
+        for (int i = kFirstOut; i < kN; ++i)
+            for (int j = 0; j < kN; ++j)
+                if (i != j && overlaps(regs[i], regs[j]))
+                    return fail(SSM_ERR_INVALID_ARGUMENT, "%s overlaps %s", regs[i].name,
+                                regs[j].name);
+
+        char* ws = static_cast<char*>(workspace);
+        hipStream_t strm = static_cast<hipStream_t>(stream);
+        // 1. B/C widening and the forward in checkpoint mode (the state before every
+        //    16th token), with the forward's own plan
+        ssm::ScanParams fp{};
+        fp.x = x;
+        fp.delta = delta;
+        fp.z = nullptr;
+        fp.y = nullptr;
+        fp.A = A;
+        fp.D = D;
+        fp.bias = delta_bias;
+        fp.h0 = h0;
+        fp.h_final = nullptr;
+        fp.bcq = reinterpret_cast<float*>(ws + bp.fwd.ws_bcq);
+        fp.chunk_state =
+            bp.fwd.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.fwd.ws_state) : nullptr;
+        fp.chunk_sum = bp.fwd.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.fwd.ws_sum) : nullptr;
+        fp.chunk_flag =
+            bp.fwd.nchunks > 1 ? reinterpret_cast<int32_t*>(ws + bp.fwd.ws_flag) : nullptr;
+        fp.cu = nullptr;
+        fp.ckpt = reinterpret_cast<float*>(ws + bp.ws_ckpt);
+        fp.nckpt = bp.nckpt;
+        fp.batch = batch;
+        fp.seqlen = seqlen;
+        fp.dim = dim;
+        fp.lpad = (seqlen + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
+        fp.chunk_len = bp.fwd.chunk_len;
+        fp.nchunks = bp.fwd.nchunks;
+        fp.groups_per_batch =
+            (int32_t)((dim + bp.fwd.group_channels - 1) / bp.fwd.group_channels);
+        fp.ngroups = (int32_t)(batch * fp.groups_per_batch);
+        fp.softplus = delta_softplus;
+        fp.aligned = ((seqlen * elem) % 16) == 0;
+        hipError_t e = ssm::launch_scan(bp.fwd, fp, B, C, io_dtype == SSM_BF16, strm, nullptr,
+                                        nullptr);
+        if (e != hipSuccess)
+            return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        // 2. the backward kernel and its reductions
+        ssm::BwdParams prm{};
+        prm.x = x;
+        prm.delta = delta;
+        prm.z = z;
+        prm.dy = dy;
+        prm.A = A;
+        prm.D = D;
+        prm.bias = delta_bias;
+        prm.dh_final = dh_final;
+        prm.ckpt = fp.ckpt;
+        prm.bcq = fp.bcq;
+        prm.dx = dx;
+        prm.ddelta = ddelta;
+        prm.dz = dz;
+        prm.dA = dA;
+        prm.dB = dB;
+        prm.dC = dC;
+        prm.dD = dD;
+        prm.dbias = ddelta_bias;
+        prm.dh0 = dh0;
+        prm.part_bc = reinterpret_cast<float*>(ws + bp.ws_bc);
+        prm.part_A = reinterpret_cast<float*>(ws + bp.ws_A);
+        prm.part_D = reinterpret_cast<float*>(ws + bp.ws_D);
+        prm.part_bias = reinterpret_cast<float*>(ws + bp.ws_bias);
+        prm.batch = batch;
+        prm.seqlen = seqlen;
+        prm.dim = dim;
+        prm.lpad = fp.lpad;
+        prm.nckpt = bp.nckpt;
+        prm.groups_per_batch = (int32_t)((dim + bp.cg - 1) / bp.cg);
+        prm.softplus = delta_softplus;
+        prm.aligned = fp.aligned;
+        if (getenv("SSMSCAN_LOG"))
+            fprintf(stderr,
+                    "[ssmscan] bwd b=%lld L=%lld d=%lld %s: checkpoint pass %d channels/group "
+                    "x %d chunks, backward %d channels/group\n",
+                    (long long)batch, (long long)seqlen, (long long)dim,
+                    io_dtype == SSM_BF16 ? "bf16" : "f32", bp.fwd.group_channels,
+                    bp.fwd.nchunks, bp.cg);
+        hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->timing_begin) : nullptr;
+        hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->timing_end) : nullptr;
+        e = ssm::launch_scan_bwd(bp.cg, prm, io_dtype == SSM_BF16, strm, ev0, ev1);
+        if (e != hipSuccess)
+            return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        return SSM_OK;
+    } catch (...) {
+        return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
+    }
+}
 
 const char* ssm_status_string(ssm_status s) {
     switch (s) {

@@ -1,0 +1,484 @@
+// ssm_bwd.hip - gfx950 kernels of the backward selective scan (training).
+//
+// The pages say the model trains with parallel scans ("Mamba: Linear-Time Sequence
+// Modeling with Selective State Spaces", key points; the aidatadrop page, "The
+// Magic of Selective Scan") but never write the gradients down. These kernels
+// compute the reverse-mode derivative of the forward recurrence: with
+// a_t = exp(Delta_t A), u_t = Delta_t x_t, q_t = sum_n C_t h_t + D x_t and
+// G_t = dLoss/dh_t, for t from the last token to the first
+//   dq_t = dy_t silu(z_t),   dz_t = dy_t q_t silu'(z_t)
+//   G_t  = a_{t+1} G_{t+1} + dq_t C_t
+//   dC_t += dq_t h_t,  dB_t += G_t u_t          (summed over channels)
+//   dx_t = dq_t D + Delta_t sum_n G_t B_t
+//   dDelta_t = x_t sum_n G_t B_t + sum_n G_t h_{t-1} a_t A,  ddelta = dDelta softplus'(v)
+//   dA += G_t h_{t-1} a_t Delta_t,  dD += dq_t x_t,  dbias += ddelta,  dh0 = a_0 G_0.
+//
+// Mapping (the forward's, with 16-token tiles): a workgroup owns CG channels of one
+// batch row and all 16 states; a lane keeps 2 states of one channel. The sequence
+// is walked tile by tile from the end. Per tile:
+//   pre    per (channel, 2 tokens): Delta, u, dq, and what post needs, into LDS
+//   fwd    from the tile's checkpoint (the state before its first token, written by
+//          the forward scan in checkpoint mode) the 16 states h_t are recomputed and
+//          kept in registers; partial readouts C.h -> LDS; dq.h (for dC) is summed
+//          over the 16 channels of a lane row with DPP and the row sums go to LDS
+//   mid    q_t and dz_t; the workgroup's dC partial sums -> HBM
+//   bwd    the adjoint recurrence over the 16 tokens (exp recomputed): partial
+//          G.B and G.h.a.A -> LDS, dA in registers, G.u (for dB) summed like dq.h
+//   post   dx, ddelta per (channel, 2 tokens); the workgroup's dB partial sums -> HBM
+// Sums over channels across workgroups (dB, dC) and over batch rows (dA, dD, dbias)
+// are finished by small reduction kernels in a fixed order: no float atomics, the
+// result does not depend on scheduling.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+
+namespace {
+
+using namespace dev;
+
+constexpr int kT = 16;            // tokens per backward tile
+constexpr int kRowF = kT + 4;     // padded LDS row (floats)
+constexpr int kBcT = 8 * kT * 4;  // floats of widened B/C per tile
+
+// Two consecutive tokens of one row, raw, loaded one tile ahead of their use.
+template <typename IO> struct Raw2;
+template <> struct Raw2<uint16_t> {
+    uint32_t w;
+    __device__ __forceinline__ void load(const uint16_t* p, bool vec, int n) {
+        if (vec) {
+            w = *reinterpret_cast<const uint32_t*>(p);
+        } else {
+            const uint32_t lo = n > 0 ? p[0] : 0u;
+            const uint32_t hi = n > 1 ? p[1] : 0u;
+            w = lo | (hi << 16);
+        }
+    }
+    __device__ __forceinline__ void zero() { w = 0u; }
+    __device__ __forceinline__ void widen(float* o) const { o[0] = bf16_lo(w); o[1] = bf16_hi(w); }
+};
+template <> struct Raw2<float> {
+    float v[2];
+    __device__ __forceinline__ void load(const float* p, bool vec, int n) {
+        if (vec) {
+            const float2 a = *reinterpret_cast<const float2*>(p);
+            v[0] = a.x;
+            v[1] = a.y;
+        } else {
+            v[0] = n > 0 ? p[0] : 0.0f;
+            v[1] = n > 1 ? p[1] : 0.0f;
+        }
+    }
+    __device__ __forceinline__ void zero() { v[0] = v[1] = 0.0f; }
+    __device__ __forceinline__ void widen(float* o) const { o[0] = v[0]; o[1] = v[1]; }
+};
+
+template <typename IO>
+__device__ __forceinline__ void store2(IO* p, bool vec, int n, float a, float b) {
+    if (vec && sizeof(IO) == 2) {
+        *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+    } else if (vec) {
+        *reinterpret_cast<float2*>(p) = make_float2(a, b);
+    } else {
+        if (n > 0) store_one(p, a);
+        if (n > 1) store_one(p + 1, b);
+    }
+}
+
+// DPP lane moves inside a 16-lane row (ctrl is a compile-time constant)
+#define SSM_DPP(v, ctrl)                                                                    \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)),   \
+                                                          (ctrl), 0xF, 0xF, false))
+
+// Sum two values over the 16 lanes of a row: lanes 0-7 return the sum of v0, lanes
+// 8-15 the sum of v1. The first step pairs lane i with lane 15-i (row mirror) and
+// moves each lane's other value across; three more steps (half-row mirror, then
+// quad swaps of 2 and 1) finish each half.
+__device__ __forceinline__ float row_sum2(float v0, float v1, bool lo) {
+    float keep = lo ? v0 : v1;
+    const float send = lo ? v1 : v0;
+    keep += SSM_DPP(send, 0x140);   // row_mirror
+    keep += SSM_DPP(keep, 0x141);   // row_half_mirror
+    keep += SSM_DPP(keep, 0x4E);    // quad_perm [2,3,0,1]
+    keep += SSM_DPP(keep, 0xB1);    // quad_perm [1,0,3,2]
+    return keep;
+}
+
+template <typename IO, int CG>
+__global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
+    static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
+    constexpr int kRowsPerPair = CG / 16;
+    constexpr int kLaneRows = CG / 2;           // 16-lane rows in the workgroup
+    __shared__ float sD[CG * kRowF];            // Delta
+    __shared__ float sU[CG * kRowF];            // u = Delta x
+    __shared__ float sQ[CG * kRowF];            // dq
+    __shared__ float sP1[8 * CG * kRowF];       // per state pair: readout, then G.B
+    __shared__ float sP2[8 * CG * kRowF];       // per state pair: G.h.a.A
+    __shared__ float sBC[2 * kBcT];             // [buffer][pair][token][B0 B1 C0 C1]
+    __shared__ float sRed[kT * kLaneRows * 2];  // [token][lane row][2]: row sums
+
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x / p.groups_per_batch;
+    const int grp = blockIdx.x % p.groups_per_batch;
+    const int64_t d0 = (int64_t)grp * CG;
+    const int64_t L = p.seqlen;
+    const int ntiles = (int)((L + kT - 1) / kT);
+
+    // core mapping: lane row r holds state pair pr of 16 consecutive channels
+    const int r = tid >> 4;
+    const int pr = r / kRowsPerPair;
+    const int cc = (r % kRowsPerPair) * 16 + (tid & 15);
+    const int64_t d = d0 + cc;
+    const bool valid = d < p.dim;
+    const int64_t row = b * p.dim + d;
+    const bool lo8 = (tid & 15) < 8;
+    // pre/post mapping: (channel cq, tokens 2jq and 2jq+1 of the tile)
+    const int cq = tid >> 3;
+    const int jq = tid & 7;
+    const int64_t dq = d0 + cq;
+    const bool validq = dq < p.dim;
+    const int64_t rowq = b * p.dim + dq;
+
+    float a2[2] = {0.f, 0.f}, Ar[2] = {0.f, 0.f}, Gc[2] = {0.f, 0.f}, dA[2] = {0.f, 0.f};
+    if (valid) {
+        const float2 av = *reinterpret_cast<const float2*>(p.A + d * kDState + 2 * pr);
+        Ar[0] = av.x;
+        Ar[1] = av.y;
+        a2[0] = av.x * kLog2e;
+        a2[1] = av.y * kLog2e;
+        if (p.dh_final) {
+            const float2 g = *reinterpret_cast<const float2*>(p.dh_final + row * kDState + 2 * pr);
+            Gc[0] = g.x;
+            Gc[1] = g.y;
+        }
+    }
+    const float bias = (validq && p.bias) ? p.bias[dq] : 0.0f;
+    const float Dd = (validq && p.D) ? p.D[dq] : 0.0f;
+    const IO* xr = static_cast<const IO*>(p.x) + rowq * L;
+    const IO* dr = static_cast<const IO*>(p.delta) + rowq * L;
+    const IO* zr = p.z ? static_cast<const IO*>(p.z) + rowq * L : nullptr;
+    const IO* gr = static_cast<const IO*>(p.dy) + rowq * L;
+    IO* dxr = static_cast<IO*>(p.dx) + rowq * L;
+    IO* ddr = static_cast<IO*>(p.ddelta) + rowq * L;
+    IO* dzr = p.z ? static_cast<IO*>(p.dz) + rowq * L : nullptr;
+    const float* ck = p.ckpt + row * p.nckpt * kDState + 2 * pr;
+    float* const pbc = p.part_bc + ((b * p.groups_per_batch + grp) * L) * 32;
+    // B/C staging: threads 0..127 move one 16-byte (pair, token) entry per tile
+    const bool bc_mover = tid < 128;
+    const float* bcsrc = p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + (tid & 15)) * 4;
+    float* const bcdst = sBC + tid * 4;
+
+    float* const myD = sD + cq * kRowF + 2 * jq;
+    float* const myU = sU + cq * kRowF + 2 * jq;
+    float* const myQ = sQ + cq * kRowF + 2 * jq;
+    const float* const cD = sD + cc * kRowF;
+    const float* const cU = sU + cc * kRowF;
+    const float* const cQ = sQ + cc * kRowF;
+    float* const p1 = sP1 + (pr * CG + cc) * kRowF;
+    float* const p2 = sP2 + (pr * CG + cc) * kRowF;
+    float* const red = sRed + r * 2 + (lo8 ? 0 : 1);
+
+    Raw2<IO> rx, rd, rz, rg;
+    float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float2 rck = make_float2(0.f, 0.f);
+    auto load_tile = [&](int ti) {
+        const int64_t t0 = (int64_t)ti * kT;
+        const int nvalid = (L - t0 < kT) ? (int)(L - t0) : kT;
+        const int nq = nvalid - 2 * jq;
+        const bool vec = p.aligned && nvalid == kT;
+        if (validq) {
+            rx.load(xr + t0 + 2 * jq, vec, nq);
+            rd.load(dr + t0 + 2 * jq, vec, nq);
+            if (zr) rz.load(zr + t0 + 2 * jq, vec, nq);
+            rg.load(gr + t0 + 2 * jq, vec, nq);
+        }
+        if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
+        if (valid) rck = *reinterpret_cast<const float2*>(ck + ti * kDState);
+    };
+    rx.zero();
+    rd.zero();
+    rz.zero();
+    rg.zero();
+    load_tile(ntiles - 1);
+    if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
+
+    float dDacc = 0.0f, dbacc = 0.0f;
+    for (int it = 0; it < ntiles; ++it) {
+        const int ti = ntiles - 1 - it;
+        const int64_t t0 = (int64_t)ti * kT;
+        const int nvalid = (L - t0 < kT) ? (int)(L - t0) : kT;
+        const int nq = nvalid - 2 * jq;
+        const bool vec = p.aligned && nvalid == kT;
+
+        // ---- pre
+        float xv[2], dv[2], zv[2], gv[2];
+        rx.widen(xv);
+        rd.widen(dv);
+        rz.widen(zv);
+        rg.widen(gv);
+        const float hs0 = rck.x, hs1 = rck.y;   // the state before the tile's first token
+        if (it + 1 < ntiles) load_tile(ti - 1);
+        float dl[2], sg[2], dsz[2], dqv[2], uu[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float v = dv[k] + bias;
+            float delta = p.softplus ? softplus_f(v) : v;
+            delta = k < nq ? delta : 0.0f;       // padding tokens: no decay, no input
+            dl[k] = delta;
+            sg[k] = p.softplus ? sigmoid_f(v) : 1.0f;
+            uu[k] = delta * xv[k];
+            const float gz = zr ? silu_f(zv[k]) : 1.0f;
+            dsz[k] = zr ? dsilu_f(zv[k]) : 0.0f;
+            dqv[k] = gv[k] * gz;
+        }
+        *reinterpret_cast<float2*>(myD) = make_float2(dl[0], dl[1]);
+        *reinterpret_cast<float2*>(myU) = make_float2(uu[0], uu[1]);
+        *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
+        __syncthreads();
+
+        // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint
+        const float* bct = sBC + (it & 1) * kBcT + pr * (kT * 4);
+        float hs[kT][2];
+        {
+            float h0 = hs0, h1 = hs1;
+#pragma unroll
+            for (int g4 = 0; g4 < kT; g4 += 4) {
+                const float4 D4 = *reinterpret_cast<const float4*>(cD + g4);
+                const float4 U4 = *reinterpret_cast<const float4*>(cU + g4);
+                const float4 Q4 = *reinterpret_cast<const float4*>(cQ + g4);
+                const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+                const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
+                const float Qs[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
+                float out[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int k = g4 + j;
+                    const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
+                    const float e0 = fast_exp2(Ds[j] * a2[0]);
+                    const float e1 = fast_exp2(Ds[j] * a2[1]);
+                    h0 = __builtin_fmaf(e0, h0, q.x * Us[j]);
+                    h1 = __builtin_fmaf(e1, h1, q.y * Us[j]);
+                    hs[k][0] = h0;
+                    hs[k][1] = h1;
+                    out[j] = __builtin_fmaf(q.w, h1, q.z * h0);
+                    const float sc = row_sum2(Qs[j] * h0, Qs[j] * h1, lo8);
+                    if ((tid & 7) == 0) red[k * kLaneRows * 2] = sc;
+                }
+                *reinterpret_cast<float4*>(p1 + g4) = make_float4(out[0], out[1], out[2], out[3]);
+            }
+        }
+        __syncthreads();
+
+        // ---- mid: q_t and dz_t for (cq, 2 tokens); the workgroup's dC partial sums
+        float qv[2];
+        {
+            float2 s2 = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float2 a = *reinterpret_cast<const float2*>(sP1 + (q * CG + cq) * kRowF + 2 * jq);
+                s2.x += a.x;
+                s2.y += a.y;
+            }
+            qv[0] = __builtin_fmaf(Dd, xv[0], s2.x);
+            qv[1] = __builtin_fmaf(Dd, xv[1], s2.y);
+            if (zr && validq && nq > 0)
+                store2(dzr + t0 + 2 * jq, vec, nq, gv[0] * qv[0] * dsz[0], gv[1] * qv[1] * dsz[1]);
+        }
+        if (tid < 256) {
+            const int k = tid >> 4, n = tid & 15;
+            float sum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kRowsPerPair; ++j)
+                sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 2 + (n & 1)];
+            if (k < nvalid) pbc[(t0 + k) * 32 + 16 + n] = sum;
+        }
+        __syncthreads();
+
+        // ---- bwd: the adjoint recurrence over the tile, last token first
+#pragma unroll
+        for (int g4 = kT - 4; g4 >= 0; g4 -= 4) {
+            const float4 D4 = *reinterpret_cast<const float4*>(cD + g4);
+            const float4 U4 = *reinterpret_cast<const float4*>(cU + g4);
+            const float4 Q4 = *reinterpret_cast<const float4*>(cQ + g4);
+            const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+            const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
+            const float Qs[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
+            float o1[4], o2[4];
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                const int k = g4 + j;
+                const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
+                const float e0 = fast_exp2(Ds[j] * a2[0]);
+                const float e1 = fast_exp2(Ds[j] * a2[1]);
+                const float G0 = __builtin_fmaf(Qs[j], q.z, Gc[0]);
+                const float G1 = __builtin_fmaf(Qs[j], q.w, Gc[1]);
+                const float hp0 = k > 0 ? hs[k > 0 ? k - 1 : 0][0] : hs0;
+                const float hp1 = k > 0 ? hs[k > 0 ? k - 1 : 0][1] : hs1;
+                o1[j] = __builtin_fmaf(G1, q.y, G0 * q.x);          // G.B
+                const float w0 = G0 * hp0 * e0;
+                const float w1 = G1 * hp1 * e1;
+                o2[j] = __builtin_fmaf(w1, Ar[1], w0 * Ar[0]);      // G.h.a.A
+                dA[0] = __builtin_fmaf(w0, Ds[j], dA[0]);
+                dA[1] = __builtin_fmaf(w1, Ds[j], dA[1]);
+                const float sb = row_sum2(G0 * Us[j], G1 * Us[j], lo8);
+                if ((tid & 7) == 0) red[k * kLaneRows * 2] = sb;
+                Gc[0] = e0 * G0;
+                Gc[1] = e1 * G1;
+            }
+            *reinterpret_cast<float4*>(p1 + g4) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+            *reinterpret_cast<float4*>(p2 + g4) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+        }
+        __syncthreads();
+
+        // ---- post: dx, ddelta for (cq, 2 tokens); the workgroup's dB partial sums
+        {
+            float2 du = make_float2(0.f, 0.f), da = du;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float2 a = *reinterpret_cast<const float2*>(sP1 + (q * CG + cq) * kRowF + 2 * jq);
+                const float2 c = *reinterpret_cast<const float2*>(sP2 + (q * CG + cq) * kRowF + 2 * jq);
+                du.x += a.x;
+                du.y += a.y;
+                da.x += c.x;
+                da.y += c.y;
+            }
+            const float dus[2] = {du.x, du.y}, das[2] = {da.x, da.y};
+            float dxo[2], ddo[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                dxo[k] = __builtin_fmaf(dqv[k], Dd, dus[k] * dl[k]);
+                const float dD = __builtin_fmaf(dus[k], xv[k], das[k]);
+                ddo[k] = dD * sg[k];
+                if (k < nq) {
+                    dDacc = __builtin_fmaf(dqv[k], xv[k], dDacc);
+                    dbacc += ddo[k];
+                }
+            }
+            if (validq && nq > 0) {
+                store2(dxr + t0 + 2 * jq, vec, nq, dxo[0], dxo[1]);
+                store2(ddr + t0 + 2 * jq, vec, nq, ddo[0], ddo[1]);
+            }
+        }
+        if (tid < 256) {
+            const int k = tid >> 4, n = tid & 15;
+            float sum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kRowsPerPair; ++j)
+                sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 2 + (n & 1)];
+            if (k < nvalid) pbc[(t0 + k) * 32 + n] = sum;
+        }
+        // the next tile's B/C into the other buffer (last read before the barrier above)
+        if (bc_mover && it + 1 < ntiles)
+            *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcT) = rbc;
+        __syncthreads();
+    }
+
+    // ---- per-row results: dh0 = a_0 G_0 (the carry after token 0), dA partials
+    if (valid) {
+        if (p.dh0)
+            *reinterpret_cast<float2*>(p.dh0 + row * kDState + 2 * pr) = make_float2(Gc[0], Gc[1]);
+        *reinterpret_cast<float2*>(p.part_A + row * kDState + 2 * pr) = make_float2(dA[0], dA[1]);
+    }
+    // dD and dbias of channel cq: sum over its 8 token threads (lanes 8c..8c+7)
+    dDacc += SSM_DPP(dDacc, 0x141);
+    dDacc += SSM_DPP(dDacc, 0x4E);
+    dDacc += SSM_DPP(dDacc, 0xB1);
+    dbacc += SSM_DPP(dbacc, 0x141);
+    dbacc += SSM_DPP(dbacc, 0x4E);
+    dbacc += SSM_DPP(dbacc, 0xB1);
+    if (jq == 0 && validq) {
+        p.part_D[rowq] = dDacc;
+        p.part_bias[rowq] = dbacc;
+    }
+}
+
+// dB[b][t][n] and dC[b][t][n]: the workgroups' partial sums over channel groups, in
+// group order. One thread per (b, t, 32 values).
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ dB,
+                                                            float* __restrict__ dC,
+                                                            int64_t batch, int64_t L,
+                                                            int groups) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= batch * L * 32) return;
+    const int64_t b = i / (L * 32);
+    const int64_t rem = i - b * L * 32;       // t * 32 + n32
+    const float* src = part + (b * groups) * L * 32 + rem;
+    float s = 0.0f;
+    for (int g = 0; g < groups; ++g) s += src[(int64_t)g * L * 32];
+    const int64_t t = rem / 32;
+    const int n32 = (int)(rem % 32);
+    float* out = n32 < 16 ? dB : dC;
+    out[(b * L + t) * kDState + (n32 & 15)] = s;
+}
+
+// dA[d][n], dD[d], dbias[d]: sums over batch rows, in row order.
+__global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
+    const float* __restrict__ part_A, const float* __restrict__ part_D,
+    const float* __restrict__ part_bias, float* __restrict__ dA, float* __restrict__ dD,
+    float* __restrict__ dbias, int64_t batch, int64_t dim) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < dim * kDState) {
+        float s = 0.0f;
+        for (int64_t b = 0; b < batch; ++b) s += part_A[b * dim * kDState + i];
+        dA[i] = s;
+    }
+    if (i < dim) {
+        float sd = 0.0f, sb = 0.0f;
+        for (int64_t b = 0; b < batch; ++b) {
+            sd += part_D[b * dim + i];
+            sb += part_bias[b * dim + i];
+        }
+        if (dD) dD[i] = sd;
+        if (dbias) dbias[i] = sb;
+    }
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t stream,
+                           hipEvent_t ev_begin, hipEvent_t ev_end) {
+    const dim3 grid((unsigned)(prm.batch * prm.groups_per_batch));
+    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipGetLastError();
+#define SSM_BWD(IO, N)                                                                     \
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, N>), grid, dim3(N * 8), 0, stream, prm)
+    if (bf16) {
+        switch (cg) {
+            case 32: SSM_BWD(uint16_t, 32); break;
+            case 48: SSM_BWD(uint16_t, 48); break;
+            case 64: SSM_BWD(uint16_t, 64); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (cg) {
+            case 32: SSM_BWD(float, 32); break;
+            case 48: SSM_BWD(float, 48); break;
+            case 64: SSM_BWD(float, 64); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef SSM_BWD
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return hipGetLastError();
+    {
+        const int64_t n = prm.batch * prm.seqlen * 32;
+        hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
+                           stream, prm.part_bc, prm.dB, prm.dC, prm.batch, prm.seqlen,
+                           prm.groups_per_batch);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)cdiv(prm.dim * kDState, 256)),
+                       dim3(256), 0, stream, prm.part_A, prm.part_D, prm.part_bias, prm.dA,
+                       prm.dD, prm.dbias, prm.batch, prm.dim);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -1,0 +1,65 @@
+// ssm_device.h - element-wise device helpers shared by the library's HIP sources
+// (softplus, SiLU and their derivatives on the hardware exp2/log2/rcp, bf16 <-> fp32).
+// Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+namespace dev {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- element-wise
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
+__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// softplus(v) = max(v, 0) + log1p(e^-|v|). log1p(e) is taken as log(w) + (e - (w - 1))
+// with w = 1 + e rounded: the second term restores what the rounding of 1 + e lost
+// (w - 1 is exact for w in [1, 2]), so small e keeps full relative accuracy.
+__device__ __forceinline__ float softplus_f(float v) {
+    const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+    const float w = 1.0f + e;
+    const float r = e - (w - 1.0f);
+    const float lp = __builtin_fmaf(fast_log2(w), kLn2, r);
+    return __builtin_fmaxf(v, 0.0f) + lp;
+}
+
+// silu(z) = z / (1 + e^-z); for z -> -inf the exp overflows to inf, rcp gives 0.
+__device__ __forceinline__ float silu_f(float z) {
+    return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // RNE
+}
+__device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_one(uint16_t* p, float v) {
+    *p = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// sigma(v) = 1 / (1 + e^-v): the derivative of softplus
+__device__ __forceinline__ float sigmoid_f(float v) {
+    return fast_rcp(1.0f + fast_exp2(-v * kLog2e));
+}
+
+// d silu / dz = s (1 + z (1 - s)) with s = sigma(z)
+__device__ __forceinline__ float dsilu_f(float z) {
+    const float s = sigmoid_f(z);
+    return s * __builtin_fmaf(z, 1.0f - s, 1.0f);
+}
+
+}  // namespace dev
+}  // namespace ssm

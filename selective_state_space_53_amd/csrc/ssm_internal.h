@@ -37,6 +37,9 @@ struct ScanParams {
     float* chunk_sum;    // [batch*dim][nchunks]
     int32_t* chunk_flag; // [nchunks]: 1 = a sequence begins inside the chunk (packed input)
     const int32_t* cu;   // packed sequences: [nseq+1] token offsets, or null (batch rows)
+    float* ckpt;         // checkpoint pass: [batch*dim][nckpt][16], the state before every
+                         // 16th token (then y is not written); null otherwise
+    int64_t nckpt;
     int64_t batch, seqlen, dim, lpad, chunk_len;
     int32_t nchunks, ngroups, groups_per_batch, chunk_offset;
     int32_t nseq;
@@ -69,6 +72,34 @@ struct ConvParams {
     int32_t silu, aligned;
 };
 
+struct BwdParams {
+    const void* x;
+    const void* delta;
+    const void* z;
+    const void* dy;
+    const float* A;
+    const float* D;
+    const float* bias;
+    const float* dh_final;   // [batch*dim][16] or null
+    const float* ckpt;       // [batch*dim][nckpt][16]: the state before every 16th token
+    const float* bcq;        // B and C widened, as for the forward
+    void* dx;
+    void* ddelta;
+    void* dz;
+    float* dA;               // [dim][16]
+    float* dB;               // [batch][seqlen][16]
+    float* dC;
+    float* dD;               // [dim] or null
+    float* dbias;            // [dim] or null
+    float* dh0;              // [batch*dim][16] or null
+    float* part_bc;          // [batch][groups_per_batch][seqlen][32]: dB (16) then dC (16)
+    float* part_A;           // [batch*dim][16]
+    float* part_D;           // [batch*dim]
+    float* part_bias;        // [batch*dim]
+    int64_t batch, seqlen, dim, lpad, nckpt;
+    int32_t groups_per_batch, softplus, aligned;
+};
+
 // ev_begin / ev_end (may be null) are recorded around the launch of the scan kernel
 // that writes y.
 hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* B, const void* C,
@@ -76,6 +107,9 @@ hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* 
 hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream);
 // h_final[i] = h0 ? h0[i] : 0 for i < n (packed input with no tokens: every sequence is empty)
 hipError_t launch_copy_state(const float* h0, float* h_final, int64_t n, hipStream_t stream);
+// The backward kernel (ev_begin / ev_end around it) and its reductions.
+hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t stream,
+                           hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_conv1d_fwd(const ConvParams& prm, bool bf16, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvParams& prm, bool bf16, hipStream_t stream);
 

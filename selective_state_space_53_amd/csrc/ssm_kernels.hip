@@ -37,52 +37,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssm_device.h"
 #include "ssm_internal.h"
 
 namespace ssm {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+using namespace dev;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------- element-wise
-__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
-__device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
-__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
-
-// softplus(v) = max(v, 0) + log1p(e^-|v|). log1p(e) is taken as log(w) + (e - (w - 1))
-// with w = 1 + e rounded: the second term restores what the rounding of 1 + e lost
-// (w - 1 is exact for w in [1, 2]), so small e keeps full relative accuracy.
-__device__ __forceinline__ float softplus_f(float v) {
-    const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
-    const float w = 1.0f + e;
-    const float r = e - (w - 1.0f);
-    const float lp = __builtin_fmaf(fast_log2(w), kLn2, r);
-    return __builtin_fmaxf(v, 0.0f) + lp;
-}
-
-// silu(z) = z / (1 + e^-z); for z -> -inf the exp overflows to inf, rcp gives 0.
-__device__ __forceinline__ float silu_f(float z) {
-    return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    f32x2_t f = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // RNE
-}
-__device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_one(uint16_t* p, float v) {
-    *p = __builtin_bit_cast(uint16_t, (__bf16)v);
-}
 
 // Four consecutive tokens of one row, kept raw in registers between the load
 // (issued one tile ahead) and the use. `vec` = the 4 tokens are in range and the
@@ -216,13 +179,15 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int64_t t) {
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
 // without an event take the same unrolled path as unpacked input.
-template <typename IO, bool LOCAL, bool REV, bool PACKED, int CG>
+template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
+    static_assert(!CKPT || (!LOCAL && !REV && !PACKED), "checkpoints: causal, final pass");
     constexpr int kRowsPerPair = CG / 16;
+    constexpr bool kOut = !LOCAL && !CKPT;   // this pass writes y
     __shared__ float sD[CG * kLdsRow];
     __shared__ float sU[CG * kLdsRow];
-    __shared__ float sP[LOCAL ? 4 : 8 * CG * kLdsRow];
+    __shared__ float sP[kOut ? 8 * CG * kLdsRow : 4];
     __shared__ float sBC[2 * kBcTile];
 
     const int tid = threadIdx.x;
@@ -271,8 +236,10 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     const float Dd = (validq && p.D) ? p.D[dq] : 0.0f;
     const IO* xr = static_cast<const IO*>(p.x) + rowq * p.seqlen;
     const IO* dr = static_cast<const IO*>(p.delta) + rowq * p.seqlen;
-    const IO* zr = (!LOCAL && p.z) ? static_cast<const IO*>(p.z) + rowq * p.seqlen : nullptr;
-    IO* yr = LOCAL ? nullptr : static_cast<IO*>(p.y) + rowq * p.seqlen;
+    const IO* zr = (kOut && p.z) ? static_cast<const IO*>(p.z) + rowq * p.seqlen : nullptr;
+    IO* yr = kOut ? static_cast<IO*>(p.y) + rowq * p.seqlen : nullptr;
+    // CKPT: the state before every 16th token, [row][t/16][16]
+    float* const ck = CKPT ? p.ckpt + row * p.nckpt * kDState + 2 * pr : nullptr;
     // B/C staging: the first 256 threads each move 16 bytes (one token of one pair)
     const bool bc_mover = tid < 256;
     const float* bcsrc = p.bcq + ((b * 8 + (tid >> 5)) * p.lpad + (tid & 31)) * 4;
@@ -355,7 +322,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         float xv[4], dv[4], zv[4];
         rx.widen(xv);
         rdl.widen(dv);
-        if (!LOCAL) rz.widen(zv);
+        if (kOut) rz.widen(zv);
         if (it + 1 < ntiles) load_tile(tile_of(it + 1));
         float dl[4], uu[4], post_a[4], post_g[4];
 #pragma unroll
@@ -366,7 +333,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             dl[k] = delta;
             uu[k] = delta * xv[k];
         }
-        if (!LOCAL) {
+        if (kOut) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 post_g[k] = zr ? silu_f(zv[k]) : 1.0f;
@@ -389,17 +356,22 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         const float e1 = fast_exp2(DS * a2[1]);                                       \
         h[0] = __builtin_fmaf(e0, h[0], Q.x * US);                                    \
         h[1] = __builtin_fmaf(e1, h[1], Q.y * US);                                    \
-        if (!LOCAL) OUT = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                      \
-        else if (pr == 0) dsum += DS;                                                 \
+        if (kOut) OUT = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                        \
+        else if (LOCAL && pr == 0) dsum += DS;                                        \
     }
         // quiet tile: no sequence starts or ends inside it (always, for batch rows)
         const int64_t tlast = t0 + nvalid - 1;
         const bool quiet = !packed || (REV ? (hi - 1 != tlast && lo < t0)
                                            : (lo != t0 && hi > tlast + 1));
         if (quiet) {
+            if (CKPT && valid)
+                *reinterpret_cast<float2*>(ck + (t0 / 16) * kDState) = make_float2(h[0], h[1]);
 #pragma unroll
             for (int gq = 0; gq < kTile; gq += 4) {
                 const int tq = REV ? kTile - 4 - gq : gq;
+                if (CKPT && gq == 16 && valid && t0 + 16 < p.seqlen)
+                    *reinterpret_cast<float2*>(ck + (t0 / 16 + 1) * kDState) =
+                        make_float2(h[0], h[1]);
                 const float4 D4 = *reinterpret_cast<const float4*>(coreD + tq);
                 const float4 U4 = *reinterpret_cast<const float4*>(coreU + tq);
                 const float4 q0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
@@ -418,7 +390,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                     SSM_TOKEN(pp[1], D4.y, U4.y, q1)
                     SSM_TOKEN(pp[0], D4.x, U4.x, q0)
                 }
-                if (!LOCAL)
+                if (kOut)
                     *reinterpret_cast<float4*>(pout + tq) =
                         make_float4(pp[0], pp[1], pp[2], pp[3]);
             }
@@ -442,7 +414,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                 const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
                 float pk = 0.0f;
                 SSM_TOKEN(pk, ds, us, q)
-                if (!LOCAL) pout[k] = pk;
+                if (kOut) pout[k] = pk;
                 if (real && t == (REV ? lo : hi - 1)) {     // last token of sequence s
                     save_final(s, false);
                     next_seq();
@@ -453,7 +425,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         __syncthreads();
 
         // ---- post: this thread's 4 tokens: sum the 8 pairs' partials, skip, gate, store
-        if (!LOCAL) {
+        if (kOut) {
             float yv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -584,13 +556,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(const DecodeParams p)
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename IO, bool LOCAL, bool REV, bool PACKED>
+template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT>
 hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
     switch (cg) {
-#define SSM_CASE(N)                                                                  \
-    case N:                                                                          \
-        hipLaunchKernelGGL((scan_kernel<IO, LOCAL, REV, PACKED, N>), grid, dim3(N * 8), 0, \
-                           stream, prm);                                             \
+#define SSM_CASE(N)                                                                      \
+    case N:                                                                              \
+        hipLaunchKernelGGL((scan_kernel<IO, LOCAL, REV, PACKED, CKPT, N>), grid, dim3(N * 8), \
+                           0, stream, prm);                                              \
         break;
         SSM_CASE(32)
         SSM_CASE(48)
@@ -606,11 +578,14 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
 
 template <typename IO, bool LOCAL>
 hipError_t launch_scan_dir(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
+    if (!LOCAL && prm.ckpt)
+        return launch_scan_kernel<IO, false, false, false, true>(cg, grid, stream, prm);
     if (prm.cu)
-        return prm.reverse ? launch_scan_kernel<IO, LOCAL, true, true>(cg, grid, stream, prm)
-                           : launch_scan_kernel<IO, LOCAL, false, true>(cg, grid, stream, prm);
-    return prm.reverse ? launch_scan_kernel<IO, LOCAL, true, false>(cg, grid, stream, prm)
-                       : launch_scan_kernel<IO, LOCAL, false, false>(cg, grid, stream, prm);
+        return prm.reverse
+                   ? launch_scan_kernel<IO, LOCAL, true, true, false>(cg, grid, stream, prm)
+                   : launch_scan_kernel<IO, LOCAL, false, true, false>(cg, grid, stream, prm);
+    return prm.reverse ? launch_scan_kernel<IO, LOCAL, true, false, false>(cg, grid, stream, prm)
+                       : launch_scan_kernel<IO, LOCAL, false, false, false>(cg, grid, stream, prm);
 }
 
 template <typename IO>

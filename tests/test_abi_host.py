@@ -180,3 +180,38 @@ def test_conv_update_rejects(b, kw, status):
     p.update(kw)
     assert b.lib.ssm_causal_conv1d_update(p["state"], p["x"], p["A"], p["D"], p["y"], batch, 32,
                                           width, act, 1, None) == status
+
+
+def test_binding_wraps_every_export(b):
+    for n in b.EXPORTS:
+        assert callable(getattr(b, n)), n
+
+
+def test_bwd_workspace_and_rejects(b):
+    ws = b.ssm_scan_bwd_workspace_bytes(2, 100, 64, 16, 1)
+    assert ws > b.ssm_scan_workspace_bytes(2, 100, 64, 16, 1)
+    assert b.ssm_scan_bwd_workspace_bytes(2, 100, 64, 8, 1) == 0
+    assert b.ssm_scan_bwd_workspace_bytes(2, 100, 64, 16, 1, bwd_group_channels=40) == 0
+    p = dict(P, dy=P["z"] + (1 << 35), dx=P["y"], dd=P["y"] + (1 << 34), dz=P["hf"] + (1 << 34),
+             dA=P["ws"] + (1 << 35), dB=P["ws"] + (1 << 34), dC=P["ws"] + (3 << 33),
+             dD=P["D"] + (1 << 34), dbias=P["bias"] + (1 << 34), dh0=P["h0"] + (1 << 34))
+
+    def call(**over):
+        q = dict(p)
+        q.update(over)
+        return b.lib.ssm_scan_bwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"],
+                                  q["bias"], 1, q["h0"], q["dy"], None, q["dx"], q["dd"], q["dz"],
+                                  q["dA"], q["dB"], q["dC"], q["dD"], q["dbias"], q["dh0"], 2,
+                                  100, 64, 16, 1, q["ws"], 1 << 40, None, None)
+    assert call(dy=None) == 1
+    assert call(dz=None) == 1                  # z given, dz missing
+    assert call(dx=P["x"]) == 1                # output overlaps an input
+    assert call(dB=p["dC"]) == 1               # outputs overlap each other
+    assert call(dx=P["y"] + 8) == 2            # misaligned
+    assert call(ws=None) == 3
+    opts = b.ScanOptions(0, 0, 0, None, None, 1, 0, 0)
+    q = dict(p)
+    assert b.lib.ssm_scan_bwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"],
+                              q["bias"], 1, q["h0"], q["dy"], None, q["dx"], q["dd"], q["dz"],
+                              q["dA"], q["dB"], q["dC"], q["dD"], q["dbias"], q["dh0"], 2, 100,
+                              64, 16, 1, q["ws"], 1 << 40, ctypes.byref(opts), None) == 2
