@@ -368,8 +368,9 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
 constexpr int kBwdTile = 16;
 
 // LDS bytes of one backward workgroup of cg channels (must match scan_bwd_kernel):
-// Delta, u, dq [cg][20]; two [8][cg][20] partial arrays; two B/C tiles; row sums.
-int64_t bwd_lds_bytes(int cg) { return (int64_t)(396 * cg + 1024) * 4; }
+// Delta, u, dq [cg][20]; two [8][cg][16] partial arrays; two B/C tiles; row sums
+// [16][cg/2][4].
+int64_t bwd_lds_bytes(int cg) { return (int64_t)(348 * cg + 1024) * 4; }
 
 int choose_bwd_group(int64_t batch, int64_t dim) {
     static const int kCands[] = {64, 48, 32};
@@ -395,10 +396,10 @@ int choose_bwd_group(int64_t batch, int64_t dim) {
 }
 
 struct BwdPlan {
-    ssm::ScanPlan fwd;      // the checkpoint pass
+    ssm::ScanPlan fwd;      // the forward pass that writes q and the checkpoints
     int cg;
     int64_t nckpt;
-    size_t ws_ckpt, ws_bc, ws_A, ws_D, ws_bias, ws_total;
+    size_t ws_ckpt, ws_q, ws_bc, ws_A, ws_D, ws_bias, ws_total;
 };
 
 ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
@@ -415,13 +416,15 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
     bp->cg = req ? req : choose_bwd_group(batch, dim);
     const int64_t gpb = (dim + bp->cg - 1) / bp->cg;
     bp->nckpt = (seqlen + kBwdTile - 1) / kBwdTile;
-    int64_t ck, bc, pa, pd;
+    int64_t ck, qb, bc, pa, pd;
+    const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
     if (!bytes4(batch * dim, bp->nckpt, ssm::kDState, 4, &ck) ||
-        !bytes4(batch * gpb, seqlen, 32, 4, &bc) || !bytes4(batch * dim, ssm::kDState, 1, 4, &pa) ||
-        !bytes4(batch * dim, 1, 1, 4, &pd))
+        !bytes4(batch * dim, seqlen, elem, 1, &qb) || !bytes4(batch * gpb, seqlen, 32, 4, &bc) ||
+        !bytes4(batch * dim, ssm::kDState, 1, 4, &pa) || !bytes4(batch * dim, 1, 1, 4, &pd))
         return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
     bp->ws_ckpt = align_up(bp->fwd.ws_total, 256);
-    bp->ws_bc = align_up(bp->ws_ckpt + (size_t)ck, 256);
+    bp->ws_q = align_up(bp->ws_ckpt + (size_t)ck, 256);
+    bp->ws_bc = align_up(bp->ws_q + (size_t)qb, 256);
     bp->ws_A = align_up(bp->ws_bc + (size_t)bc, 256);
     bp->ws_D = align_up(bp->ws_A + (size_t)pa, 256);
     bp->ws_bias = align_up(bp->ws_D + (size_t)pd, 256);
@@ -510,13 +513,14 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
 
         char* ws = static_cast<char*>(workspace);
         hipStream_t strm = static_cast<hipStream_t>(stream);
-        // 1. B/C widening and the forward in checkpoint mode (the state before every
-        //    16th token), with the forward's own plan
+        // 1. B/C widening and the forward in checkpoint mode, with the forward's own
+        //    plan: it writes q (the output before the gate: no z) and the state before
+        //    every 16th token
         ssm::ScanParams fp{};
         fp.x = x;
         fp.delta = delta;
         fp.z = nullptr;
-        fp.y = nullptr;
+        fp.y = ws + bp.ws_q;
         fp.A = A;
         fp.D = D;
         fp.bias = delta_bias;
@@ -557,6 +561,7 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         prm.bias = delta_bias;
         prm.dh_final = dh_final;
         prm.ckpt = fp.ckpt;
+        prm.q = ws + bp.ws_q;
         prm.bcq = fp.bcq;
         prm.dx = dx;
         prm.ddelta = ddelta;

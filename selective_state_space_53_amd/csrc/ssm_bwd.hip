@@ -15,16 +15,16 @@
 //
 // Mapping (the forward's, with 16-token tiles): a workgroup owns CG channels of one
 // batch row and all 16 states; a lane keeps 2 states of one channel. The sequence
-// is walked tile by tile from the end. Per tile:
-//   pre    per (channel, 2 tokens): Delta, u, dq, and what post needs, into LDS
-//   fwd    from the tile's checkpoint (the state before its first token, written by
-//          the forward scan in checkpoint mode) the 16 states h_t are recomputed and
-//          kept in registers; partial readouts C.h -> LDS; dq.h (for dC) is summed
-//          over the 16 channels of a lane row with DPP and the row sums go to LDS
-//   mid    q_t and dz_t; the workgroup's dC partial sums -> HBM
-//   bwd    the adjoint recurrence over the 16 tokens (exp recomputed): partial
-//          G.B and G.h.a.A -> LDS, dA in registers, G.u (for dB) summed like dq.h
-//   post   dx, ddelta per (channel, 2 tokens); the workgroup's dB partial sums -> HBM
+// is walked tile by tile from the end. Per tile (two barriers):
+//   pre    per (channel, 2 tokens): Delta, u, dq into LDS; dz = dy q silu'(z) at once,
+//          with q (the output before the gate) written by the forward pass
+//   fwd    from the tile's checkpoint (the state before its first token, also written
+//          by the forward pass) the 16 states h_t are recomputed into registers
+//   bwd    the adjoint recurrence over the 16 tokens (exp recomputed rather than
+//          kept): partial G.B and G.h.a.A per state pair -> LDS, dA in registers, and
+//          G.u (dB) and dq.h (dC) summed over the 16 channels of a lane row with DPP
+//   post   dx, ddelta per (channel, 2 tokens); the workgroup's dB, dC partial sums ->
+//          HBM
 // Sums over channels across workgroups (dB, dC) and over batch rows (dA, dD, dbias)
 // are finished by small reduction kernels in a fixed order: no float atomics, the
 // result does not depend on scheduling.
@@ -42,7 +42,9 @@ namespace {
 using namespace dev;
 
 constexpr int kT = 16;            // tokens per backward tile
-constexpr int kRowF = kT + 4;     // padded LDS row (floats)
+constexpr int kRowF = kT + 4;     // padded LDS row of the per-channel arrays (floats)
+constexpr int kRowP = kT;         // row of the per-pair partial arrays (unpadded: their
+                                  // size decides whether two workgroups fit in a CU)
 constexpr int kBcT = 8 * kT * 4;  // floats of widened B/C per tile
 
 // Two consecutive tokens of one row, raw, loaded one tile ahead of their use.
@@ -94,18 +96,23 @@ __device__ __forceinline__ void store2(IO* p, bool vec, int n, float a, float b)
     __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)),   \
                                                           (ctrl), 0xF, 0xF, false))
 
-// Sum two values over the 16 lanes of a row: lanes 0-7 return the sum of v0, lanes
-// 8-15 the sum of v1. The first step pairs lane i with lane 15-i (row mirror) and
-// moves each lane's other value across; three more steps (half-row mirror, then
-// quad swaps of 2 and 1) finish each half.
-__device__ __forceinline__ float row_sum2(float v0, float v1, bool lo) {
-    float keep = lo ? v0 : v1;
-    const float send = lo ? v1 : v0;
-    keep += SSM_DPP(send, 0x140);   // row_mirror
-    keep += SSM_DPP(keep, 0x141);   // row_half_mirror
-    keep += SSM_DPP(keep, 0x4E);    // quad_perm [2,3,0,1]
-    keep += SSM_DPP(keep, 0xB1);    // quad_perm [1,0,3,2]
-    return keep;
+// Sum four values over the 16 lanes of a row (a reduce-scatter): afterwards lanes 0-3
+// hold the sum of v0, lanes 4-7 of v1, lanes 8-11 of v2, lanes 12-15 of v3. Each step
+// pairs lanes across a half (mirror of the row, then of each half) and moves the
+// values the lane does not keep; two quad swaps finish. 6 selects + 5 DPP adds.
+__device__ __forceinline__ float row_sum4(float v0, float v1, float v2, float v3, int lane16) {
+    const bool lo = lane16 < 8;
+    float k0 = lo ? v0 : v2, k1 = lo ? v1 : v3;      // kept: (v0, v1) low, (v2, v3) high
+    const float s0 = lo ? v2 : v0, s1 = lo ? v3 : v1;
+    k0 += SSM_DPP(s0, 0x140);   // row_mirror: lane i <-> 15 - i
+    k1 += SSM_DPP(s1, 0x140);
+    const bool lo4 = (lane16 & 4) == 0;
+    float k = lo4 ? k0 : k1;
+    const float s = lo4 ? k1 : k0;
+    k += SSM_DPP(s, 0x141);     // row_half_mirror: lane i <-> 7 - i within each half
+    k += SSM_DPP(k, 0x4E);      // quad_perm [2,3,0,1]
+    k += SSM_DPP(k, 0xB1);      // quad_perm [1,0,3,2]
+    return k;
 }
 
 template <typename IO, int CG>
@@ -116,10 +123,10 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     __shared__ float sD[CG * kRowF];            // Delta
     __shared__ float sU[CG * kRowF];            // u = Delta x
     __shared__ float sQ[CG * kRowF];            // dq
-    __shared__ float sP1[8 * CG * kRowF];       // per state pair: readout, then G.B
-    __shared__ float sP2[8 * CG * kRowF];       // per state pair: G.h.a.A
+    __shared__ float sP1[8 * CG * kRowP];       // per state pair: G.B
+    __shared__ float sP2[8 * CG * kRowP];       // per state pair: G.h.a.A
     __shared__ float sBC[2 * kBcT];             // [buffer][pair][token][B0 B1 C0 C1]
-    __shared__ float sRed[kT * kLaneRows * 2];  // [token][lane row][2]: row sums
+    __shared__ float sRed[kT * kLaneRows * 4];  // [token][lane row][dB0 dB1 dC0 dC1]
 
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x / p.groups_per_batch;
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     const int64_t d = d0 + cc;
     const bool valid = d < p.dim;
     const int64_t row = b * p.dim + d;
-    const bool lo8 = (tid & 15) < 8;
+    const int lane16 = tid & 15;
     // pre/post mapping: (channel cq, tokens 2jq and 2jq+1 of the tile)
     const int cq = tid >> 3;
     const int jq = tid & 7;
@@ -162,6 +169,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     const IO* dr = static_cast<const IO*>(p.delta) + rowq * L;
     const IO* zr = p.z ? static_cast<const IO*>(p.z) + rowq * L : nullptr;
     const IO* gr = static_cast<const IO*>(p.dy) + rowq * L;
+    const IO* qr = static_cast<const IO*>(p.q) + rowq * L;
     IO* dxr = static_cast<IO*>(p.dx) + rowq * L;
     IO* ddr = static_cast<IO*>(p.ddelta) + rowq * L;
     IO* dzr = p.z ? static_cast<IO*>(p.dz) + rowq * L : nullptr;
@@ -178,11 +186,12 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     const float* const cD = sD + cc * kRowF;
     const float* const cU = sU + cc * kRowF;
     const float* const cQ = sQ + cc * kRowF;
-    float* const p1 = sP1 + (pr * CG + cc) * kRowF;
-    float* const p2 = sP2 + (pr * CG + cc) * kRowF;
-    float* const red = sRed + r * 2 + (lo8 ? 0 : 1);
+    float* const p1 = sP1 + (pr * CG + cc) * kRowP;
+    float* const p2 = sP2 + (pr * CG + cc) * kRowP;
+    // lanes 0, 4, 8, 12 of a row hold its sums of dB0, dB1, dC0, dC1
+    float* const red = sRed + r * 4 + (lane16 >> 2);
 
-    Raw2<IO> rx, rd, rz, rg;
+    Raw2<IO> rx, rd, rz, rg, rq;
     float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
     float2 rck = make_float2(0.f, 0.f);
     auto load_tile = [&](int ti) {
@@ -193,7 +202,10 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         if (validq) {
             rx.load(xr + t0 + 2 * jq, vec, nq);
             rd.load(dr + t0 + 2 * jq, vec, nq);
-            if (zr) rz.load(zr + t0 + 2 * jq, vec, nq);
+            if (zr) {
+                rz.load(zr + t0 + 2 * jq, vec, nq);
+                rq.load(qr + t0 + 2 * jq, vec, nq);
+            }
             rg.load(gr + t0 + 2 * jq, vec, nq);
         }
         if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
@@ -203,7 +215,9 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     rd.zero();
     rz.zero();
     rg.zero();
+    rq.zero();
     load_tile(ntiles - 1);
+
     if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
 
     float dDacc = 0.0f, dbacc = 0.0f;
@@ -214,15 +228,16 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
 
-        // ---- pre
-        float xv[2], dv[2], zv[2], gv[2];
+        // ---- pre: Delta, u, dq to LDS; dz right away (q comes from the forward pass)
+        float xv[2], dv[2], zv[2], gv[2], qv[2];
         rx.widen(xv);
         rd.widen(dv);
         rz.widen(zv);
         rg.widen(gv);
+        rq.widen(qv);
         const float hs0 = rck.x, hs1 = rck.y;   // the state before the tile's first token
         if (it + 1 < ntiles) load_tile(ti - 1);
-        float dl[2], sg[2], dsz[2], dqv[2], uu[2];
+        float dl[2], sg[2], dqv[2], uu[2], dzv[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const float v = dv[k] + bias;
@@ -232,12 +247,13 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             sg[k] = p.softplus ? sigmoid_f(v) : 1.0f;
             uu[k] = delta * xv[k];
             const float gz = zr ? silu_f(zv[k]) : 1.0f;
-            dsz[k] = zr ? dsilu_f(zv[k]) : 0.0f;
             dqv[k] = gv[k] * gz;
+            dzv[k] = zr ? gv[k] * qv[k] * dsilu_f(zv[k]) : 0.0f;
         }
         *reinterpret_cast<float2*>(myD) = make_float2(dl[0], dl[1]);
         *reinterpret_cast<float2*>(myU) = make_float2(uu[0], uu[1]);
         *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
+        if (zr && validq && nq > 0) store2(dzr + t0 + 2 * jq, vec, nq, dzv[0], dzv[1]);
         __syncthreads();
 
         // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint
@@ -249,54 +265,19 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             for (int g4 = 0; g4 < kT; g4 += 4) {
                 const float4 D4 = *reinterpret_cast<const float4*>(cD + g4);
                 const float4 U4 = *reinterpret_cast<const float4*>(cU + g4);
-                const float4 Q4 = *reinterpret_cast<const float4*>(cQ + g4);
                 const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
                 const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
-                const float Qs[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
-                float out[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int k = g4 + j;
-                    const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
-                    const float e0 = fast_exp2(Ds[j] * a2[0]);
-                    const float e1 = fast_exp2(Ds[j] * a2[1]);
-                    h0 = __builtin_fmaf(e0, h0, q.x * Us[j]);
-                    h1 = __builtin_fmaf(e1, h1, q.y * Us[j]);
+                    const float2 bb = *reinterpret_cast<const float2*>(bct + k * 4);
+                    h0 = __builtin_fmaf(fast_exp2(Ds[j] * a2[0]), h0, bb.x * Us[j]);
+                    h1 = __builtin_fmaf(fast_exp2(Ds[j] * a2[1]), h1, bb.y * Us[j]);
                     hs[k][0] = h0;
                     hs[k][1] = h1;
-                    out[j] = __builtin_fmaf(q.w, h1, q.z * h0);
-                    const float sc = row_sum2(Qs[j] * h0, Qs[j] * h1, lo8);
-                    if ((tid & 7) == 0) red[k * kLaneRows * 2] = sc;
                 }
-                *reinterpret_cast<float4*>(p1 + g4) = make_float4(out[0], out[1], out[2], out[3]);
             }
         }
-        __syncthreads();
-
-        // ---- mid: q_t and dz_t for (cq, 2 tokens); the workgroup's dC partial sums
-        float qv[2];
-        {
-            float2 s2 = make_float2(0.f, 0.f);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float2 a = *reinterpret_cast<const float2*>(sP1 + (q * CG + cq) * kRowF + 2 * jq);
-                s2.x += a.x;
-                s2.y += a.y;
-            }
-            qv[0] = __builtin_fmaf(Dd, xv[0], s2.x);
-            qv[1] = __builtin_fmaf(Dd, xv[1], s2.y);
-            if (zr && validq && nq > 0)
-                store2(dzr + t0 + 2 * jq, vec, nq, gv[0] * qv[0] * dsz[0], gv[1] * qv[1] * dsz[1]);
-        }
-        if (tid < 256) {
-            const int k = tid >> 4, n = tid & 15;
-            float sum = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kRowsPerPair; ++j)
-                sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 2 + (n & 1)];
-            if (k < nvalid) pbc[(t0 + k) * 32 + 16 + n] = sum;
-        }
-        __syncthreads();
 
         // ---- bwd: the adjoint recurrence over the tile, last token first
 #pragma unroll
@@ -324,8 +305,10 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 o2[j] = __builtin_fmaf(w1, Ar[1], w0 * Ar[0]);      // G.h.a.A
                 dA[0] = __builtin_fmaf(w0, Ds[j], dA[0]);
                 dA[1] = __builtin_fmaf(w1, Ds[j], dA[1]);
-                const float sb = row_sum2(G0 * Us[j], G1 * Us[j], lo8);
-                if ((tid & 7) == 0) red[k * kLaneRows * 2] = sb;
+                // dB += G u, dC += dq h (this token's state), summed over the row
+                const float sr = row_sum4(G0 * Us[j], G1 * Us[j], Qs[j] * hs[k][0],
+                                          Qs[j] * hs[k][1], lane16);
+                if ((lane16 & 3) == 0) red[k * kLaneRows * 4] = sr;
                 Gc[0] = e0 * G0;
                 Gc[1] = e1 * G1;
             }
@@ -334,13 +317,13 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         }
         __syncthreads();
 
-        // ---- post: dx, ddelta for (cq, 2 tokens); the workgroup's dB partial sums
+        // ---- post: dx, ddelta for (cq, 2 tokens); the workgroup's dB, dC partial sums
         {
             float2 du = make_float2(0.f, 0.f), da = du;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const float2 a = *reinterpret_cast<const float2*>(sP1 + (q * CG + cq) * kRowF + 2 * jq);
-                const float2 c = *reinterpret_cast<const float2*>(sP2 + (q * CG + cq) * kRowF + 2 * jq);
+                const float2 a = *reinterpret_cast<const float2*>(sP1 + (q * CG + cq) * kRowP + 2 * jq);
+                const float2 c = *reinterpret_cast<const float2*>(sP2 + (q * CG + cq) * kRowP + 2 * jq);
                 du.x += a.x;
                 du.y += a.y;
                 da.x += c.x;
@@ -363,18 +346,24 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 store2(ddr + t0 + 2 * jq, vec, nq, ddo[0], ddo[1]);
             }
         }
-        if (tid < 256) {
-            const int k = tid >> 4, n = tid & 15;
+        // 16 tokens x 32 values (dB then dC): value i < 512 (i = tid, tid + CG*8) is the
+        // sum over the CG/16 rows of value i & 31 of token i >> 5; a wave writes 64
+        // contiguous floats
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = tid + m * CG * 8;
+            if (i >= kT * 32) break;
+            const int k = i >> 5, v = i & 31;
+            const int n = v & 15, which = v >> 4;             // which: 0 = dB, 1 = dC
             float sum = 0.0f;
 #pragma unroll
             for (int j = 0; j < kRowsPerPair; ++j)
-                sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 2 + (n & 1)];
-            if (k < nvalid) pbc[(t0 + k) * 32 + n] = sum;
+                sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 4 + which * 2 + (n & 1)];
+            if (k < nvalid) pbc[(t0 + k) * 32 + v] = sum;
         }
         // the next tile's B/C into the other buffer (last read before the barrier above)
         if (bc_mover && it + 1 < ntiles)
             *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcT) = rbc;
-        __syncthreads();
     }
 
     // ---- per-row results: dh0 = a_0 G_0 (the carry after token 0), dA partials
@@ -408,8 +397,18 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
     const int64_t b = i / (L * 32);
     const int64_t rem = i - b * L * 32;       // t * 32 + n32
     const float* src = part + (b * groups) * L * 32 + rem;
+    const int64_t stride = L * 32;
     float s = 0.0f;
-    for (int g = 0; g < groups; ++g) s += src[(int64_t)g * L * 32];
+    int g = 0;
+    for (; g + 4 <= groups; g += 4) {   // four loads in flight, added in group order
+        const float a0 = src[(int64_t)g * stride], a1 = src[(int64_t)(g + 1) * stride];
+        const float a2 = src[(int64_t)(g + 2) * stride], a3 = src[(int64_t)(g + 3) * stride];
+        s += a0;
+        s += a1;
+        s += a2;
+        s += a3;
+    }
+    for (; g < groups; ++g) s += src[(int64_t)g * stride];
     const int64_t t = rem / 32;
     const int n32 = (int)(rem % 32);
     float* out = n32 < 16 ? dB : dC;

@@ -82,6 +82,7 @@ struct BwdParams {
     const float* bias;
     const float* dh_final;   // [batch*dim][16] or null
     const float* ckpt;       // [batch*dim][nckpt][16]: the state before every 16th token
+    const void* q;           // [batch][dim][seqlen] io: the forward output before the gate
     const float* bcq;        // B and C widened, as for the forward
     void* dx;
     void* ddelta;

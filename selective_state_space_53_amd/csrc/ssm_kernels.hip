@@ -175,6 +175,8 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int64_t t) {
 // state and its sum of Delta. Otherwise: outputs y (and final states).
 // REV = anti-causal: tiles, and tokens inside a tile, are taken from the last to the
 // first; the tiles stay where they are in memory, so loads and stores are the same.
+// CKPT = the forward of the backward pass: as the last pass, and it also stores the
+// state before every 16th token (the backward recomputes its tiles from them).
 // PACKED = packed sequences (p.cu set): the state is reset to the sequence's initial state
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
     static_assert(!CKPT || (!LOCAL && !REV && !PACKED), "checkpoints: causal, final pass");
     constexpr int kRowsPerPair = CG / 16;
-    constexpr bool kOut = !LOCAL && !CKPT;   // this pass writes y
+    constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
     __shared__ float sD[CG * kLdsRow];
     __shared__ float sU[CG * kLdsRow];
     __shared__ float sP[kOut ? 8 * CG * kLdsRow : 4];
