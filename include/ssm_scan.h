@@ -91,6 +91,11 @@ typedef struct {
                            summed output.                                                 */
     int32_t bwd_group_channels; /* ssm_scan_bwd: channels per backward workgroup, 0 =
                            library choice, else 32, 48 or 64                              */
+    int64_t bwd_chunk_len; /* ssm_scan_bwd: tokens per chunk of the backward (a pass that
+                           runs the gradient chain of every chunk but the first from zero,
+                           a carry from the last chunk backwards, then every chunk from its
+                           carried-in gradient); 0 = library choice, else a multiple of 32
+                           (>= seqlen: one pass)                                          */
 } ssm_scan_options;
 
 /*

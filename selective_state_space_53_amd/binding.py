@@ -31,7 +31,8 @@ class ScanOptions(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int64), ("plan", ctypes.c_int32),
                 ("group_channels", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
                 ("timing_end", ctypes.c_void_p), ("reverse", ctypes.c_int32),
-                ("accumulate", ctypes.c_int32), ("bwd_group_channels", ctypes.c_int32)]
+                ("accumulate", ctypes.c_int32), ("bwd_group_channels", ctypes.c_int32),
+                ("bwd_chunk_len", ctypes.c_int64)]
 
 
 _vp = ctypes.c_void_p
@@ -115,13 +116,14 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 
 def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0,
-             reverse=False, accumulate=False, bwd_group_channels: int = 0):
+             reverse=False, accumulate=False, bwd_group_channels: int = 0, bwd_chunk_len: int = 0):
     if (plan == 0 and chunk_len == 0 and events is None and group_channels == 0
-            and not reverse and not accumulate and bwd_group_channels == 0):
+            and not reverse and not accumulate and bwd_group_channels == 0
+            and bwd_chunk_len == 0):
         return None
     ev0, ev1 = (None, None) if events is None else events
     return ctypes.byref(ScanOptions(chunk_len, plan, group_channels, ev0, ev1, int(bool(reverse)),
-                                    int(bool(accumulate)), bwd_group_channels))
+                                    int(bool(accumulate)), bwd_group_channels, bwd_chunk_len))
 
 
 def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
@@ -131,10 +133,12 @@ def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk
 
 
 def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
-                                 group_channels=0, bwd_group_channels=0) -> int:
+                                 group_channels=0, bwd_group_channels=0,
+                                 bwd_chunk_len=0) -> int:
     return lib.ssm_scan_bwd_workspace_bytes(
         batch, seqlen, dim, dstate, io_dtype,
-        _options(plan, chunk_len, None, group_channels, bwd_group_channels=bwd_group_channels))
+        _options(plan, chunk_len, None, group_channels, bwd_group_channels=bwd_group_channels,
+                 bwd_chunk_len=bwd_chunk_len))
 
 
 def ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype, plan=0, chunk_len=0,
@@ -189,7 +193,8 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
 
 def ssm_scan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=True,
                  h0=None, dh_final=None, want_dh0=False, workspace=None, plan=0, chunk_len=0,
-                 stream=None, timing_events=None, group_channels=0, bwd_group_channels=0):
+                 stream=None, timing_events=None, group_channels=0, bwd_group_channels=0,
+                 bwd_chunk_len=0):
     """Gradients of the forward scan with the same arguments, given dy [batch][dim][L]
     (and dh_final [batch][dim][16]). Returns a dict: dx, ddelta, dz (x's dtype), dA,
     dB, dC, dD, ddelta_bias, dh0 (fp32; None where the input is absent / not asked)."""
@@ -220,7 +225,7 @@ def ssm_scan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_s
     }
     code = _dtype_code(x)
     opts = _options(plan, chunk_len, timing_events, group_channels,
-                    bwd_group_channels=bwd_group_channels)
+                    bwd_group_channels=bwd_group_channels, bwd_chunk_len=bwd_chunk_len)
     ws_bytes = lib.ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, N, code, opts)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)

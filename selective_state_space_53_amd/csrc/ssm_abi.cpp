@@ -372,35 +372,65 @@ constexpr int kBwdTile = 16;
 // [16][cg/2][4].
 int64_t bwd_lds_bytes(int cg) { return (int64_t)(348 * cg + 1024) * 4; }
 
-int choose_bwd_group(int64_t batch, int64_t dim) {
-    static const int kCands[] = {64, 48, 32};
-    int best = 32;
-    double best_c = 1e300;
-    for (int cg : kCands) {
-        const int64_t groups = batch * ((dim + cg - 1) / cg);
-        int64_t k = kLdsPerCU / bwd_lds_bytes(cg);
-        const int64_t kw = 4 * 3 / (cg / 8);        // <= 168 VGPRs: 3 waves per SIMD
-        if (kw < k) k = kw;
-        const int64_t per_cu = (groups + kCUs - 1) / kCUs;
-        if (k > per_cu) k = per_cu;
-        if (k < 1) k = 1;
-        const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
-        const int64_t w = (k * (cg / 8) + 3) / 4;
-        const double c = (double)rounds * (double)w * wave_cost(w);
-        if (c < best_c * (1 - 1e-9)) {
-            best = cg;
-            best_c = c;
-        }
-    }
-    return best;
+// Relative time of one backward pass: `groups` workgroups of cg channels over `tiles`
+// 16-token tiles (as pass_cost, with the backward's LDS and its <= 168 VGPRs: 3 waves
+// per SIMD).
+double bwd_pass_cost(int64_t groups, int64_t tiles, int cg) {
+    int64_t k = kLdsPerCU / bwd_lds_bytes(cg);
+    const int64_t kw = 4 * 3 / (cg / 8);
+    if (kw < k) k = kw;
+    const int64_t per_cu = (groups + kCUs - 1) / kCUs;
+    if (k > per_cu) k = per_cu;
+    if (k < 1) k = 1;
+    const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
+    const int64_t w = (k * (cg / 8) + 3) / 4;
+    return (double)rounds * (double)(tiles + 1) * (double)w * wave_cost(w);
 }
 
 struct BwdPlan {
     ssm::ScanPlan fwd;      // the forward pass that writes q and the checkpoints
     int cg;
-    int64_t nckpt;
-    size_t ws_ckpt, ws_q, ws_bc, ws_A, ws_D, ws_bias, ws_total;
+    int64_t nckpt, chunk_len, nchunks;
+    size_t ws_ckpt, ws_q, ws_bc, ws_A, ws_D, ws_bias, ws_gc, ws_gs, ws_total;
 };
+
+// Channels per backward workgroup and chunking of the sequence (the cost model of
+// make_plan: pass 1 of the chunked backward -- only the gradient chain -- costs about a
+// quarter of a full pass).
+void choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int req_cg, int64_t req_chunk,
+                     BwdPlan* bp) {
+    static const int kCands[] = {64, 48, 32};
+    const int64_t tile = 16;
+    double best_c = 1e300;
+    bp->cg = 32;
+    bp->chunk_len = seqlen;
+    bp->nchunks = 1;
+    for (int cg : kCands) {
+        if (req_cg && cg != req_cg) continue;
+        const int64_t groups = batch * ((dim + cg - 1) / cg);
+        for (int64_t kk = 1; kk <= 4096; kk = kk < 4 ? kk + 1 : kk + kk / 2) {
+            int64_t cl = seqlen;
+            if (req_chunk > 0) {
+                cl = req_chunk;
+            } else if (kk > 1) {
+                cl = (seqlen + kk - 1) / kk;
+                cl = (cl + 31) / 32 * 32;
+            }
+            const int64_t k = (seqlen + cl - 1) / cl;
+            if (req_chunk == 0 && kk > 1 && (cl >= seqlen || cl < 256)) break;
+            const int64_t tiles = (cl + tile - 1) / tile;
+            double c = bwd_pass_cost(groups * k, tiles, cg);
+            if (k > 1) c += 0.25 * bwd_pass_cost(groups * (k - 1), tiles, cg) + 300.0;
+            if (c < best_c * (1 - 1e-9)) {
+                best_c = c;
+                bp->cg = cg;
+                bp->chunk_len = k > 1 ? cl : seqlen;
+                bp->nchunks = k;
+            }
+            if (req_chunk > 0) break;
+        }
+    }
+}
 
 ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                          ssm_dtype io_dtype, const ssm_scan_options* opts, BwdPlan* bp) {
@@ -413,22 +443,34 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
     if (req != 0 && req != 32 && req != 48 && req != 64)
         return fail(SSM_ERR_INVALID_ARGUMENT,
                     "ssm_scan_options.bwd_group_channels=%d not in {0, 32, 48, 64}", req);
-    bp->cg = req ? req : choose_bwd_group(batch, dim);
+    const int64_t req_chunk = opts ? opts->bwd_chunk_len : 0;
+    if (req_chunk < 0 || req_chunk % 32 != 0)
+        return fail(SSM_ERR_INVALID_ARGUMENT,
+                    "ssm_scan_options.bwd_chunk_len=%lld must be a multiple of 32",
+                    (long long)req_chunk);
+    choose_bwd_plan(batch, seqlen, dim, req, req_chunk, bp);
     const int64_t gpb = (dim + bp->cg - 1) / bp->cg;
+    const int64_t K = bp->nchunks;
     bp->nckpt = (seqlen + kBwdTile - 1) / kBwdTile;
-    int64_t ck, qb, bc, pa, pd;
+    int64_t ck, qb, bc, pa, pd, gc = 0, gs = 0;
     const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
     if (!bytes4(batch * dim, bp->nckpt, ssm::kDState, 4, &ck) ||
         !bytes4(batch * dim, seqlen, elem, 1, &qb) || !bytes4(batch * gpb, seqlen, 32, 4, &bc) ||
-        !bytes4(batch * dim, ssm::kDState, 1, 4, &pa) || !bytes4(batch * dim, 1, 1, 4, &pd))
+        !bytes4(batch * K, dim, ssm::kDState, 4, &pa) || !bytes4(batch * K, dim, 1, 4, &pd) ||
+        (K > 1 && (!bytes4(batch * dim, K, ssm::kDState, 4, &gc) ||
+                   !bytes4(batch * dim, K, 1, 4, &gs))))
         return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
+    if (batch * gpb * K >= (int64_t(1) << 31))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "too many backward chunks");
     bp->ws_ckpt = align_up(bp->fwd.ws_total, 256);
     bp->ws_q = align_up(bp->ws_ckpt + (size_t)ck, 256);
     bp->ws_bc = align_up(bp->ws_q + (size_t)qb, 256);
     bp->ws_A = align_up(bp->ws_bc + (size_t)bc, 256);
     bp->ws_D = align_up(bp->ws_A + (size_t)pa, 256);
     bp->ws_bias = align_up(bp->ws_D + (size_t)pd, 256);
-    bp->ws_total = align_up(bp->ws_bias + (size_t)pd, 256);
+    bp->ws_gc = align_up(bp->ws_bias + (size_t)pd, 256);
+    bp->ws_gs = align_up(bp->ws_gc + (size_t)gc, 256);
+    bp->ws_total = align_up(bp->ws_gs + (size_t)gs, 256);
     return SSM_OK;
 }
 
@@ -576,6 +618,11 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         prm.part_A = reinterpret_cast<float*>(ws + bp.ws_A);
         prm.part_D = reinterpret_cast<float*>(ws + bp.ws_D);
         prm.part_bias = reinterpret_cast<float*>(ws + bp.ws_bias);
+        prm.g_carry = bp.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.ws_gc) : nullptr;
+        prm.g_sum = bp.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.ws_gs) : nullptr;
+        prm.chunk_len = bp.chunk_len;
+        prm.nchunks = (int32_t)bp.nchunks;
+        prm.chunk_offset = 0;
         prm.batch = batch;
         prm.seqlen = seqlen;
         prm.dim = dim;
@@ -587,10 +634,10 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         if (getenv("SSMSCAN_LOG"))
             fprintf(stderr,
                     "[ssmscan] bwd b=%lld L=%lld d=%lld %s: checkpoint pass %d channels/group "
-                    "x %d chunks, backward %d channels/group\n",
+                    "x %d chunks, backward %d channels/group x %lld chunks of %lld\n",
                     (long long)batch, (long long)seqlen, (long long)dim,
                     io_dtype == SSM_BF16 ? "bf16" : "f32", bp.fwd.group_channels,
-                    bp.fwd.nchunks, bp.cg);
+                    bp.fwd.nchunks, bp.cg, (long long)bp.nchunks, (long long)bp.chunk_len);
         hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->timing_begin) : nullptr;
         hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->timing_end) : nullptr;
         e = ssm::launch_scan_bwd(bp.cg, prm, io_dtype == SSM_BF16, strm, ev0, ev1);

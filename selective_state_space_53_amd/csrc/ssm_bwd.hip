@@ -129,11 +129,16 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     __shared__ float sRed[kT * kLaneRows * 4];  // [token][lane row][dB0 dB1 dC0 dC1]
 
     const int tid = threadIdx.x;
-    const int64_t b = blockIdx.x / p.groups_per_batch;
-    const int grp = blockIdx.x % p.groups_per_batch;
+    const int64_t ngroups = p.batch * p.groups_per_batch;
+    const int64_t gidx = blockIdx.x % ngroups;
+    const int c = (int)(blockIdx.x / ngroups) + p.chunk_offset;   // chunk of the sequence
+    const int64_t b = gidx / p.groups_per_batch;
+    const int grp = (int)(gidx % p.groups_per_batch);
     const int64_t d0 = (int64_t)grp * CG;
     const int64_t L = p.seqlen;
-    const int ntiles = (int)((L + kT - 1) / kT);
+    const int64_t t_beg = (int64_t)c * p.chunk_len;
+    const int64_t t_end = (t_beg + p.chunk_len < L) ? t_beg + p.chunk_len : L;
+    const int ntiles = (int)((t_end - t_beg + kT - 1) / kT);
 
     // core mapping: lane row r holds state pair pr of 16 consecutive channels
     const int r = tid >> 4;
@@ -157,10 +162,13 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         Ar[1] = av.y;
         a2[0] = av.x * kLog2e;
         a2[1] = av.y * kLog2e;
-        if (p.dh_final) {
-            const float2 g = *reinterpret_cast<const float2*>(p.dh_final + row * kDState + 2 * pr);
-            Gc[0] = g.x;
-            Gc[1] = g.y;
+        // the gradient reaching the chunk's last token from later ones
+        const float* g = p.g_carry ? p.g_carry + (row * p.nchunks + c) * kDState + 2 * pr
+                                   : (p.dh_final ? p.dh_final + row * kDState + 2 * pr : nullptr);
+        if (g) {
+            const float2 gv = *reinterpret_cast<const float2*>(g);
+            Gc[0] = gv.x;
+            Gc[1] = gv.y;
         }
     }
     const float bias = (validq && p.bias) ? p.bias[dq] : 0.0f;
@@ -194,9 +202,10 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     Raw2<IO> rx, rd, rz, rg, rq;
     float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
     float2 rck = make_float2(0.f, 0.f);
+    // ti: tile of the chunk; its checkpoint is the global tile t0 / 16
     auto load_tile = [&](int ti) {
-        const int64_t t0 = (int64_t)ti * kT;
-        const int nvalid = (L - t0 < kT) ? (int)(L - t0) : kT;
+        const int64_t t0 = t_beg + (int64_t)ti * kT;
+        const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
         if (validq) {
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             rg.load(gr + t0 + 2 * jq, vec, nq);
         }
         if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
-        if (valid) rck = *reinterpret_cast<const float2*>(ck + ti * kDState);
+        if (valid) rck = *reinterpret_cast<const float2*>(ck + (t0 / kT) * kDState);
     };
     rx.zero();
     rd.zero();
@@ -223,8 +232,8 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     float dDacc = 0.0f, dbacc = 0.0f;
     for (int it = 0; it < ntiles; ++it) {
         const int ti = ntiles - 1 - it;
-        const int64_t t0 = (int64_t)ti * kT;
-        const int nvalid = (L - t0 < kT) ? (int)(L - t0) : kT;
+        const int64_t t0 = t_beg + (int64_t)ti * kT;
+        const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
 
@@ -367,10 +376,12 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     }
 
     // ---- per-row results: dh0 = a_0 G_0 (the carry after token 0), dA partials
+    const int64_t prow = (b * p.nchunks + c) * p.dim;   // partials of (batch row, chunk)
     if (valid) {
-        if (p.dh0)
+        if (p.dh0 && c == 0)
             *reinterpret_cast<float2*>(p.dh0 + row * kDState + 2 * pr) = make_float2(Gc[0], Gc[1]);
-        *reinterpret_cast<float2*>(p.part_A + row * kDState + 2 * pr) = make_float2(dA[0], dA[1]);
+        *reinterpret_cast<float2*>(p.part_A + (prow + d) * kDState + 2 * pr) =
+            make_float2(dA[0], dA[1]);
     }
     // dD and dbias of channel cq: sum over its 8 token threads (lanes 8c..8c+7)
     dDacc += SSM_DPP(dDacc, 0x141);
@@ -380,8 +391,115 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     dbacc += SSM_DPP(dbacc, 0x4E);
     dbacc += SSM_DPP(dbacc, 0xB1);
     if (jq == 0 && validq) {
-        p.part_D[rowq] = dDacc;
-        p.part_bias[rowq] = dbacc;
+        p.part_D[prow + dq] = dDacc;
+        p.part_bias[prow + dq] = dbacc;
+    }
+}
+
+// Pass 1 of the chunked backward: for every chunk but the first, the gradient the chunk
+// passes to the token before it when nothing reaches it from later tokens,
+//   G_loc = sum over its tokens t of (prod_{r from its first token to t} a_r) dq_t C_t,
+// and its sum of Delta (the decay of a gradient crossing the whole chunk is
+// exp(A sum Delta)). The same mapping and tiles as the full kernel, only the G chain.
+template <typename IO, int CG>
+__global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams p) {
+    static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
+    constexpr int kRowsPerPair = CG / 16;
+    __shared__ float sD[CG * kRowF];
+    __shared__ float sQ[CG * kRowF];
+    __shared__ float sC[8 * kT * 2];            // [pair][token][C0 C1]
+
+    const int tid = threadIdx.x;
+    const int64_t ngroups = p.batch * p.groups_per_batch;
+    const int64_t gidx = blockIdx.x % ngroups;
+    const int c = (int)(blockIdx.x / ngroups) + p.chunk_offset;
+    const int64_t b = gidx / p.groups_per_batch;
+    const int64_t d0 = (int64_t)(gidx % p.groups_per_batch) * CG;
+    const int64_t L = p.seqlen;
+    const int64_t t_beg = (int64_t)c * p.chunk_len;
+    const int64_t t_end = (t_beg + p.chunk_len < L) ? t_beg + p.chunk_len : L;
+    const int ntiles = (int)((t_end - t_beg + kT - 1) / kT);
+
+    const int r = tid >> 4;
+    const int pr = r / kRowsPerPair;
+    const int cc = (r % kRowsPerPair) * 16 + (tid & 15);
+    const int64_t d = d0 + cc;
+    const bool valid = d < p.dim;
+    const int64_t row = b * p.dim + d;
+    const int cq = tid >> 3;
+    const int jq = tid & 7;
+    const int64_t dq = d0 + cq;
+    const bool validq = dq < p.dim;
+    const int64_t rowq = b * p.dim + dq;
+
+    float a2[2] = {0.f, 0.f};
+    if (valid) {
+        const float2 av = *reinterpret_cast<const float2*>(p.A + d * kDState + 2 * pr);
+        a2[0] = av.x * kLog2e;
+        a2[1] = av.y * kLog2e;
+    }
+    const float bias = (validq && p.bias) ? p.bias[dq] : 0.0f;
+    const IO* dr = static_cast<const IO*>(p.delta) + rowq * L;
+    const IO* zr = p.z ? static_cast<const IO*>(p.z) + rowq * L : nullptr;
+    const IO* gr = static_cast<const IO*>(p.dy) + rowq * L;
+    float G[2] = {0.f, 0.f}, dsum = 0.0f;
+    float* const myD = sD + cq * kRowF + 2 * jq;
+    float* const myQ = sQ + cq * kRowF + 2 * jq;
+    const float* const cD = sD + cc * kRowF;
+    const float* const cQ = sQ + cc * kRowF;
+    for (int it = 0; it < ntiles; ++it) {
+        const int ti = ntiles - 1 - it;
+        const int64_t t0 = t_beg + (int64_t)ti * kT;
+        const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
+        const int nq = nvalid - 2 * jq;
+        const bool vec = p.aligned && nvalid == kT;
+        Raw2<IO> rd, rz, rg;
+        rd.zero();
+        rz.zero();
+        rg.zero();
+        if (validq) {
+            rd.load(dr + t0 + 2 * jq, vec, nq);
+            if (zr) rz.load(zr + t0 + 2 * jq, vec, nq);
+            rg.load(gr + t0 + 2 * jq, vec, nq);
+        }
+        // C of the tile, per state pair: threads 0..127 move (pair, token)
+        if (tid < 128) {
+            const float4 q = *reinterpret_cast<const float4*>(
+                p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + t0 + (tid & 15)) * 4);
+            *reinterpret_cast<float2*>(sC + tid * 2) = make_float2(q.z, q.w);
+        }
+        float dv[2], zv[2], gv[2];
+        rd.widen(dv);
+        rz.widen(zv);
+        rg.widen(gv);
+        float dl[2], dqv[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float v = dv[k] + bias;
+            float delta = p.softplus ? softplus_f(v) : v;
+            dl[k] = k < nq ? delta : 0.0f;
+            dqv[k] = gv[k] * (zr ? silu_f(zv[k]) : 1.0f);
+        }
+        *reinterpret_cast<float2*>(myD) = make_float2(dl[0], dl[1]);
+        *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
+        __syncthreads();
+        const float* ct = sC + pr * kT * 2;
+#pragma unroll
+        for (int k = kT - 1; k >= 0; --k) {
+            const float ds = cD[k];
+            const float2 cv = *reinterpret_cast<const float2*>(ct + 2 * k);
+            const float qk = cQ[k];
+            // G_k = dq_k C_k + (what comes from later tokens); then carried to k - 1
+            G[0] = fast_exp2(ds * a2[0]) * __builtin_fmaf(qk, cv.x, G[0]);
+            G[1] = fast_exp2(ds * a2[1]) * __builtin_fmaf(qk, cv.y, G[1]);
+            dsum += ds;
+        }
+        __syncthreads();
+    }
+    if (valid) {
+        *reinterpret_cast<float2*>(p.g_carry + (row * p.nchunks + c) * kDState + 2 * pr) =
+            make_float2(G[0], G[1]);
+        if (pr == 0) p.g_sum[row * p.nchunks + c] = dsum;
     }
 }
 
@@ -420,6 +538,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     const float* __restrict__ part_A, const float* __restrict__ part_D,
     const float* __restrict__ part_bias, float* __restrict__ dA, float* __restrict__ dD,
     float* __restrict__ dbias, int64_t batch, int64_t dim) {
+    // batch = the number of partial rows (batch rows x chunks)
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < dim * kDState) {
         float s = 0.0f;
@@ -443,27 +562,43 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t stream,
                            hipEvent_t ev_begin, hipEvent_t ev_end) {
-    const dim3 grid((unsigned)(prm.batch * prm.groups_per_batch));
-    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipGetLastError();
-#define SSM_BWD(IO, N)                                                                     \
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, N>), grid, dim3(N * 8), 0, stream, prm)
-    if (bf16) {
-        switch (cg) {
-            case 32: SSM_BWD(uint16_t, 32); break;
-            case 48: SSM_BWD(uint16_t, 48); break;
-            case 64: SSM_BWD(uint16_t, 64); break;
-            default: return hipErrorInvalidValue;
-        }
-    } else {
-        switch (cg) {
-            case 32: SSM_BWD(float, 32); break;
-            case 48: SSM_BWD(float, 48); break;
-            case 64: SSM_BWD(float, 64); break;
-            default: return hipErrorInvalidValue;
-        }
+    const int64_t ngroups = prm.batch * prm.groups_per_batch;
+    hipError_t e;
+#define SSM_BWD(KERNEL, IO, N, GRID, P)                                                    \
+    hipLaunchKernelGGL((KERNEL<IO, N>), GRID, dim3(N * 8), 0, stream, P)
+#define SSM_BWD_ALL(KERNEL, GRID, P)                                                       \
+    switch (cg * 2 + (bf16 ? 1 : 0)) {                                                     \
+        case 65: SSM_BWD(KERNEL, uint16_t, 32, GRID, P); break;                            \
+        case 97: SSM_BWD(KERNEL, uint16_t, 48, GRID, P); break;                            \
+        case 129: SSM_BWD(KERNEL, uint16_t, 64, GRID, P); break;                           \
+        case 64: SSM_BWD(KERNEL, float, 32, GRID, P); break;                               \
+        case 96: SSM_BWD(KERNEL, float, 48, GRID, P); break;                               \
+        case 128: SSM_BWD(KERNEL, float, 64, GRID, P); break;                              \
+        default: return hipErrorInvalidValue;                                              \
     }
+    if (prm.nchunks > 1) {
+        // pass 1: every chunk but the first, from a zero gradient; then the carry from the
+        // last chunk backwards, starting from dh_final
+        BwdParams p1 = prm;
+        p1.chunk_offset = 1;
+        const dim3 g1((unsigned)(ngroups * (prm.nchunks - 1)));
+        SSM_BWD_ALL(scan_bwd_local_kernel, g1, p1)
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_carry(prm.A, prm.dh_final, prm.g_carry, prm.g_sum, nullptr,
+                         prm.batch * prm.dim, prm.dim, prm.nchunks, 1, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipGetLastError();
+    {
+        BwdParams p2 = prm;
+        p2.chunk_offset = 0;
+        const dim3 g2((unsigned)(ngroups * prm.nchunks));
+        SSM_BWD_ALL(scan_bwd_kernel, g2, p2)
+    }
+#undef SSM_BWD_ALL
 #undef SSM_BWD
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return hipGetLastError();
     {
@@ -476,7 +611,7 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
     }
     hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)cdiv(prm.dim * kDState, 256)),
                        dim3(256), 0, stream, prm.part_A, prm.part_D, prm.part_bias, prm.dA,
-                       prm.dD, prm.dbias, prm.batch, prm.dim);
+                       prm.dD, prm.dbias, prm.batch * prm.nchunks, prm.dim);
     return hipGetLastError();
 }
 

@@ -94,11 +94,14 @@ struct BwdParams {
     float* dbias;            // [dim] or null
     float* dh0;              // [batch*dim][16] or null
     float* part_bc;          // [batch][groups_per_batch][seqlen][32]: dB (16) then dC (16)
-    float* part_A;           // [batch*dim][16]
-    float* part_D;           // [batch*dim]
-    float* part_bias;        // [batch*dim]
-    int64_t batch, seqlen, dim, lpad, nckpt;
-    int32_t groups_per_batch, softplus, aligned;
+    float* part_A;           // [batch][nchunks][dim][16]
+    float* part_D;           // [batch][nchunks][dim]
+    float* part_bias;        // [batch][nchunks][dim]
+    float* g_carry;          // chunked: [batch*dim][nchunks][16], the gradient reaching the
+                             // end of each chunk from later tokens (pass 1: local values)
+    float* g_sum;            // chunked: [batch*dim][nchunks], the sum of Delta per chunk
+    int64_t batch, seqlen, dim, lpad, nckpt, chunk_len;
+    int32_t groups_per_batch, nchunks, chunk_offset, softplus, aligned;
 };
 
 // ev_begin / ev_end (may be null) are recorded around the launch of the scan kernel
@@ -108,6 +111,11 @@ hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* 
 hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream);
 // h_final[i] = h0 ? h0[i] : 0 for i < n (packed input with no tokens: every sequence is empty)
 hipError_t launch_copy_state(const float* h0, float* h_final, int64_t n, hipStream_t stream);
+// The chunk carry (see carry_kernel): in scan order, chunk_state[c] <- the value carried
+// into chunk c; value <- exp(A * sum_c) * value + local_c (just local_c where flag[c]).
+hipError_t launch_carry(const float* A, const float* init, float* chunk_state,
+                        const float* chunk_sum, const int32_t* chunk_flag, int64_t nrows,
+                        int64_t dim, int nchunks, int reverse, hipStream_t stream);
 // The backward kernel (ev_begin / ev_end around it) and its reductions.
 hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t stream,
                            hipEvent_t ev_begin, hipEvent_t ev_end);

@@ -644,6 +644,15 @@ hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* 
                 : launch_scan_t<float>(plan, prm, B, C, stream, ev_begin, ev_end);
 }
 
+hipError_t launch_carry(const float* A, const float* init, float* chunk_state,
+                        const float* chunk_sum, const int32_t* chunk_flag, int64_t nrows,
+                        int64_t dim, int nchunks, int reverse, hipStream_t stream) {
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)cdiv(nrows * kDState, 256)), dim3(256), 0,
+                       stream, A, init, chunk_state, chunk_sum, chunk_flag, nrows, dim, nchunks,
+                       reverse);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy_state(const float* h0, float* h_final, int64_t n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream, h0,

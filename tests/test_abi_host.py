@@ -192,6 +192,10 @@ def test_bwd_workspace_and_rejects(b):
     assert ws > b.ssm_scan_workspace_bytes(2, 100, 64, 16, 1)
     assert b.ssm_scan_bwd_workspace_bytes(2, 100, 64, 8, 1) == 0
     assert b.ssm_scan_bwd_workspace_bytes(2, 100, 64, 16, 1, bwd_group_channels=40) == 0
+    assert b.ssm_scan_bwd_workspace_bytes(2, 100, 64, 16, 1, bwd_chunk_len=48) == 0
+    # chunking adds the carried gradients, sums of Delta and per-chunk partials
+    assert (b.ssm_scan_bwd_workspace_bytes(2, 1000, 64, 16, 1, bwd_chunk_len=64)
+            > b.ssm_scan_bwd_workspace_bytes(2, 1000, 64, 16, 1, bwd_chunk_len=1024))
     p = dict(P, dy=P["z"] + (1 << 35), dx=P["y"], dd=P["y"] + (1 << 34), dz=P["hf"] + (1 << 34),
              dA=P["ws"] + (1 << 35), dB=P["ws"] + (1 << 34), dC=P["ws"] + (3 << 33),
              dD=P["D"] + (1 << 34), dbias=P["bias"] + (1 << 34), dh0=P["h0"] + (1 << 34))
@@ -209,7 +213,7 @@ def test_bwd_workspace_and_rejects(b):
     assert call(dB=p["dC"]) == 1               # outputs overlap each other
     assert call(dx=P["y"] + 8) == 2            # misaligned
     assert call(ws=None) == 3
-    opts = b.ScanOptions(0, 0, 0, None, None, 1, 0, 0)
+    opts = b.ScanOptions(0, 0, 0, None, None, 1, 0, 0, 0)
     q = dict(p)
     assert b.lib.ssm_scan_bwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"],
                               q["bias"], 1, q["h0"], q["dy"], None, q["dx"], q["dd"], q["dz"],

@@ -61,13 +61,14 @@ def _compare(g, ref, io, tol=None):
 
 
 def _run(inp, dy, io, use_z=True, use_D=True, use_bias=True, h0=None, dhf=None, plan=0,
-         chunk=0, bwd_cg=0):
+         chunk=0, bwd_cg=0, bwd_chunk=0):
     from selective_state_space_53_amd import binding
     g = binding.ssm_scan_bwd(
         inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
         D=inp["D"] if use_D else None, z=inp["z"] if use_z else None,
         delta_bias=inp["delta_bias"] if use_bias else None, h0=h0, dh_final=dhf,
-        want_dh0=True, plan=plan, chunk_len=chunk, bwd_group_channels=bwd_cg)
+        want_dh0=True, plan=plan, chunk_len=chunk, bwd_group_channels=bwd_cg,
+        bwd_chunk_len=bwd_chunk)
     torch.cuda.synchronize()
     ref = oracle.Oracle().scan_bwd(
         inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
@@ -110,6 +111,38 @@ def test_bwd_every_group_size(cg):
     _compare(g, ref, "f32")
 
 
+@pytest.mark.parametrize("shape", [(1, 1000, 200, "bf16"), (2, 333, 70, "f32"),
+                                   (1, 4103, 96, "bf16"), (1, 65, 33, "f32")],
+                         ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
+@pytest.mark.parametrize("bwd_chunk", [32, 64, 96])
+def test_bwd_chunked_all_outputs(shape, bwd_chunk):
+    """The chunked backward (gradient chains of the chunks from zero, a carry from the
+    last chunk backwards, then every chunk from its carried-in gradient), with ragged
+    last chunks and tiles, against the oracle."""
+    batch, L, dim, io = shape
+    cfg = synth.ScanConfig("bwdch", batch, L, dim, io=io, seed=350 + L)
+    inp = synth.scan_inputs(cfg, DEV)
+    dy = _dy((batch, dim, L), cfg.io_dtype, L + 1)
+    h0 = torch.randn((batch, dim, 16), generator=torch.Generator().manual_seed(3)).to(DEV)
+    dhf = torch.randn((batch, dim, 16), generator=torch.Generator().manual_seed(4)).to(DEV)
+    say("case bwd chunked", shape, bwd_chunk)
+    g, ref = _run(inp, dy, io, h0=h0, dhf=dhf, bwd_chunk=bwd_chunk)
+    _compare(g, ref, io)
+
+
+def test_bwd_long_sequence():
+    """One row of 65,536 tokens x 256 channels (bf16) in the library's own plan: the
+    backward is chunked (the sequence is what gives parallelism here); every output
+    against the full fp64 oracle."""
+    cfg = synth.ScanConfig("bwdlong", 1, 65536, 256, io="bf16", seed=44, dt_lo=1e-4,
+                           dt_hi=1e-2)
+    inp = synth.scan_inputs(cfg, DEV)
+    dy = _dy((1, 256, 65536), torch.bfloat16, 45)
+    say("case bwd long")
+    g, ref = _run(inp, dy, "bf16")
+    _compare(g, ref, "bf16")
+
+
 def test_bwd_full_size():
     """The Mamba-2.8B layer shape (batch 4, 2048 tokens, d_inner 5120, bf16), every
     output against the full fp64 oracle."""
@@ -144,11 +177,13 @@ def test_bwd_integer_exact():
     }
     dy = t(rng.integers(-1, 2, size=(batch, dim, L)))
     dhf = t(rng.integers(-2, 3, size=(batch, dim, 16)))
-    for plan, chunk, cg in [(1, 0, 48), (2, 64, 32), (2, 32, 64)]:
-        say("case bwd integer", plan, chunk, cg)
+    for plan, chunk, cg, bch in [(1, 0, 48, 0), (2, 64, 32, 0), (2, 32, 64, 0), (1, 0, 48, 32),
+                                 (2, 64, 32, 64)]:
+        say("case bwd integer", plan, chunk, cg, bch)
         g = binding.ssm_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
                                  D=inp["D"], delta_softplus=False, dh_final=dhf, want_dh0=True,
-                                 plan=plan, chunk_len=chunk, bwd_group_channels=cg)
+                                 plan=plan, chunk_len=chunk, bwd_group_channels=cg,
+                                 bwd_chunk_len=bch)
         torch.cuda.synchronize()
         ref = oracle.Oracle().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
                                        D=inp["D"], delta_softplus=False, dh_final=dhf)
