@@ -43,8 +43,10 @@ using namespace dev;
 
 constexpr int kT = 16;            // tokens per backward tile
 constexpr int kRowF = kT + 4;     // padded LDS row of the per-channel arrays (floats)
-constexpr int kRowP = kT;         // row of the per-pair partial arrays (unpadded: their
-                                  // size decides whether two workgroups fit in a CU)
+constexpr int kRowP = kT;         // row of the per-pair partial arrays: unpadded (their
+                                  // size decides whether two workgroups fit in a CU); the
+                                  // 4-token slots of channel c are XOR-swizzled by c & 3
+                                  // instead, so 16 lanes writing 16 rows hit 8 bank groups
 constexpr int kBcT = 8 * kT * 4;  // floats of widened B/C per tile
 
 // Two consecutive tokens of one row, raw, loaded one tile ahead of their use.
@@ -321,18 +323,20 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 Gc[0] = e0 * G0;
                 Gc[1] = e1 * G1;
             }
-            *reinterpret_cast<float4*>(p1 + g4) = make_float4(o1[0], o1[1], o1[2], o1[3]);
-            *reinterpret_cast<float4*>(p2 + g4) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+            const int slot = ((g4 >> 2) ^ (cc & 3)) << 2;
+            *reinterpret_cast<float4*>(p1 + slot) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+            *reinterpret_cast<float4*>(p2 + slot) = make_float4(o2[0], o2[1], o2[2], o2[3]);
         }
         __syncthreads();
 
         // ---- post: dx, ddelta for (cq, 2 tokens); the workgroup's dB, dC partial sums
         {
             float2 du = make_float2(0.f, 0.f), da = du;
+            const int off = (((jq >> 1) ^ (cq & 3)) << 2) + 2 * (jq & 1);   // swizzled slot
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const float2 a = *reinterpret_cast<const float2*>(sP1 + (q * CG + cq) * kRowP + 2 * jq);
-                const float2 c = *reinterpret_cast<const float2*>(sP2 + (q * CG + cq) * kRowP + 2 * jq);
+                const float2 a = *reinterpret_cast<const float2*>(sP1 + (q * CG + cq) * kRowP + off);
+                const float2 c = *reinterpret_cast<const float2*>(sP2 + (q * CG + cq) * kRowP + off);
                 du.x += a.x;
                 du.y += a.y;
                 da.x += c.x;
