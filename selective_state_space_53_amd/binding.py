@@ -76,6 +76,14 @@ lib.ssm_last_error.argtypes = []
 lib.ssm_abi_version.restype = ctypes.c_int
 lib.ssm_abi_version.argtypes = []
 
+# SSM_SCAN_ABI_VERSION this binding's argument lists and ScanOptions follow; a library
+# built from other sources (a stale .so) is refused rather than called with the wrong
+# layout.
+ABI_VERSION = 2
+if lib.ssm_abi_version() != ABI_VERSION:
+    raise ImportError(f"{_LIB_PATH} has ABI version {lib.ssm_abi_version()}, this binding "
+                      f"expects {ABI_VERSION}: rebuild the library")
+
 
 class SSMError(RuntimeError):
     def __init__(self, status: int):

@@ -45,6 +45,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     f32x2_t f = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // RNE
 }
+// Streaming (non-temporal) 16-byte load and store, for data touched exactly once per
+// launch: they keep the caches for data that is reused.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream4(float* p, float a, float b, float c, float d) {
+    const f32x4_t v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+
 __device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_one(uint16_t* p, float v) {
     *p = __builtin_bit_cast(uint16_t, (__bf16)v);

@@ -37,7 +37,9 @@ def test_exports_every_declared_symbol(b):
 
 
 def test_version_and_strings(b):
-    assert b.ssm_abi_version() == 2
+    hdr = open(os.path.join(ROOT, "include", "ssm_scan.h")).read()
+    declared = int(re.search(r"#define SSM_SCAN_ABI_VERSION (\d+)", hdr).group(1))
+    assert b.ssm_abi_version() == declared == b.ABI_VERSION
     assert b.ssm_status_string(0) == "ok"
     assert b.ssm_status_string(3) == "workspace too small"
     assert b.ssm_status_string(99) == "unknown status"
