@@ -105,6 +105,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"io tensors must be bfloat16 or float32, got {t.dtype}")
 
 
+def _io_code(io) -> int:
+    """io dtype argument of the workspace queries: SSM_F32 / SSM_BF16, or a torch dtype."""
+    if isinstance(io, torch.dtype):
+        if io == torch.bfloat16:
+            return SSM_BF16
+        if io == torch.float32:
+            return SSM_F32
+        raise TypeError(f"io dtype must be bfloat16 or float32, got {io}")
+    return int(io)
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -136,7 +147,7 @@ def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0,
 
 def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
                              group_channels=0) -> int:
-    return lib.ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype,
+    return lib.ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, _io_code(io_dtype),
                                         _options(plan, chunk_len, None, group_channels))
 
 
@@ -144,14 +155,14 @@ def ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, c
                                  group_channels=0, bwd_group_channels=0,
                                  bwd_chunk_len=0) -> int:
     return lib.ssm_scan_bwd_workspace_bytes(
-        batch, seqlen, dim, dstate, io_dtype,
+        batch, seqlen, dim, dstate, _io_code(io_dtype),
         _options(plan, chunk_len, None, group_channels, bwd_group_channels=bwd_group_channels,
                  bwd_chunk_len=bwd_chunk_len))
 
 
 def ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype, plan=0, chunk_len=0,
                                     group_channels=0) -> int:
-    return lib.ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype,
+    return lib.ssm_scan_varlen_workspace_bytes(total, dim, dstate, _io_code(io_dtype),
                                                _options(plan, chunk_len, None, group_channels))
 
 

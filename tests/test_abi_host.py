@@ -89,6 +89,10 @@ def test_scan_rejects_bad_options(b):
 def test_workspace_query(b):
     # single pass: B and C widened to fp32, per state quad, tokens padded to 32
     assert b.ssm_scan_workspace_bytes(4, 2048, 5120, 16, 1) == 4 * 2048 * 32 * 4
+    import torch
+    assert b.ssm_scan_workspace_bytes(4, 2048, 5120, 16, torch.bfloat16) == 4 * 2048 * 32 * 4
+    with pytest.raises(TypeError):
+        b.ssm_scan_workspace_bytes(4, 2048, 5120, 16, torch.float16)
     assert b.ssm_scan_workspace_bytes(1, 100, 16, 16, 0, plan=1) == 128 * 32 * 4
     # forced chunking adds one state (16 fp32) and one sum per (row, chunk)
     ws = b.ssm_scan_workspace_bytes(2, 1000, 70, 16, 1, plan=2, chunk_len=64)

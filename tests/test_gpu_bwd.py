@@ -154,6 +154,55 @@ def test_bwd_full_size():
     _compare(g, ref, cfg.io)
 
 
+def test_bwd_m130_full_size():
+    """The Mamba-130M layer shape (batch 8, 2048 tokens, d_inner 1536, bf16) in the
+    library's own plan, which chunks the backward here (as the benchmark runs it): every
+    output against the full fp64 oracle."""
+    cfg = synth.CONFIGS["m130"]
+    inp = synth.scan_inputs(cfg, DEV)
+    dy = _dy((cfg.batch, cfg.dim, cfg.seqlen), cfg.io_dtype, 13)
+    say("case bwd m130 full size")
+    g, ref = _run(inp, dy, cfg.io)
+    _compare(g, ref, cfg.io)
+
+
+def test_bwd_long_full_size_sampled_channels():
+    """The million-token row (1 x 1,048,576 x 1536, bf16) in the library's own plan. Every
+    gradient of a channel -- dx, ddelta, dz and dh0 of its row, and dA, dD, d_bias summed
+    over its batch rows -- depends on that channel's inputs alone, so the fp64 oracle run
+    on a few sampled channels gives them exactly; dB and dC (sums over all channels) are
+    checked at the 2.8B and 65,536-token sizes."""
+    from selective_state_space_53_amd import binding
+    cfg = synth.CONFIGS["long"]
+    inp = synth.scan_inputs(cfg, DEV)
+    dy = torch.randn((1, cfg.dim, cfg.seqlen), generator=torch.Generator(device=DEV).manual_seed(17),
+                     device=DEV).to(cfg.io_dtype)
+    say("case bwd long full size")
+    g = binding.ssm_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                             D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                             want_dh0=True)
+    torch.cuda.synchronize()
+    chans = [0, 517, 1024, cfg.dim - 1]
+    idx = torch.tensor(chans, device=DEV)
+    sub = lambda t: t.index_select(1, idx).cpu()
+    ref = oracle.Oracle().scan_bwd(
+        sub(inp["x"]), sub(inp["delta"]), inp["A"][idx].cpu(), inp["B"].cpu(),
+        inp["C"].cpu(), sub(dy), D=inp["D"][idx].cpu(), z=sub(inp["z"]),
+        delta_bias=inp["delta_bias"][idx].cpu(), nthreads=parity.threads())
+    got = {k: (g[k].index_select(1, idx) if k in ("dx", "ddelta", "dz", "dh0")
+               else g[k].index_select(0, idx)) for k in OUTS if k not in ("dB", "dC")}
+    errs = {}
+    for k, v in got.items():
+        r = np.asarray(ref[OKEY.get(k, k)])
+        gv = oracle.f64(v)
+        if k in ("dA", "dD", "ddelta_bias"):
+            gv, r = gv.reshape(1, -1), r.reshape(1, -1)
+        errs[k] = parity.rowwise_err(gv, r)
+    say("   " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= parity.TOL["bf16"]}
+    assert not bad, bad
+
+
 def test_bwd_integer_exact():
     """A = 0, Delta = 1 (softplus off), no gate, small integers everywhere: every
     intermediate is an exact integer in fp32, so the GPU gradients equal the oracle's
