@@ -72,7 +72,7 @@ int64_t scan_lds_bytes(int cg, bool local) {
 // ---- launch cost model -------------------------------------------------------------
 // SIMD cycles per wave per (token, state pair) of the recurrence, by waves resident on
 // the SIMD: one wave cannot hide the exp/FMA latencies, more than three add little
-// (measured on gfx950 with the same instruction mix: microbench/core_mix.hip).
+// (measured on gfx950 with a probe kernel running the same instruction mix).
 double wave_cost(int64_t waves_per_simd) {
     static const double kCost[] = {0.0, 55.5, 36.5, 31.0, 30.7};
     return waves_per_simd <= 4 ? kCost[waves_per_simd < 1 ? 1 : waves_per_simd] : 30.5;
