@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 2
+#define SSM_SCAN_ABI_VERSION 3
 
 typedef enum {
     SSM_OK = 0,
@@ -96,6 +96,24 @@ typedef struct {
                            a carry from the last chunk backwards, then every chunk from its
                            carried-in gradient); 0 = library choice, else a multiple of 32
                            (>= seqlen: one pass)                                          */
+    void* save_workspace; /* ssm_scan_fwd, training: NULL, or a device buffer into which
+                           the call also writes what ssm_scan_bwd needs -- the state
+                           before every 16th token and q, the output before the gate --
+                           in the layout that starts every backward workspace (see
+                           ssm_scan_bwd_workspace_bytes). Allocate the backward's
+                           workspace, pass it here, then to ssm_scan_bwd with saved = 1.
+                           Causal scans only (SSM_ERR_UNSUPPORTED with reverse,
+                           accumulate or packed sequences).                               */
+    size_t save_workspace_bytes; /* its size; the forward writes its first
+                           S = round_up(batch*dim*ceil(seqlen/16)*64, 256)
+                               + batch*dim*seqlen*sizeof(io) bytes and returns
+                           SSM_ERR_WORKSPACE_TOO_SMALL when it is smaller than S           */
+    int32_t saved;      /* ssm_scan_bwd: 1 = the workspace holds the checkpoints and q
+                           written by ssm_scan_fwd (save_workspace = this workspace) for
+                           the same x, delta, A, B, C, D, delta_bias, delta_softplus and
+                           h0, and the backward skips its own forward pass; nothing
+                           checks that they match (stale contents give wrong gradients).
+                           0 = the backward recomputes them.                              */
 } ssm_scan_options;
 
 /*
@@ -136,7 +154,9 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int6
  *   h_final    [batch][dim][dstate] fp32 out (the state after the last token) or
  *              NULL. It may be exactly h0 (in-place resume) but not partly overlap it.
  *   workspace  device buffer of at least ssm_scan_workspace_bytes(...) bytes
- *   opts       plan options or NULL
+ *   opts       plan options or NULL; with opts->save_workspace set (training) the call
+ *              also saves what ssm_scan_bwd needs there (the save buffer may overlap
+ *              no other buffer); opts->saved must be 0
  * batch, seqlen, dim >= 1; dstate must be 16.
  */
 ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B,
@@ -161,9 +181,15 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
  *   ddelta_t = (x_t (G_t . B_t) + sum_n G_t h_{t-1} a_t A) * softplus'(v_t)
  *   dA = sum_{b,t} G_t h_{t-1} a_t Delta_t   dD = sum dq_t x_t   ddelta_bias = sum ddelta
  *   dh0 = a_0 G_0
- * The states are recomputed from checkpoints the call writes into its workspace (a
- * forward pass that keeps the state before every 16th token), so the forward's
- * outputs are not needed.
+ * The states are recomputed from checkpoints: the state before every 16th token and
+ * q, kept at the start of the workspace. Either the call writes them itself (a forward
+ * pass in checkpoint mode; the forward's outputs are not needed), or, with
+ * opts->saved = 1, they were written there by the training forward (ssm_scan_fwd with
+ * opts->save_workspace = this workspace) and the backward starts from them.
+ * Workspace layout (ssm_scan_bwd_workspace_bytes), each part 256-byte aligned:
+ *   checkpoints  [batch*dim][ceil(seqlen/16)][16] fp32 (offset 0)
+ *   q            [batch][dim][seqlen] io_dtype
+ *   then the forward's workspace and the backward's partial sums (internal).
  *
  *   x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0: as for ssm_scan_fwd
  *   dy           [batch][dim][seqlen] io_dtype
@@ -178,7 +204,8 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
  *   dh0          [batch][dim][dstate] fp32 out or NULL
  *   workspace    ssm_scan_bwd_workspace_bytes(...) bytes
  *   opts         as for ssm_scan_fwd (the plan of the checkpoint pass); reverse and
- *                accumulate must be 0 (SSM_ERR_UNSUPPORTED otherwise)
+ *                accumulate must be 0 (SSM_ERR_UNSUPPORTED otherwise), save_workspace
+ *                NULL; saved as described above
  * Every output overlaps nothing. Sums over channels and batch rows are finished in a
  * fixed order, so results are deterministic. timing events, when given, bracket the
  * backward kernel itself.

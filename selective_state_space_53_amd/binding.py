@@ -32,7 +32,8 @@ class ScanOptions(ctypes.Structure):
                 ("group_channels", ctypes.c_int32), ("timing_begin", ctypes.c_void_p),
                 ("timing_end", ctypes.c_void_p), ("reverse", ctypes.c_int32),
                 ("accumulate", ctypes.c_int32), ("bwd_group_channels", ctypes.c_int32),
-                ("bwd_chunk_len", ctypes.c_int64)]
+                ("bwd_chunk_len", ctypes.c_int64), ("save_workspace", ctypes.c_void_p),
+                ("save_workspace_bytes", ctypes.c_size_t), ("saved", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -79,7 +80,7 @@ lib.ssm_abi_version.argtypes = []
 # SSM_SCAN_ABI_VERSION this binding's argument lists and ScanOptions follow; a library
 # built from other sources (a stale .so) is refused rather than called with the wrong
 # layout.
-ABI_VERSION = 2
+ABI_VERSION = 3
 if lib.ssm_abi_version() != ABI_VERSION:
     raise ImportError(f"{_LIB_PATH} has ABI version {lib.ssm_abi_version()}, this binding "
                       f"expects {ABI_VERSION}: rebuild the library")
@@ -135,14 +136,17 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 
 def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0,
-             reverse=False, accumulate=False, bwd_group_channels: int = 0, bwd_chunk_len: int = 0):
+             reverse=False, accumulate=False, bwd_group_channels: int = 0, bwd_chunk_len: int = 0,
+             save=None, saved=False):
     if (plan == 0 and chunk_len == 0 and events is None and group_channels == 0
             and not reverse and not accumulate and bwd_group_channels == 0
-            and bwd_chunk_len == 0):
+            and bwd_chunk_len == 0 and save is None and not saved):
         return None
     ev0, ev1 = (None, None) if events is None else events
     return ctypes.byref(ScanOptions(chunk_len, plan, group_channels, ev0, ev1, int(bool(reverse)),
-                                    int(bool(accumulate)), bwd_group_channels, bwd_chunk_len))
+                                    int(bool(accumulate)), bwd_group_channels, bwd_chunk_len,
+                                    _ptr(save), 0 if save is None else save.numel(),
+                                    int(bool(saved))))
 
 
 def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
@@ -169,12 +173,15 @@ def ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype, plan=0, chunk_
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                  h0=None, return_final_state=False, y=None, h_final=None, workspace=None,
                  plan=0, chunk_len=0, stream=None, timing_events=None, group_channels=0,
-                 reverse=False, accumulate=False):
+                 reverse=False, accumulate=False, save_for_backward=None):
     """x, delta, z: [batch][dim][seqlen]; B, C: [batch][seqlen][16]; A: [dim][16];
     D, delta_bias: [dim]; h0: [batch][dim][16]. Returns y (and h_final).
     reverse: anti-causal scan; accumulate: add into the given y instead of writing it.
     timing_events: optional (begin, end) pair of raw hipEvent_t handles (ints) that
-    the library records around the launch of the scan kernel that writes y."""
+    the library records around the launch of the scan kernel that writes y.
+    save_for_backward: a uint8 device tensor of ssm_scan_bwd_workspace_bytes(...) bytes
+    into which the call also saves the checkpoints and q; pass it to ssm_scan_bwd as its
+    workspace with saved=True."""
     _dev(x, "x")
     io = x.dtype
     batch, dim, seqlen = x.shape
@@ -197,7 +204,9 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     if return_final_state and h_final is None:
         h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _dev(h_final, "h_final", torch.float32, (batch, dim, N))
-    opts = _options(plan, chunk_len, timing_events, group_channels, reverse, accumulate)
+    _dev(save_for_backward, "save_for_backward", torch.uint8)
+    opts = _options(plan, chunk_len, timing_events, group_channels, reverse, accumulate,
+                    save=save_for_backward)
     ws_bytes = lib.ssm_scan_workspace_bytes(batch, seqlen, dim, N, code, opts)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -213,10 +222,12 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
 def ssm_scan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=True,
                  h0=None, dh_final=None, want_dh0=False, workspace=None, plan=0, chunk_len=0,
                  stream=None, timing_events=None, group_channels=0, bwd_group_channels=0,
-                 bwd_chunk_len=0):
+                 bwd_chunk_len=0, saved=False):
     """Gradients of the forward scan with the same arguments, given dy [batch][dim][L]
     (and dh_final [batch][dim][16]). Returns a dict: dx, ddelta, dz (x's dtype), dA,
-    dB, dC, dD, ddelta_bias, dh0 (fp32; None where the input is absent / not asked)."""
+    dB, dC, dD, ddelta_bias, dh0 (fp32; None where the input is absent / not asked).
+    saved=True: workspace is the save_for_backward tensor of the training forward on
+    the same inputs, and its checkpoint pass is skipped."""
     _dev(x, "x")
     io = x.dtype
     batch, dim, seqlen = x.shape
@@ -244,10 +255,14 @@ def ssm_scan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_s
     }
     code = _dtype_code(x)
     opts = _options(plan, chunk_len, timing_events, group_channels,
-                    bwd_group_channels=bwd_group_channels, bwd_chunk_len=bwd_chunk_len)
+                    bwd_group_channels=bwd_group_channels, bwd_chunk_len=bwd_chunk_len,
+                    saved=saved)
     ws_bytes = lib.ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, N, code, opts)
     if workspace is None:
+        if saved:
+            raise ValueError("saved=True needs the workspace the training forward saved into")
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
         _check(lib.ssm_scan_bwd(

@@ -242,6 +242,10 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     return SSM_OK;
 }
 
+constexpr int kBwdTile = 16;   // tokens per backward tile: a checkpoint every kBwdTile tokens
+bool saved_layout(int64_t batch, int64_t seqlen, int64_t dim, ssm_dtype io_dtype, size_t* ws_q,
+                  size_t* total);
+
 ssm_status scan_impl(const void* x, const void* delta, const float* A, const void* B,
                      const void* C, const float* D, const void* z, const float* delta_bias,
                      int delta_softplus, const int32_t* cu_seqlens, int64_t nseq,
@@ -317,6 +321,31 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
     if (h_final && overlaps(rws, rhf))
         return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps h_final");
 
+    // training: also save the checkpoints and q for the backward
+    void* const save = opts ? opts->save_workspace : nullptr;
+    if (opts && opts->saved)
+        return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.saved is an option of ssm_scan_bwd");
+    size_t save_q = 0, save_total = 0;
+    if (save) {
+        if (packed || opts->reverse || opts->accumulate)
+            return fail(SSM_ERR_UNSUPPORTED,
+                        "save_workspace: causal scans of ssm_scan_fwd without accumulate only");
+        if (!saved_layout(batch, seqlen, dim, io_dtype, &save_q, &save_total))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "save_workspace size overflows");
+        if (!aligned(save, 16))
+            return fail(SSM_ERR_UNSUPPORTED, "save_workspace=%p is not 16-byte aligned", save);
+        if (opts->save_workspace_bytes < save_total)
+            return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "save_workspace needs %zu bytes (got %zu)",
+                        save_total, opts->save_workspace_bytes);
+        const Region rsv = region("save_workspace", save, (int64_t)save_total);
+        for (const Region& r : inputs)
+            if (overlaps(rsv, r))
+                return fail(SSM_ERR_INVALID_ARGUMENT, "save_workspace overlaps %s", r.name);
+        if (overlaps(rsv, ry) || (h_final && overlaps(rsv, rhf)) || overlaps(rsv, rws))
+            return fail(SSM_ERR_INVALID_ARGUMENT,
+                        "save_workspace overlaps y, h_final or the workspace");
+    }
+
     ssm::ScanParams prm{};
     char* ws = static_cast<char*>(workspace);
     prm.x = x;
@@ -347,6 +376,11 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
     prm.aligned = ((seqlen * elem) % 16) == 0;
     prm.reverse = opts ? opts->reverse : 0;
     prm.accumulate = opts ? opts->accumulate : 0;
+    if (save) {
+        prm.ckpt = static_cast<float*>(save);
+        prm.nckpt = (seqlen + kBwdTile - 1) / kBwdTile;
+        prm.q = static_cast<char*>(save) + save_q;
+    }
     if (getenv("SSMSCAN_LOG"))
         fprintf(stderr,
                 "[ssmscan] scan b=%lld L=%lld d=%lld %s%s%s%s: %s, %d channels/group, %lld "
@@ -365,7 +399,6 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
 }
 
 // ---- backward ---------------------------------------------------------------------
-constexpr int kBwdTile = 16;
 
 // LDS bytes of one backward workgroup of cg channels (must match scan_bwd_kernel):
 // Delta, u, dq [cg][20]; two [8][cg][16] partial arrays; two B/C tiles; row sums
@@ -391,8 +424,25 @@ struct BwdPlan {
     ssm::ScanPlan fwd;      // the forward pass that writes q and the checkpoints
     int cg;
     int64_t nckpt, chunk_len, nchunks;
-    size_t ws_ckpt, ws_q, ws_bc, ws_A, ws_D, ws_bias, ws_gc, ws_gs, ws_total;
+    // workspace offsets: the checkpoints and q first (what a training forward saves;
+    // their place depends on the shape only), then the forward's own workspace
+    size_t ws_ckpt, ws_q, ws_fwd, ws_bc, ws_A, ws_D, ws_bias, ws_gc, ws_gs, ws_total;
 };
+
+// Where the checkpoints ([batch*dim][ceil(L/16)][16] fp32, offset 0) and q ([batch][dim][L]
+// io) start a backward workspace, and the bytes they take. False on overflow.
+bool saved_layout(int64_t batch, int64_t seqlen, int64_t dim, ssm_dtype io_dtype, size_t* ws_q,
+                  size_t* total) {
+    const int64_t nckpt = (seqlen + kBwdTile - 1) / kBwdTile;
+    const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
+    int64_t ck, qb;
+    if (!bytes4(batch * dim, nckpt, ssm::kDState, 4, &ck) ||
+        !bytes4(batch * dim, seqlen, elem, 1, &qb))
+        return false;
+    *ws_q = align_up((size_t)ck, 256);
+    *total = *ws_q + (size_t)qb;
+    return true;
+}
 
 // Channels per backward workgroup and chunking of the sequence (the cost model of
 // make_plan: pass 1 of the chunked backward -- only the gradient chain -- costs about a
@@ -437,6 +487,12 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
     if (opts && (opts->reverse || opts->accumulate))
         return fail(SSM_ERR_UNSUPPORTED,
                     "the backward scan supports the causal scan without accumulate only");
+    if (opts && opts->save_workspace)
+        return fail(SSM_ERR_INVALID_ARGUMENT,
+                    "ssm_scan_options.save_workspace is an option of ssm_scan_fwd");
+    if (opts && opts->saved != 0 && opts->saved != 1)
+        return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.saved=%d must be 0 or 1",
+                    opts->saved);
     ssm_status st = make_plan(batch, seqlen, dim, dstate, io_dtype, opts, &bp->fwd);
     if (st != SSM_OK) return st;
     const int req = opts ? opts->bwd_group_channels : 0;
@@ -462,9 +518,12 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
         return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
     if (batch * gpb * K >= (int64_t(1) << 31))
         return fail(SSM_ERR_INVALID_ARGUMENT, "too many backward chunks");
-    bp->ws_ckpt = align_up(bp->fwd.ws_total, 256);
-    bp->ws_q = align_up(bp->ws_ckpt + (size_t)ck, 256);
-    bp->ws_bc = align_up(bp->ws_q + (size_t)qb, 256);
+    size_t saved_total = 0;
+    if (!saved_layout(batch, seqlen, dim, io_dtype, &bp->ws_q, &saved_total))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
+    bp->ws_ckpt = 0;
+    bp->ws_fwd = align_up(saved_total, 256);
+    bp->ws_bc = align_up(bp->ws_fwd + bp->fwd.ws_total, 256);
     bp->ws_A = align_up(bp->ws_bc + (size_t)bc, 256);
     bp->ws_D = align_up(bp->ws_A + (size_t)pa, 256);
     bp->ws_bias = align_up(bp->ws_D + (size_t)pd, 256);
@@ -554,10 +613,13 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
                                 regs[j].name);
 
         char* ws = static_cast<char*>(workspace);
+        char* fws = ws + bp.ws_fwd;   // the forward's own workspace
         hipStream_t strm = static_cast<hipStream_t>(stream);
+        const bool saved = opts && opts->saved;
         // 1. B/C widening and the forward in checkpoint mode, with the forward's own
         //    plan: it writes q (the output before the gate: no z) and the state before
-        //    every 16th token
+        //    every 16th token -- or, when the training forward saved those, the widening
+        //    alone
         ssm::ScanParams fp{};
         fp.x = x;
         fp.delta = delta;
@@ -568,12 +630,13 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         fp.bias = delta_bias;
         fp.h0 = h0;
         fp.h_final = nullptr;
-        fp.bcq = reinterpret_cast<float*>(ws + bp.fwd.ws_bcq);
+        fp.bcq = reinterpret_cast<float*>(fws + bp.fwd.ws_bcq);
         fp.chunk_state =
-            bp.fwd.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.fwd.ws_state) : nullptr;
-        fp.chunk_sum = bp.fwd.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.fwd.ws_sum) : nullptr;
+            bp.fwd.nchunks > 1 ? reinterpret_cast<float*>(fws + bp.fwd.ws_state) : nullptr;
+        fp.chunk_sum =
+            bp.fwd.nchunks > 1 ? reinterpret_cast<float*>(fws + bp.fwd.ws_sum) : nullptr;
         fp.chunk_flag =
-            bp.fwd.nchunks > 1 ? reinterpret_cast<int32_t*>(ws + bp.fwd.ws_flag) : nullptr;
+            bp.fwd.nchunks > 1 ? reinterpret_cast<int32_t*>(fws + bp.fwd.ws_flag) : nullptr;
         fp.cu = nullptr;
         fp.ckpt = reinterpret_cast<float*>(ws + bp.ws_ckpt);
         fp.nckpt = bp.nckpt;
@@ -588,8 +651,10 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         fp.ngroups = (int32_t)(batch * fp.groups_per_batch);
         fp.softplus = delta_softplus;
         fp.aligned = ((seqlen * elem) % 16) == 0;
-        hipError_t e = ssm::launch_scan(bp.fwd, fp, B, C, io_dtype == SSM_BF16, strm, nullptr,
-                                        nullptr);
+        hipError_t e = saved ? ssm::launch_bc_widen(B, C, fp.bcq, batch, seqlen, fp.lpad,
+                                                    io_dtype == SSM_BF16, strm)
+                             : ssm::launch_scan(bp.fwd, fp, B, C, io_dtype == SSM_BF16, strm,
+                                                nullptr, nullptr);
         if (e != hipSuccess)
             return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
         // 2. the backward kernel and its reductions
@@ -633,11 +698,12 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         prm.aligned = fp.aligned;
         if (getenv("SSMSCAN_LOG"))
             fprintf(stderr,
-                    "[ssmscan] bwd b=%lld L=%lld d=%lld %s: checkpoint pass %d channels/group "
+                    "[ssmscan] bwd b=%lld L=%lld d=%lld %s: checkpoint pass %s%d channels/group "
                     "x %d chunks, backward %d channels/group x %lld chunks of %lld\n",
                     (long long)batch, (long long)seqlen, (long long)dim,
-                    io_dtype == SSM_BF16 ? "bf16" : "f32", bp.fwd.group_channels,
-                    bp.fwd.nchunks, bp.cg, (long long)bp.nchunks, (long long)bp.chunk_len);
+                    io_dtype == SSM_BF16 ? "bf16" : "f32", saved ? "(saved by the forward) " : "",
+                    bp.fwd.group_channels, bp.fwd.nchunks, bp.cg, (long long)bp.nchunks,
+                    (long long)bp.chunk_len);
         hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->timing_begin) : nullptr;
         hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->timing_end) : nullptr;
         e = ssm::launch_scan_bwd(bp.cg, prm, io_dtype == SSM_BF16, strm, ev0, ev1);

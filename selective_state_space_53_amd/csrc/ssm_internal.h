@@ -38,7 +38,9 @@ struct ScanParams {
     int32_t* chunk_flag; // [nchunks]: 1 = a sequence begins inside the chunk (packed input)
     const int32_t* cu;   // packed sequences: [nseq+1] token offsets, or null (batch rows)
     float* ckpt;         // checkpoint pass: [batch*dim][nckpt][16], the state before every
-                         // 16th token (then y is not written); null otherwise
+                         // 16th token; null otherwise
+    void* q;             // checkpoint pass: [batch][dim][L] io, the output before the gate
+                         // (y still gets the gated output), or null
     int64_t nckpt;
     int64_t batch, seqlen, dim, lpad, chunk_len;
     int32_t nchunks, ngroups, groups_per_batch, chunk_offset;
@@ -108,6 +110,10 @@ struct BwdParams {
 // that writes y.
 hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* B, const void* C,
                        bool bf16, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+// B and C widened to fp32 into bcq ([batch][8][lpad][4], the scan's layout) on its own:
+// the backward runs it when the training forward saved the checkpoints.
+hipError_t launch_bc_widen(const void* B, const void* C, float* bcq, int64_t batch,
+                           int64_t seqlen, int64_t lpad, bool bf16, hipStream_t stream);
 hipError_t launch_state_update(const DecodeParams& prm, bool bf16, hipStream_t stream);
 // h_final[i] = h0 ? h0[i] : 0 for i < n (packed input with no tokens: every sequence is empty)
 hipError_t launch_copy_state(const float* h0, float* h_final, int64_t n, hipStream_t stream);

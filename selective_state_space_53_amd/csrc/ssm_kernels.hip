@@ -175,8 +175,9 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int64_t t) {
 // state and its sum of Delta. Otherwise: outputs y (and final states).
 // REV = anti-causal: tiles, and tokens inside a tile, are taken from the last to the
 // first; the tiles stay where they are in memory, so loads and stores are the same.
-// CKPT = the forward of the backward pass: as the last pass, and it also stores the
-// state before every 16th token (the backward recomputes its tiles from them).
+// CKPT = a forward that keeps what the backward needs: as the last pass, and it also
+// stores the state before every 16th token (the backward recomputes its tiles from
+// them) and, when p.q is set, the output before the gate.
 // PACKED = packed sequences (p.cu set): the state is reset to the sequence's initial state
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
@@ -435,7 +436,13 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                 yv[0] += a.x; yv[1] += a.y; yv[2] += a.z; yv[3] += a.w;
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) yv[k] = (yv[k] + post_a[k]) * post_g[k];
+            for (int k = 0; k < 4; ++k) yv[k] += post_a[k];
+            // training forward: q, the output before the gate, for the backward
+            if (CKPT && p.q && validq && nq > 0)
+                Store4<IO>::store(static_cast<IO*>(p.q) + rowq * p.seqlen + t0 + 4 * jq, vec, nq,
+                                  yv);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) yv[k] *= post_g[k];
             if (validq && nq > 0) {
                 if (p.accumulate) {
                     Raw4<IO> old;
@@ -592,14 +599,21 @@ hipError_t launch_scan_dir(int cg, dim3 grid, hipStream_t stream, const ScanPara
 }
 
 template <typename IO>
+hipError_t launch_bc_widen_t(const void* B, const void* C, float* bcq, int64_t batch,
+                             int64_t seqlen, int64_t lpad, hipStream_t stream) {
+    const int64_t n = batch * lpad * 8;
+    hipLaunchKernelGGL(bc_widen_kernel<IO>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
+                       static_cast<const IO*>(B), static_cast<const IO*>(C), bcq, batch, seqlen,
+                       lpad);
+    return hipGetLastError();
+}
+
+template <typename IO>
 hipError_t launch_scan_t(const ScanPlan& plan, ScanParams prm, const void* B, const void* C,
                          hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     {
-        const int64_t n = prm.batch * prm.lpad * 8;
-        hipLaunchKernelGGL(bc_widen_kernel<IO>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
-                           stream, static_cast<const IO*>(B), static_cast<const IO*>(C),
-                           prm.bcq, prm.batch, prm.seqlen, prm.lpad);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_bc_widen_t<IO>(B, C, prm.bcq, prm.batch, prm.seqlen, prm.lpad,
+                                             stream);
         if (e != hipSuccess) return e;
     }
     const int cg = plan.group_channels;
@@ -643,6 +657,12 @@ hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* 
                        bool bf16, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
     return bf16 ? launch_scan_t<uint16_t>(plan, prm, B, C, stream, ev_begin, ev_end)
                 : launch_scan_t<float>(plan, prm, B, C, stream, ev_begin, ev_end);
+}
+
+hipError_t launch_bc_widen(const void* B, const void* C, float* bcq, int64_t batch,
+                           int64_t seqlen, int64_t lpad, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_bc_widen_t<uint16_t>(B, C, bcq, batch, seqlen, lpad, stream)
+                : launch_bc_widen_t<float>(B, C, bcq, batch, seqlen, lpad, stream);
 }
 
 hipError_t launch_carry(const float* A, const float* init, float* chunk_state,

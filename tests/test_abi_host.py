@@ -225,3 +225,49 @@ def test_bwd_workspace_and_rejects(b):
                               q["bias"], 1, q["h0"], q["dy"], None, q["dx"], q["dd"], q["dz"],
                               q["dA"], q["dB"], q["dC"], q["dD"], q["dbias"], q["dh0"], 2, 100,
                               64, 16, 1, q["ws"], 1 << 40, ctypes.byref(opts), None) == 2
+
+
+def _save_opts(b, save, nbytes, saved=0, reverse=0, accumulate=0):
+    return ctypes.byref(b.ScanOptions(0, 0, 0, None, None, reverse, accumulate, 0, 0, save,
+                                      nbytes, saved))
+
+
+def test_training_forward_save_rejects(b):
+    """ssm_scan_fwd with save_workspace (checkpoints and q for the backward): the size
+    formula in the header, and every check before anything is launched."""
+    batch, L, dim = 2, 64, 64
+    need = (batch * dim * ((L + 15) // 16) * 64 + 255) // 256 * 256 + batch * dim * L * 2
+    sv = 0x7d0000000000
+    # one byte fewer than the header's formula is refused (every call here fails a check
+    # before any launch: the addresses are not real)
+    assert scan(b, opts=_save_opts(b, sv, need - 1)) == 3
+    assert scan(b, opts=_save_opts(b, sv, need, reverse=1)) == 2
+    assert scan(b, opts=_save_opts(b, sv, need, accumulate=1)) == 2
+    assert scan(b, opts=_save_opts(b, sv + 8, need)) == 2             # misaligned
+    assert scan(b, opts=_save_opts(b, P["x"], need)) == 1             # overlaps an input
+    assert scan(b, opts=_save_opts(b, P["y"] - 64, need)) == 1        # overlaps y
+    assert scan(b, opts=_save_opts(b, P["ws"], need)) == 1            # overlaps the workspace
+    assert scan(b, opts=_save_opts(b, None, 0, saved=1)) == 1         # a backward option
+    # packed sequences cannot save
+    p = dict(P, cu=0x7e0000000000)
+    assert b.lib.ssm_scan_varlen_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                     p["z"], p["bias"], 1, p["cu"], 3, p["h0"], p["y"],
+                                     p["hf"], 100, 64, 16, 1, p["ws"], 1 << 40,
+                                     _save_opts(b, sv, 1 << 30), None) == 2
+    # the backward workspace starts with that region
+    assert b.ssm_scan_bwd_workspace_bytes(batch, L, dim, 16, 1) > need
+
+
+def test_backward_saved_option_rejects(b):
+    p = dict(P, dy=P["z"] + (1 << 35), dx=P["y"], dd=P["y"] + (1 << 34), dz=P["hf"] + (1 << 34),
+             dA=P["ws"] + (1 << 35), dB=P["ws"] + (1 << 34), dC=P["ws"] + (3 << 33),
+             dD=P["D"] + (1 << 34), dbias=P["bias"] + (1 << 34), dh0=P["h0"] + (1 << 34))
+
+    def call(opts):
+        q = p
+        return b.lib.ssm_scan_bwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"],
+                                  q["bias"], 1, q["h0"], q["dy"], None, q["dx"], q["dd"], q["dz"],
+                                  q["dA"], q["dB"], q["dC"], q["dD"], q["dbias"], q["dh0"], 2,
+                                  100, 64, 16, 1, q["ws"], 1 << 40, opts, None)
+    assert call(_save_opts(b, 0x7d0000000000, 1 << 30)) == 1   # save_workspace: forward only
+    assert call(_save_opts(b, None, 0, saved=2)) == 1

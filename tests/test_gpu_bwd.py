@@ -203,6 +203,45 @@ def test_bwd_long_full_size_sampled_channels():
     assert not bad, bad
 
 
+@pytest.mark.parametrize("shape", [(2, 1000, 200, "bf16"), (1, 333, 70, "f32"),
+                                   (1, 4103, 96, "bf16"), (3, 17, 33, "f32")],
+                         ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
+@pytest.mark.parametrize("plan,chunk", [(0, 0), (2, 64)], ids=["auto", "c64"])
+def test_training_forward_saves_for_backward(shape, plan, chunk):
+    """Training pair: the forward with save_for_backward writes the same y and h_final as
+    the plain forward, and the backward that starts from what it saved (saved=True, no
+    checkpoint pass of its own) gives the same gradients, bit for bit, as the backward
+    that recomputes them."""
+    from selective_state_space_53_amd import binding
+    batch, L, dim, io = shape
+    cfg = synth.ScanConfig("train", batch, L, dim, io=io, seed=500 + L)
+    inp = synth.scan_inputs(cfg, DEV)
+    dy = _dy((batch, dim, L), cfg.io_dtype, L + 7)
+    h0 = torch.randn((batch, dim, 16), generator=torch.Generator().manual_seed(5)).to(DEV)
+    dhf = torch.randn((batch, dim, 16), generator=torch.Generator().manual_seed(6)).to(DEV)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
+    kw = dict(D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], h0=h0)
+    say("case training pair", shape, plan, chunk)
+    ws = torch.empty(binding.ssm_scan_bwd_workspace_bytes(batch, L, dim, 16, cfg.io_dtype,
+                                                          plan=plan, chunk_len=chunk),
+                     dtype=torch.uint8, device=DEV)
+    ys, hs = binding.ssm_scan_fwd(*args, **kw, return_final_state=True, plan=plan,
+                                  chunk_len=chunk, save_for_backward=ws)
+    yp, hp = binding.ssm_scan_fwd(*args, **kw, return_final_state=True, plan=plan,
+                                  chunk_len=chunk)
+    gs = binding.ssm_scan_bwd(*args, dy, **kw, dh_final=dhf, want_dh0=True, plan=plan,
+                              chunk_len=chunk, workspace=ws, saved=True)
+    gr = binding.ssm_scan_bwd(*args, dy, **kw, dh_final=dhf, want_dh0=True, plan=plan,
+                              chunk_len=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, yp) and torch.equal(hs, hp)
+    for k in OUTS:
+        assert torch.equal(gs[k], gr[k]), k
+    # and the saved path against the oracle
+    ref = oracle.Oracle().scan_bwd(*args, dy, **kw, dh_final=dhf, nthreads=parity.threads())
+    _compare(gs, ref, io)
+
+
 def test_bwd_integer_exact():
     """A = 0, Delta = 1 (softplus off), no gate, small integers everywhere: every
     intermediate is an exact integer in fp32, so the GPU gradients equal the oracle's
