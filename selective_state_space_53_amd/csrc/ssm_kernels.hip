@@ -369,18 +369,26 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         if (quiet) {
             if (CKPT && valid)
                 *reinterpret_cast<float2*>(ck + (t0 / 16) * kDState) = make_float2(h[0], h[1]);
+            // the LDS operands of 4 tokens, read one group ahead of their use
+            float4 nD, nU, n0, n1, n2, n3;
+            auto fetch = [&](int tq) {
+                nD = *reinterpret_cast<const float4*>(coreD + tq);
+                nU = *reinterpret_cast<const float4*>(coreU + tq);
+                n0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
+                n1 = *reinterpret_cast<const float4*>(bct + (tq + 1) * 4);
+                n2 = *reinterpret_cast<const float4*>(bct + (tq + 2) * 4);
+                n3 = *reinterpret_cast<const float4*>(bct + (tq + 3) * 4);
+            };
+            fetch(REV ? kTile - 4 : 0);
 #pragma unroll
             for (int gq = 0; gq < kTile; gq += 4) {
                 const int tq = REV ? kTile - 4 - gq : gq;
                 if (CKPT && gq == 16 && valid && t0 + 16 < p.seqlen)
                     *reinterpret_cast<float2*>(ck + (t0 / 16 + 1) * kDState) =
                         make_float2(h[0], h[1]);
-                const float4 D4 = *reinterpret_cast<const float4*>(coreD + tq);
-                const float4 U4 = *reinterpret_cast<const float4*>(coreU + tq);
-                const float4 q0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
-                const float4 q1 = *reinterpret_cast<const float4*>(bct + (tq + 1) * 4);
-                const float4 q2 = *reinterpret_cast<const float4*>(bct + (tq + 2) * 4);
-                const float4 q3 = *reinterpret_cast<const float4*>(bct + (tq + 3) * 4);
+                const float4 D4 = nD, U4 = nU, q0 = n0, q1 = n1, q2 = n2, q3 = n3;
+                if (gq + 4 < kTile) fetch(REV ? kTile - 8 - gq : gq + 4);
+                __builtin_amdgcn_sched_barrier(0);
                 float pp[4];
                 if (!REV) {
                     SSM_TOKEN(pp[0], D4.x, U4.x, q0)
