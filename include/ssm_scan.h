@@ -203,6 +203,10 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
  *   ddelta_bias  [dim] fp32 out or NULL (needs delta_bias)
  *   dh0          [batch][dim][dstate] fp32 out or NULL
  *   workspace    ssm_scan_bwd_workspace_bytes(...) bytes
+ *   seqlen       below 2^32 / (32 * sizeof(io)) tokens (33,554,432 for fp32, 67,108,864
+ *                for bf16; SSM_ERR_UNSUPPORTED beyond): the backward addresses the rows of
+ *                one workgroup with 32-bit offsets, and picks its channels per workgroup
+ *                so that they span less than 4 GiB
  *   opts         as for ssm_scan_fwd (the plan of the checkpoint pass); reverse and
  *                accumulate must be 0 (SSM_ERR_UNSUPPORTED otherwise), save_workspace
  *                NULL; saved as described above

@@ -447,16 +447,24 @@ bool saved_layout(int64_t batch, int64_t seqlen, int64_t dim, ssm_dtype io_dtype
 // Channels per backward workgroup and chunking of the sequence (the cost model of
 // make_plan: pass 1 of the chunked backward -- only the gradient chain -- costs about a
 // quarter of a full pass).
-void choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int req_cg, int64_t req_chunk,
-                     BwdPlan* bp) {
+// The backward kernel addresses a workgroup's cg rows of [batch][dim][L] with 32-bit
+// byte offsets: cg * L * elem must stay below 2^32.
+bool bwd_rows_fit(int cg, int64_t seqlen, int64_t elem) {
+    return (int64_t)cg * seqlen * elem < (int64_t(1) << 32);
+}
+
+// Returns false when no allowed channel group fits (the sequence is too long).
+bool choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t elem, int req_cg,
+                     int64_t req_chunk, BwdPlan* bp) {
     static const int kCands[] = {64, 48, 32};
     const int64_t tile = 16;
     double best_c = 1e300;
-    bp->cg = 32;
+    bp->cg = 0;
     bp->chunk_len = seqlen;
     bp->nchunks = 1;
     for (int cg : kCands) {
         if (req_cg && cg != req_cg) continue;
+        if (!bwd_rows_fit(cg, seqlen, elem)) continue;
         const int64_t groups = batch * ((dim + cg - 1) / cg);
         for (int64_t kk = 1; kk <= 4096; kk = kk < 4 ? kk + 1 : kk + kk / 2) {
             int64_t cl = seqlen;
@@ -480,6 +488,7 @@ void choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int req_cg, int
             if (req_chunk > 0) break;
         }
     }
+    return bp->cg != 0;
 }
 
 ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
@@ -504,12 +513,17 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
         return fail(SSM_ERR_INVALID_ARGUMENT,
                     "ssm_scan_options.bwd_chunk_len=%lld must be a multiple of 32",
                     (long long)req_chunk);
-    choose_bwd_plan(batch, seqlen, dim, req, req_chunk, bp);
+    const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
+    if (!choose_bwd_plan(batch, seqlen, dim, elem, req, req_chunk, bp))
+        return fail(SSM_ERR_UNSUPPORTED,
+                    "ssm_scan_bwd: seqlen=%lld is too long for one row (a workgroup's rows must "
+                    "span less than 4 GiB: seqlen < %lld for this dtype%s)",
+                    (long long)seqlen, (long long)(((int64_t)1 << 32) / ((req ? req : 32) * elem)),
+                    req ? " and bwd_group_channels" : "");
     const int64_t gpb = (dim + bp->cg - 1) / bp->cg;
     const int64_t K = bp->nchunks;
     bp->nckpt = (seqlen + kBwdTile - 1) / kBwdTile;
     int64_t ck, qb, bc, pa, pd, gc = 0, gs = 0;
-    const int64_t elem = io_dtype == SSM_BF16 ? 2 : 4;
     if (!bytes4(batch * dim, bp->nckpt, ssm::kDState, 4, &ck) ||
         !bytes4(batch * dim, seqlen, elem, 1, &qb) || !bytes4(batch * gpb, seqlen, 32, 4, &bc) ||
         !bytes4(batch * K, dim, ssm::kDState, 4, &pa) || !bytes4(batch * K, dim, 1, 4, &pd) ||

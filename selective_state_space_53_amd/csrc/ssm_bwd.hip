@@ -99,7 +99,9 @@ __device__ __forceinline__ void store2(IO* p, bool vec, int n, float a, float b)
                                                           (ctrl), 0xF, 0xF, false))
 
 // Sum four values over the 16 lanes of a row (a reduce-scatter): afterwards lanes 0-3
-// hold the sum of v0, lanes 4-7 of v1, lanes 8-11 of v2, lanes 12-15 of v3. Each step
+// hold the sum of v0, lanes 4-7 of v1, lanes 8-11 of v2, lanes 12-15 of v3 (the four
+// lanes of a quad the same bits: the last two steps add the same pairs in swapped
+// order, and IEEE addition commutes). Each step
 // pairs lanes across a half (mirror of the row, then of each half) and moves the
 // values the lane does not keep; two quad swaps finish. 6 selects + 5 DPP adds.
 __device__ __forceinline__ float row_sum4(float v0, float v1, float v2, float v3, int lane16) {
@@ -175,14 +177,24 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     }
     const float bias = (validq && p.bias) ? p.bias[dq] : 0.0f;
     const float Dd = (validq && p.D) ? p.D[dq] : 0.0f;
-    const IO* xr = static_cast<const IO*>(p.x) + rowq * L;
-    const IO* dr = static_cast<const IO*>(p.delta) + rowq * L;
-    const IO* zr = p.z ? static_cast<const IO*>(p.z) + rowq * L : nullptr;
-    const IO* gr = static_cast<const IO*>(p.dy) + rowq * L;
-    const IO* qr = static_cast<const IO*>(p.q) + rowq * L;
-    IO* dxr = static_cast<IO*>(p.dx) + rowq * L;
-    IO* ddr = static_cast<IO*>(p.ddelta) + rowq * L;
-    IO* dzr = p.z ? static_cast<IO*>(p.dz) + rowq * L : nullptr;
+    // The eight [batch][dim][L] streams: a base per workgroup (uniform, in SGPRs) and one
+    // 32-bit byte offset per lane shared by all eight (the workgroup's CG rows span
+    // CG * L * sizeof(IO) < 2^32 bytes; the planner guarantees it). Per-lane 64-bit row
+    // pointers would take 16 more VGPRs.
+    const int64_t wbase = (b * p.dim + d0) * L;
+    const char* xw = reinterpret_cast<const char*>(static_cast<const IO*>(p.x) + wbase);
+    const char* dw = reinterpret_cast<const char*>(static_cast<const IO*>(p.delta) + wbase);
+    const char* zw =
+        p.z ? reinterpret_cast<const char*>(static_cast<const IO*>(p.z) + wbase) : nullptr;
+    const char* gw = reinterpret_cast<const char*>(static_cast<const IO*>(p.dy) + wbase);
+    const char* qw = reinterpret_cast<const char*>(static_cast<const IO*>(p.q) + wbase);
+    char* dxw = reinterpret_cast<char*>(static_cast<IO*>(p.dx) + wbase);
+    char* ddw = reinterpret_cast<char*>(static_cast<IO*>(p.ddelta) + wbase);
+    char* dzw = p.z ? reinterpret_cast<char*>(static_cast<IO*>(p.dz) + wbase) : nullptr;
+    const bool zr = p.z != nullptr;
+    const uint32_t lrow = (uint32_t)((int64_t)cq * L * (int64_t)sizeof(IO));
+    // byte offset of this thread's 2 tokens starting at token t
+    auto at = [&](int64_t t) { return lrow + (uint32_t)((t + 2 * jq) * (int64_t)sizeof(IO)); };
     const float* ck = p.ckpt + row * p.nckpt * kDState + 2 * pr;
     float* const pbc = p.part_bc + ((b * p.groups_per_batch + grp) * L) * 32;
     // B/C staging: threads 0..127 move one 16-byte (pair, token) entry per tile
@@ -198,7 +210,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     const float* const cQ = sQ + cc * kRowF;
     float* const p1 = sP1 + (pr * CG + cc) * kRowP;
     float* const p2 = sP2 + (pr * CG + cc) * kRowP;
-    // lanes 0, 4, 8, 12 of a row hold its sums of dB0, dB1, dC0, dC1
+    // lanes 4j..4j+3 of a row hold its sum of value j (dB0, dB1, dC0, dC1)
     float* const red = sRed + r * 4 + (lane16 >> 2);
 
     Raw2<IO> rx, rd, rz, rg, rq;
@@ -211,13 +223,13 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
         if (validq) {
-            rx.load(xr + t0 + 2 * jq, vec, nq);
-            rd.load(dr + t0 + 2 * jq, vec, nq);
+            rx.load(reinterpret_cast<const IO*>(xw + at(t0)), vec, nq);
+            rd.load(reinterpret_cast<const IO*>(dw + at(t0)), vec, nq);
             if (zr) {
-                rz.load(zr + t0 + 2 * jq, vec, nq);
-                rq.load(qr + t0 + 2 * jq, vec, nq);
+                rz.load(reinterpret_cast<const IO*>(zw + at(t0)), vec, nq);
+                rq.load(reinterpret_cast<const IO*>(qw + at(t0)), vec, nq);
             }
-            rg.load(gr + t0 + 2 * jq, vec, nq);
+            rg.load(reinterpret_cast<const IO*>(gw + at(t0)), vec, nq);
         }
         if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
         if (valid) rck = *reinterpret_cast<const float2*>(ck + (t0 / kT) * kDState);
@@ -264,7 +276,8 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         *reinterpret_cast<float2*>(myD) = make_float2(dl[0], dl[1]);
         *reinterpret_cast<float2*>(myU) = make_float2(uu[0], uu[1]);
         *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
-        if (zr && validq && nq > 0) store2(dzr + t0 + 2 * jq, vec, nq, dzv[0], dzv[1]);
+        if (zr && validq && nq > 0)
+            store2(reinterpret_cast<IO*>(dzw + at(t0)), vec, nq, dzv[0], dzv[1]);
         __syncthreads();
 
         // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint
@@ -319,13 +332,18 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 // dB += G u, dC += dq h (this token's state), summed over the row
                 const float sr = row_sum4(G0 * Us[j], G1 * Us[j], Qs[j] * hs[k][0],
                                           Qs[j] * hs[k][1], lane16);
-                if ((lane16 & 3) == 0) red[k * kLaneRows * 4] = sr;
+                // the 4 lanes of a quad hold the same bits, so all of them write: no
+                // branch, and the adjoint stays one scheduling region per 4 tokens
+                red[k * kLaneRows * 4] = sr;
                 Gc[0] = e0 * G0;
                 Gc[1] = e1 * G1;
             }
             const int slot = ((g4 >> 2) ^ (cc & 3)) << 2;
             *reinterpret_cast<float4*>(p1 + slot) = make_float4(o1[0], o1[1], o1[2], o1[3]);
             *reinterpret_cast<float4*>(p2 + slot) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+            // keep the scheduler's hoisting inside the group: across groups it raises the
+            // register count past 3 waves per SIMD
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
 
@@ -355,8 +373,8 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 }
             }
             if (validq && nq > 0) {
-                store2(dxr + t0 + 2 * jq, vec, nq, dxo[0], dxo[1]);
-                store2(ddr + t0 + 2 * jq, vec, nq, ddo[0], ddo[1]);
+                store2(reinterpret_cast<IO*>(dxw + at(t0)), vec, nq, dxo[0], dxo[1]);
+                store2(reinterpret_cast<IO*>(ddw + at(t0)), vec, nq, ddo[0], ddo[1]);
             }
         }
         // 16 tokens x 32 values (dB then dC): value i < 512 (i = tid, tid + CG*8) is the

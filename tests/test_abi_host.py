@@ -271,3 +271,15 @@ def test_backward_saved_option_rejects(b):
                                   100, 64, 16, 1, q["ws"], 1 << 40, opts, None)
     assert call(_save_opts(b, 0x7d0000000000, 1 << 30)) == 1   # save_workspace: forward only
     assert call(_save_opts(b, None, 0, saved=2)) == 1
+
+
+def test_backward_sequence_length_limit(b):
+    """The backward addresses one workgroup's rows with 32-bit offsets: the planner picks
+    channels per workgroup (64, 48, 32) whose rows span less than 4 GiB, and refuses a
+    row too long even for 32 channels."""
+    f32, bf16 = 0, 1
+    assert b.ssm_scan_bwd_workspace_bytes(1, (1 << 32) // 128 - 1, 16, 16, f32) > 0
+    assert b.ssm_scan_bwd_workspace_bytes(1, (1 << 32) // 128, 16, 16, f32) == 0
+    assert b.ssm_scan_bwd_workspace_bytes(1, 1 << 25, 16, 16, bf16) > 0          # 48 or 32
+    assert b.ssm_scan_bwd_workspace_bytes(1, 1 << 25, 16, 16, bf16, bwd_group_channels=64) == 0
+    assert b.ssm_scan_bwd_workspace_bytes(1, 1 << 26, 16, 16, bf16) == 0

@@ -242,6 +242,44 @@ def test_training_forward_saves_for_backward(shape, plan, chunk):
     _compare(gs, ref, io)
 
 
+def test_bwd_row_offsets_near_4gib():
+    """64 channels of one bf16 row of 33,554,400 tokens in one 64-channel workgroup: the
+    last channel's 32-bit byte offsets reach 98.7% of 2^32. The first and last channels'
+    own gradients (dx, ddelta, dz, dh0, dA, dD, d_bias) against the fp64 oracle on those
+    channels alone."""
+    from selective_state_space_53_amd import binding
+    L, dim = 33_554_400, 64
+    cfg = synth.ScanConfig("near4g", 1, L, dim, io="bf16", seed=71, dt_lo=1e-4, dt_hi=1e-2)
+    inp = synth.scan_inputs(cfg, DEV)
+    dy = torch.randn((1, dim, L), generator=torch.Generator(device=DEV).manual_seed(19),
+                     device=DEV).to(torch.bfloat16)
+    say("case bwd offsets near 4 GiB")
+    g = binding.ssm_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                             D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                             want_dh0=True, bwd_group_channels=64)
+    torch.cuda.synchronize()
+    idx = torch.tensor([0, dim - 1], device=DEV)
+    sub = lambda t: t.index_select(1, idx).cpu()
+    ref = oracle.Oracle().scan_bwd(
+        sub(inp["x"]), sub(inp["delta"]), inp["A"][idx].cpu(), inp["B"].cpu(),
+        inp["C"].cpu(), sub(dy), D=inp["D"][idx].cpu(), z=sub(inp["z"]),
+        delta_bias=inp["delta_bias"][idx].cpu(), nthreads=2)
+    errs = {}
+    for k in OUTS:
+        if k in ("dB", "dC"):
+            continue
+        v = (g[k].index_select(1, idx) if k in ("dx", "ddelta", "dz", "dh0")
+             else g[k].index_select(0, idx))
+        r = np.asarray(ref[OKEY.get(k, k)])
+        gv = oracle.f64(v)
+        if k in ("dA", "dD", "ddelta_bias"):
+            gv, r = gv.reshape(1, -1), r.reshape(1, -1)
+        errs[k] = parity.rowwise_err(gv, r)
+    say("   " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= parity.TOL["bf16"]}
+    assert not bad, bad
+
+
 def test_bwd_integer_exact():
     """A = 0, Delta = 1 (softplus off), no gate, small integers everywhere: every
     intermediate is an exact integer in fp32, so the GPU gradients equal the oracle's
