@@ -469,13 +469,15 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     float* const myQ = sQ + cq * kRowF + 2 * jq;
     const float* const cD = sD + cc * kRowF;
     const float* const cQ = sQ + cc * kRowF;
-    for (int it = 0; it < ntiles; ++it) {
-        const int ti = ntiles - 1 - it;
+    // a tile's raw inputs, loaded one tile ahead of their use: Delta, z, dy per (channel,
+    // 2 tokens) and, for threads 0..127, C of one (state pair, token)
+    Raw2<IO> rd, rz, rg;
+    float4 rc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
-        Raw2<IO> rd, rz, rg;
         rd.zero();
         rz.zero();
         rg.zero();
@@ -484,16 +486,24 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
             if (zr) rz.load(zr + t0 + 2 * jq, vec, nq);
             rg.load(gr + t0 + 2 * jq, vec, nq);
         }
-        // C of the tile, per state pair: threads 0..127 move (pair, token)
-        if (tid < 128) {
-            const float4 q = *reinterpret_cast<const float4*>(
+        if (tid < 128)
+            rc = *reinterpret_cast<const float4*>(
                 p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + t0 + (tid & 15)) * 4);
-            *reinterpret_cast<float2*>(sC + tid * 2) = make_float2(q.z, q.w);
-        }
+    };
+    load_tile(ntiles - 1);
+    for (int it = 0; it < ntiles; ++it) {
+        const int ti = ntiles - 1 - it;
+        const int64_t t0 = t_beg + (int64_t)ti * kT;
+        const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
+        const int nq = nvalid - 2 * jq;
         float dv[2], zv[2], gv[2];
         rd.widen(dv);
         rz.widen(zv);
         rg.widen(gv);
+        const float4 cv4 = rc;
+        if (it + 1 < ntiles) load_tile(ti - 1);
+        // C of the tile, per state pair: threads 0..127 move (pair, token)
+        if (tid < 128) *reinterpret_cast<float2*>(sC + tid * 2) = make_float2(cv4.z, cv4.w);
         float dl[2], dqv[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
