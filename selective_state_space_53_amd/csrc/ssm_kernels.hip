@@ -277,8 +277,27 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             save_final(s, true);
         }
     };
+    // The tiles this workgroup scans: tbase .. tbase + nt - 1 of the chunk. Pass 1 of packed
+    // input needs only the chunk's end state (in scan order), which depends on no token
+    // before the last sequence start inside the chunk: the tiles before it are skipped
+    // (the reset there replaces whatever state the skipped tokens would have left).
+    int tbase = 0, nt = ntiles;
+    if (packed && LOCAL) {
+        if (!REV) {
+            const int64_t st = p.cu[seq_of(p.cu, p.nseq, t_end - 1)];
+            if (st > t_beg) {
+                tbase = (int)((st - t_beg) / kTile);
+                nt = ntiles - tbase;
+            }
+        } else {
+            const int64_t en = p.cu[seq_of(p.cu, p.nseq, t_beg) + 1];
+            if (en < t_end) nt = (int)((en - 1 - t_beg) / kTile) + 1;
+        }
+    }
     if (packed) {
-        s = seq_of(p.cu, p.nseq, REV ? t_end - 1 : t_beg);
+        const int64_t scan_end = t_beg + (int64_t)(tbase + nt) * kTile;
+        s = seq_of(p.cu, p.nseq,
+                   REV ? (scan_end < t_end ? scan_end : t_end) - 1 : t_beg + (int64_t)tbase * kTile);
         lo = p.cu[s];
         hi = p.cu[s + 1];
         // the workgroup that scans the first token also saves the empty sequences
@@ -296,7 +315,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
 
     Raw4<IO> rx, rdl, rz;
     float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto tile_of = [&](int it) { return REV ? ntiles - 1 - it : it; };
+    auto tile_of = [&](int it) { return REV ? tbase + nt - 1 - it : tbase + it; };
     auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kTile;
         const int nvalid = (t_end - t0 < kTile) ? (int)(t_end - t0) : kTile;
@@ -315,7 +334,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     load_tile(tile_of(0));
     if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
 
-    for (int it = 0; it < ntiles; ++it) {
+    for (int it = 0; it < nt; ++it) {
         const int ti = tile_of(it);
         const int64_t t0 = t_beg + (int64_t)ti * kTile;
         const int nvalid = (t_end - t0 < kTile) ? (int)(t_end - t0) : kTile;
@@ -326,7 +345,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         rx.widen(xv);
         rdl.widen(dv);
         if (kOut) rz.widen(zv);
-        if (it + 1 < ntiles) load_tile(tile_of(it + 1));
+        if (it + 1 < nt) load_tile(tile_of(it + 1));
         float dl[4], uu[4], post_a[4], post_g[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -465,7 +484,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         }
         // the next tile's B/C into the other LDS buffer (its last readers finished
         // before the barrier above; its next readers come after the next barrier)
-        if (bc_mover && it + 1 < ntiles)
+        if (bc_mover && it + 1 < nt)
             *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile) = rbc;
     }
 
