@@ -206,8 +206,9 @@ def test_bwd_long_full_size_sampled_channels():
 @pytest.mark.parametrize("shape", [(2, 1000, 200, "bf16"), (1, 333, 70, "f32"),
                                    (1, 4103, 96, "bf16"), (3, 17, 33, "f32")],
                          ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
-@pytest.mark.parametrize("plan,chunk", [(0, 0), (2, 64)], ids=["auto", "c64"])
-def test_training_forward_saves_for_backward(shape, plan, chunk):
+@pytest.mark.parametrize("plan,chunk,bwd_chunk", [(0, 0, 0), (2, 64, 0), (0, 0, 96)],
+                         ids=["auto", "c64", "bwd_c96"])
+def test_training_forward_saves_for_backward(shape, plan, chunk, bwd_chunk):
     """Training pair: the forward with save_for_backward writes the same y and h_final as
     the plain forward, and the backward that starts from what it saved (saved=True, no
     checkpoint pass of its own) gives the same gradients, bit for bit, as the backward
@@ -221,18 +222,19 @@ def test_training_forward_saves_for_backward(shape, plan, chunk):
     dhf = torch.randn((batch, dim, 16), generator=torch.Generator().manual_seed(6)).to(DEV)
     args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
     kw = dict(D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], h0=h0)
-    say("case training pair", shape, plan, chunk)
+    say("case training pair", shape, plan, chunk, bwd_chunk)
     ws = torch.empty(binding.ssm_scan_bwd_workspace_bytes(batch, L, dim, 16, cfg.io_dtype,
-                                                          plan=plan, chunk_len=chunk),
+                                                          plan=plan, chunk_len=chunk,
+                                                          bwd_chunk_len=bwd_chunk),
                      dtype=torch.uint8, device=DEV)
     ys, hs = binding.ssm_scan_fwd(*args, **kw, return_final_state=True, plan=plan,
                                   chunk_len=chunk, save_for_backward=ws)
     yp, hp = binding.ssm_scan_fwd(*args, **kw, return_final_state=True, plan=plan,
                                   chunk_len=chunk)
     gs = binding.ssm_scan_bwd(*args, dy, **kw, dh_final=dhf, want_dh0=True, plan=plan,
-                              chunk_len=chunk, workspace=ws, saved=True)
+                              chunk_len=chunk, workspace=ws, saved=True, bwd_chunk_len=bwd_chunk)
     gr = binding.ssm_scan_bwd(*args, dy, **kw, dh_final=dhf, want_dh0=True, plan=plan,
-                              chunk_len=chunk)
+                              chunk_len=chunk, bwd_chunk_len=bwd_chunk)
     torch.cuda.synchronize()
     assert torch.equal(ys, yp) and torch.equal(hs, hp)
     for k in OUTS:
