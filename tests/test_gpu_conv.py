@@ -78,6 +78,21 @@ def test_conv_full_size_all_rows():
     assert np.array_equal(oracle.f64(so), sr)
 
 
+def test_conv_full_size_fp32_all_rows():
+    """The 2.8B layer shape with fp32 io (two 16-byte accesses per 8 values)."""
+    from selective_state_space_53_amd import binding
+    cfg = synth.CONFIGS["m2p8"]
+    say("case conv full size fp32")
+    x, w, b, st = _inputs(cfg.batch, cfg.seqlen, cfg.dim, "f32", cfg.seed + 1)
+    y, so = binding.ssm_causal_conv1d_fwd(x, w, b, conv_state=st, return_state=True)
+    torch.cuda.synchronize()
+    yr, sr = oracle.Oracle.conv1d(x, w, b, state=st)
+    e = parity.rowwise_err(y, yr)
+    say(f"  full size fp32 y err {e:.3e}")
+    assert e <= parity.TOL["f32"]
+    assert np.array_equal(oracle.f64(so), sr)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_conv_decode_continues_prefill(io):
     """Prefill L tokens (returning the conv state), then T decode steps: the same as

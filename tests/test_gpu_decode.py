@@ -84,6 +84,17 @@ def test_decode_full_shape_64_steps_sampled():
         assert v <= parity.TOL["bf16"], k
 
 
+def test_decode_full_shape_fp32_io_sampled():
+    """The decode batch (256 x 5120) with fp32 io for 16 steps, sampled rows, fp32 bar."""
+    cfg = synth.DecodeConfig("decode_f32", batch=256, dim=5120, steps=16, io="f32", seed=23)
+    say("case decode full fp32", cfg)
+    ey, es = _run_steps(cfg, 2048)
+    say(f"decode fp32: y err {ey:.3e}; state err {es}")
+    assert ey <= 1e-5
+    for k, v in es.items():
+        assert v <= 1e-5, k
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("opts", [dict(), dict(use_z=False, use_D=False),
                                   dict(bias=False, softplus=False)],

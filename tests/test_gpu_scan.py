@@ -67,6 +67,24 @@ def test_full_size_sampled_rows(name, nrows, var):
     assert torch.isfinite(y.float()).all()
 
 
+@pytest.mark.parametrize("name,nrows", [("m2p8", 64), ("m130", 64)])
+def test_full_size_fp32_io_sampled_rows(name, nrows):
+    """The 2.8B and 130M layer shapes with fp32 io (16-byte float4 loads and stores instead
+    of the bf16 path's 8-byte ones), sampled rows against the oracle at the fp32 bar."""
+    cfg = synth.shrink(synth.CONFIGS[name], io="f32", final_state=True)
+    say("case fp32 io", name)
+    inp = synth.scan_inputs(cfg, DEV)
+    y, hf = parity.gpu_scan(inp)
+    torch.cuda.synchronize()
+    rb, rd = parity.sample_rows(cfg.batch, cfg.dim, nrows, seed=cfg.seed + 5)
+    yr, hr = parity.oracle_rows(inp, rb, rd)
+    sel = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
+    ey = parity.rowwise_err(y[sel], yr)
+    eh = parity.rowwise_err(hf[sel], hr)
+    say(f"{name} fp32: y err {ey:.3e}  h_final err {eh:.3e}")
+    assert ey <= parity.TOL["f32"] and eh <= parity.TOL["f32"]
+
+
 RAGGED = [
     # (batch, seqlen, dim, io)
     (2, 1000, 200, "bf16"),   # several tiles, ragged tail, 4 channel groups (last ragged)
