@@ -11,6 +11,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -45,19 +46,19 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     extra = []
     if save_temps:
         extra = ["--save-temps"]
-    k_objs = []
+    k_objs = [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in KERNEL_SOURCES]
+    cmds = [["hipcc", "-c", *DEVICE_FLAGS, *inc, *extra, os.path.join(CSRC, src), "-o", obj]
+            for src, obj in zip(KERNEL_SOURCES, k_objs)]
+    cmds.append(["hipcc", "-c", *HOST_FLAGS, *inc, os.path.join(CSRC, "ssm_abi.cpp"), "-o", a_obj])
     cwd = os.getcwd()
     try:
         os.chdir(BUILD_DIR)  # --save-temps writes next to the working directory
-        for src in KERNEL_SOURCES:
-            obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-            _run(["hipcc", "-c", *DEVICE_FLAGS, *inc, *extra, os.path.join(CSRC, src), "-o", obj],
-                 verbose)
-            k_objs.append(obj)
+        # the translation units are independent: compile them side by side
+        with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
     finally:
         os.chdir(cwd)
-    _run(["hipcc", "-c", *HOST_FLAGS, *inc, os.path.join(CSRC, "ssm_abi.cpp"), "-o", a_obj],
-         verbose)
     tmp = LIB + ".tmp"
     _run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *k_objs, a_obj, "-o", tmp],
          verbose)
