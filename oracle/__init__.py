@@ -198,6 +198,51 @@ class Oracle:
                           delta_softplus=delta_softplus, h0=h0, nthreads=nthreads)
         return np.ascontiguousarray(y[:, :, ::-1]), hf
 
+    def scan_varlen_bwd(self, x, delta, A, B, C, dy, cu_seqlens, D=None, z=None,
+                        delta_bias=None, delta_softplus=True, h0=None, dh_final=None,
+                        nthreads=1):
+        """Gradients through scan_varlen (causal): every sequence is its own scan, so its
+        gradients are scan_bwd of that sequence alone (with its h0 and dh_final); the
+        per-token gradients (dx, ddelta, dz [dim][total], dB, dC [total][N]) are placed
+        at its tokens, the per-channel ones (dA, dD, dbias) summed over sequences, and
+        dh0 [nseq][dim][N] is per sequence (an empty sequence passes dh_final through:
+        its final state is its initial state)."""
+        x = f64(x)
+        dim, total = x.shape
+        N = f64(A).shape[1]
+        cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+        nseq = len(cu) - 1
+        assert cu[0] == 0 and cu[-1] == total and all(a <= b for a, b in zip(cu, cu[1:]))
+        dl, Bf, Cf, dyf = f64(delta), f64(B), f64(C), f64(dy)
+        zf = None if z is None else f64(z)
+        h0f = None if h0 is None else f64(h0)
+        dhf = None if dh_final is None else f64(dh_final)
+        out = {"dx": np.zeros((dim, total)), "ddelta": np.zeros((dim, total)),
+               "dz": np.zeros((dim, total)) if z is not None else None,
+               "dA": np.zeros((dim, N)), "dB": np.zeros((total, N)), "dC": np.zeros((total, N)),
+               "dD": np.zeros(dim) if D is not None else None, "dbias": np.zeros(dim),
+               "dh0": np.zeros((nseq, dim, N))}
+        for i in range(nseq):
+            a, b = cu[i], cu[i + 1]
+            if b == a:
+                out["dh0"][i] = 0.0 if dhf is None else dhf[i]
+                continue
+            g = self.scan_bwd(x[None, :, a:b], dl[None, :, a:b], A, Bf[None, a:b, :], Cf[None, a:b, :],
+                              dyf[None, :, a:b], D=D, z=None if zf is None else zf[None, :, a:b],
+                              delta_bias=delta_bias, delta_softplus=delta_softplus,
+                              h0=None if h0f is None else h0f[i][None],
+                              dh_final=None if dhf is None else dhf[i][None], nthreads=nthreads)
+            for k in ("dx", "ddelta") + (("dz",) if z is not None else ()):
+                out[k][:, a:b] = g[k][0]
+            out["dB"][a:b] = g["dB"][0]
+            out["dC"][a:b] = g["dC"][0]
+            out["dA"] += g["dA"]
+            out["dbias"] += g["dbias"]
+            if D is not None:
+                out["dD"] += g["dD"]
+            out["dh0"][i] = g["dh0"][0]
+        return out
+
     def scan_varlen(self, x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bias=None,
                     delta_softplus=True, h0=None, reverse=False, nthreads=1):
         """Packed sequences: x, delta, z are [dim][total], B, C [total][N]; sequence i is

@@ -674,6 +674,66 @@ def pin_bwd_cumsum_closed_form(orc):
     assert _rel(g["dD"], np.einsum("bdl,bdl->d", dy, x)) < 1e-12
 
 
+def pin_varlen_bwd_autograd(orc):
+    """Packed gradients against torch.autograd of the packed forward written again in
+    torch ops (each sequence through the torch forward from its own h0; an empty
+    sequence's final state is its h0), loss sum(dy y) + sum(dh_final h_final); ragged
+    lengths with empty and one-token sequences."""
+    import torch
+    lens = [6, 0, 1, 11, 0, 4]
+    p, cu, h0 = _packed_problem(61, lens, dim=3, N=4)
+    rng = np.random.default_rng(62)
+    dim, total = p["x"].shape
+    dy = rng.standard_normal((dim, total))
+    dhf = rng.standard_normal((len(lens), dim, 4))
+    names = ["x", "delta", "A", "B", "C", "D", "z", "delta_bias"]
+    tt = {k: torch.tensor(p[k], requires_grad=True) for k in names}
+    th0 = torch.tensor(h0, requires_grad=True)
+    ys, hfs = [], []
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if a == b:
+            hfs.append(th0[i])
+            continue
+        y, hf = _torch_forward(tt["x"][None, :, a:b], tt["delta"][None, :, a:b], tt["A"],
+                               tt["B"][None, a:b], tt["C"][None, a:b], tt["D"],
+                               tt["z"][None, :, a:b], tt["delta_bias"], True, th0[i][None])
+        ys.append(y[0])
+        hfs.append(hf[0])
+    loss = (torch.cat(ys, dim=1) * torch.tensor(dy)).sum() + \
+        (torch.stack(hfs) * torch.tensor(dhf)).sum()
+    loss.backward()
+    g = orc.scan_varlen_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dy, cu, D=p["D"],
+                            z=p["z"], delta_bias=p["delta_bias"], h0=h0, dh_final=dhf)
+    for gk, tk in [("dx", "x"), ("ddelta", "delta"), ("dA", "A"), ("dB", "B"), ("dC", "C"),
+                   ("dD", "D"), ("dz", "z"), ("dbias", "delta_bias")]:
+        assert _rel(g[gk], tt[tk].grad.numpy()) < 1e-11, gk
+    assert _rel(g["dh0"], th0.grad.numpy()) < 1e-11
+
+
+def pin_varlen_bwd_equals_batched(orc):
+    """Equal lengths: the packed gradients are the batch gradients, relayouted."""
+    batch, L = 3, 13
+    p, cu, h0 = _packed_problem(63, [L] * batch, dim=2, N=3)
+    dim = p["x"].shape[0]
+    rng = np.random.default_rng(64)
+    dy = rng.standard_normal((dim, batch * L))
+    dhf = rng.standard_normal((batch, dim, 3))
+    tob = lambda v: v.reshape(dim, batch, L).transpose(1, 0, 2)
+    gb = orc.scan_bwd(tob(p["x"]), tob(p["delta"]), p["A"], p["B"].reshape(batch, L, -1),
+                      p["C"].reshape(batch, L, -1), tob(dy), D=p["D"], z=tob(p["z"]),
+                      delta_bias=p["delta_bias"], h0=h0, dh_final=dhf)
+    g = orc.scan_varlen_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dy, cu, D=p["D"],
+                            z=p["z"], delta_bias=p["delta_bias"], h0=h0, dh_final=dhf)
+    for k in ("dx", "ddelta", "dz"):
+        assert np.array_equal(g[k], gb[k].transpose(1, 0, 2).reshape(dim, batch * L)), k
+    for k in ("dB", "dC"):
+        assert np.array_equal(g[k], gb[k].reshape(batch * L, -1)), k
+    assert np.array_equal(g["dh0"], gb["dh0"])
+    for k in ("dA", "dD", "dbias"):   # sums over batch rows in another order
+        assert _rel(g[k], gb[k]) < 1e-13, k
+
+
 ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response,
             pin_free_decay, pin_brute_force, pin_chunked_equals_unchunked,
             pin_decode_equals_scan, pin_linearity_and_causality, pin_elementwise,
@@ -681,4 +741,4 @@ ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response
             pin_varlen_equals_batched, pin_varlen_isolation, pin_conv_library,
             pin_conv_np_convolve, pin_conv_impulse, pin_conv_state_continuation,
             pin_conv_decode_equals_prefill, pin_bwd_autograd, pin_bwd_finite_differences,
-            pin_bwd_cumsum_closed_form]
+            pin_bwd_cumsum_closed_form, pin_varlen_bwd_autograd, pin_varlen_bwd_equals_batched]

@@ -123,6 +123,13 @@ PY_MUTANTS = [
      "start = hf[i - 1][None] if i > 0 else None"),
     ("varlen_empty_final_zero", "hf[i] = 0.0 if start is None else start[0]", "hf[i] = 0.0"),
     ("varlen_C_from_row_start", "Cf[None, a:b]", "Cf[None, 0:b - a]"),
+    ("varlen_bwd_dh_final_of_next_seq", "dh_final=None if dhf is None else dhf[i][None]",
+     "dh_final=None if dhf is None else dhf[min(i + 1, nseq - 1)][None]"),
+    ("varlen_bwd_empty_dh0_zero", 'out["dh0"][i] = 0.0 if dhf is None else dhf[i]',
+     'out["dh0"][i] = 0.0'),
+    ("varlen_bwd_dA_not_summed", 'out["dA"] += g["dA"]', 'out["dA"] = g["dA"]'),
+    ("varlen_bwd_dB_at_row_start", 'out["dB"][a:b] = g["dB"][0]', 'out["dB"][0:b - a] = g["dB"][0]'),
+    ("varlen_bwd_B_from_row_start", "Bf[None, a:b, :]", "Bf[None, 0:b - a, :]"),
     ("varlen_reverse_ignored", "fn = self.scan_reverse if reverse else self.scan",
      "fn = self.scan"),
     ("conv_taps_reversed", "acc += w[None, :, k, None] * xp[:, :, k:k + L]",
