@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 3
+#define SSM_SCAN_ABI_VERSION 4
 
 typedef enum {
     SSM_OK = 0,
@@ -258,6 +258,45 @@ ssm_status ssm_scan_varlen_fwd(const void* x, const void* delta, const float* A,
                                const float* delta_bias, int delta_softplus,
                                const int32_t* cu_seqlens, int64_t nseq, const float* h0,
                                void* y, float* h_final, int64_t total, int64_t dim,
+                               int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                               size_t workspace_bytes, const ssm_scan_options* opts,
+                               void* stream);
+
+/*
+ * The backward of ssm_scan_varlen_fwd (causal): the gradients of ssm_scan_bwd, taken
+ * per packed sequence. Inside a sequence the recurrence and its adjoint are those of
+ * ssm_scan_bwd; at a boundary nothing crosses: the adjoint entering the last token of
+ * sequence i is dh_final[i] (not what its successor carries back), and the state
+ * before the first token of sequence i is h0[i], so dh0[i] = a G at that first token.
+ * An empty sequence passes dh_final[i] to dh0[i] unchanged. dA, dD and ddelta_bias sum
+ * over every token of every sequence.
+ *
+ *   x, delta, z, dy, dx, ddelta, dz   [dim][total] io_dtype (dz exactly when z)
+ *   B, C                              [total][dstate] io_dtype
+ *   dB, dC                            [total][dstate] fp32 out
+ *   cu_seqlens, nseq                  as for ssm_scan_varlen_fwd (not checked; outputs
+ *                                     unspecified if invalid, no access outside the
+ *                                     buffers given)
+ *   h0, dh_final                      [nseq][dim][dstate] fp32 or NULL (zero)
+ *   dh0                               [nseq][dim][dstate] fp32 out or NULL
+ *   A, D, delta_bias, delta_softplus, dA, dD, ddelta_bias   as for ssm_scan_bwd
+ *   opts                              as for ssm_scan_bwd; saved must be 0 (the call
+ *                                     recomputes its checkpoints)
+ * total >= 0 (0: dh0 = dh_final, and dA, dD, ddelta_bias are zero), nseq >= 1,
+ * dim >= 1, dstate == 16. The workspace is ssm_scan_varlen_bwd_workspace_bytes(...)
+ * bytes (0 when total == 0), laid out as for ssm_scan_bwd with batch = 1 and
+ * seqlen = total. Every output overlaps nothing; results are deterministic.
+ */
+size_t ssm_scan_varlen_bwd_workspace_bytes(int64_t total, int64_t dim, int64_t dstate,
+                                           ssm_dtype io_dtype, const ssm_scan_options* opts);
+
+ssm_status ssm_scan_varlen_bwd(const void* x, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, int delta_softplus,
+                               const int32_t* cu_seqlens, int64_t nseq, const float* h0,
+                               const void* dy, const float* dh_final, void* dx, void* ddelta,
+                               void* dz, float* dA, float* dB, float* dC, float* dD,
+                               float* ddelta_bias, float* dh0, int64_t total, int64_t dim,
                                int64_t dstate, ssm_dtype io_dtype, void* workspace,
                                size_t workspace_bytes, const ssm_scan_options* opts,
                                void* stream);

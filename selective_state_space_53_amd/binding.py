@@ -23,7 +23,8 @@ SSM_OK, SSM_ERR_INVALID_ARGUMENT, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE_TOO_SMA
 SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_scan_bwd_workspace_bytes",
            "ssm_scan_bwd", "ssm_scan_varlen_workspace_bytes",
-           "ssm_scan_varlen_fwd", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
+           "ssm_scan_varlen_fwd", "ssm_scan_varlen_bwd_workspace_bytes", "ssm_scan_varlen_bwd",
+           "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
            "ssm_state_update", "ssm_status_string", "ssm_last_error", "ssm_abi_version")
 
 
@@ -61,6 +62,14 @@ lib.ssm_scan_varlen_fwd.restype = ctypes.c_int
 lib.ssm_scan_varlen_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                     _i64, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp,
                                     ctypes.c_size_t, ctypes.POINTER(ScanOptions), _vp]
+lib.ssm_scan_varlen_bwd_workspace_bytes.restype = ctypes.c_size_t
+lib.ssm_scan_varlen_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int,
+                                                    ctypes.POINTER(ScanOptions)]
+lib.ssm_scan_varlen_bwd.restype = ctypes.c_int
+lib.ssm_scan_varlen_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                    _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _i64, _i64, _i64, ctypes.c_int, _vp, ctypes.c_size_t,
+                                    ctypes.POINTER(ScanOptions), _vp]
 lib.ssm_causal_conv1d_fwd.restype = ctypes.c_int
 lib.ssm_causal_conv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                       ctypes.c_int, ctypes.c_int, _vp]
@@ -80,7 +89,7 @@ lib.ssm_abi_version.argtypes = []
 # SSM_SCAN_ABI_VERSION this binding's argument lists and ScanOptions follow; a library
 # built from other sources (a stale .so) is refused rather than called with the wrong
 # layout.
-ABI_VERSION = 3
+ABI_VERSION = 4
 if lib.ssm_abi_version() != ABI_VERSION:
     raise ImportError(f"{_LIB_PATH} has ABI version {lib.ssm_abi_version()}, this binding "
                       f"expects {ABI_VERSION}: rebuild the library")
@@ -319,6 +328,71 @@ def ssm_scan_varlen_fwd(x, delta, A, B, C, cu_seqlens, D=None, z=None, delta_bia
             total, dim, N, code, _ptr(workspace), 0 if workspace is None else workspace.numel(),
             opts, s))
     return (y, h_final) if return_final_state else y
+
+
+def ssm_scan_varlen_bwd_workspace_bytes(total, dim, dstate, io_dtype, plan=0, chunk_len=0,
+                                        group_channels=0, bwd_group_channels=0,
+                                        bwd_chunk_len=0) -> int:
+    return lib.ssm_scan_varlen_bwd_workspace_bytes(
+        total, dim, dstate, _io_code(io_dtype),
+        _options(plan, chunk_len, None, group_channels, bwd_group_channels=bwd_group_channels,
+                 bwd_chunk_len=bwd_chunk_len))
+
+
+def ssm_scan_varlen_bwd(x, delta, A, B, C, dy, cu_seqlens, D=None, z=None, delta_bias=None,
+                        delta_softplus=True, h0=None, dh_final=None, want_dh0=False,
+                        workspace=None, plan=0, chunk_len=0, stream=None, timing_events=None,
+                        group_channels=0, bwd_group_channels=0, bwd_chunk_len=0):
+    """Gradients of ssm_scan_varlen_fwd (causal). x, delta, z, dy: [dim][total];
+    B, C: [total][16]; cu_seqlens: int32 [nseq+1] on the device; h0, dh_final:
+    [nseq][dim][16]. Returns a dict like ssm_scan_bwd's (dB, dC [total][16]; dh0
+    [nseq][dim][16])."""
+    _dev(x, "x")
+    io = x.dtype
+    dim, total = x.shape
+    N = A.shape[-1]
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least 2 entries")
+    nseq = cu_seqlens.numel() - 1
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(dy, "dy", io, x.shape)
+    _dev(A, "A", torch.float32, (dim, N))
+    _dev(B, "B", io, (total, N))
+    _dev(C, "C", io, (total, N))
+    _dev(D, "D", torch.float32, (dim,))
+    _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    _dev(h0, "h0", torch.float32, (nseq, dim, N))
+    _dev(dh_final, "dh_final", torch.float32, (nseq, dim, N))
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {
+        "dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+        "dz": torch.empty_like(x) if z is not None else None,
+        "dA": torch.empty((dim, N), **f32), "dB": torch.empty((total, N), **f32),
+        "dC": torch.empty((total, N), **f32),
+        "dD": torch.empty((dim,), **f32) if D is not None else None,
+        "ddelta_bias": torch.empty((dim,), **f32) if delta_bias is not None else None,
+        "dh0": torch.empty((nseq, dim, N), **f32) if want_dh0 else None,
+    }
+    code = _dtype_code(x)
+    opts = _options(plan, chunk_len, timing_events, group_channels,
+                    bwd_group_channels=bwd_group_channels, bwd_chunk_len=bwd_chunk_len)
+    ws_bytes = lib.ssm_scan_varlen_bwd_workspace_bytes(total, dim, N, code, opts)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        _check(lib.ssm_scan_varlen_bwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(cu_seqlens), nseq, _ptr(h0), _ptr(dy),
+            _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]),
+            _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]),
+            total, dim, N, code, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+            opts, s))
+    return g
 
 
 def ssm_causal_conv1d_fwd(x, weight, bias=None, conv_state=None, activation=True,

@@ -426,7 +426,7 @@ struct BwdPlan {
     int64_t nckpt, chunk_len, nchunks;
     // workspace offsets: the checkpoints and q first (what a training forward saves;
     // their place depends on the shape only), then the forward's own workspace
-    size_t ws_ckpt, ws_q, ws_fwd, ws_bc, ws_A, ws_D, ws_bias, ws_gc, ws_gs, ws_total;
+    size_t ws_ckpt, ws_q, ws_fwd, ws_bc, ws_A, ws_D, ws_bias, ws_gc, ws_gs, ws_flag, ws_total;
 };
 
 // Where the checkpoints ([batch*dim][ceil(L/16)][16] fp32, offset 0) and q ([batch][dim][L]
@@ -543,25 +543,17 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
     bp->ws_bias = align_up(bp->ws_D + (size_t)pd, 256);
     bp->ws_gc = align_up(bp->ws_bias + (size_t)pd, 256);
     bp->ws_gs = align_up(bp->ws_gc + (size_t)gc, 256);
-    bp->ws_total = align_up(bp->ws_gs + (size_t)gs, 256);
+    bp->ws_flag = align_up(bp->ws_gs + (size_t)gs, 256);   // [K] int32 (packed input)
+    bp->ws_total = align_up(bp->ws_flag + (size_t)K * 4, 256);
     return SSM_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                                    ssm_dtype io_dtype, const ssm_scan_options* opts) {
-    BwdPlan bp;
-    if (make_bwd_plan(batch, seqlen, dim, dstate, io_dtype, opts, &bp) != SSM_OK) return 0;
-    return bp.ws_total;
-}
-
-ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
+// The backward of ssm_scan_bwd (cu == nullptr: batch rows) and of ssm_scan_varlen_bwd
+// (cu set: batch = 1, seqlen = total, h0 / dh_final / dh0 per sequence).
+ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void* B,
                         const void* C, const float* D, const void* z,
                         const float* delta_bias, int delta_softplus, const float* h0,
-                        const void* dy, const float* dh_final, void* dx, void* ddelta,
+                        const int32_t* cu, int64_t nseq, const void* dy, const float* dh_final, void* dx, void* ddelta,
                         void* dz, float* dA, float* dB, float* dC, float* dD,
                         float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
                         int64_t dim, int64_t dstate, ssm_dtype io_dtype, void* workspace,
@@ -584,7 +576,13 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         const int64_t io = batch * dim * seqlen * elem;
         const int64_t bc = batch * seqlen * dstate * elem;
         const int64_t bc32 = batch * seqlen * dstate * 4;
-        const int64_t stb = batch * dim * dstate * 4;
+        const int64_t nstates = cu ? nseq : batch;   // rows of h0, dh_final, dh0
+        int64_t stb;
+        if (!bytes4(nstates, dim, dstate, 4, &stb))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "state size overflows");
+        if (cu && opts && opts->saved)
+            return fail(SSM_ERR_UNSUPPORTED,
+                        "ssm_scan_varlen_bwd recomputes its checkpoints (saved must be 0)");
         struct {
             const char* name;
             const void* p;
@@ -596,7 +594,8 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
                   {"dx", dx, 16},         {"ddelta", ddelta, 16}, {"dz", dz, 16},
                   {"dA", dA, 16},         {"dB", dB, 16},       {"dC", dC, 16},
                   {"dD", dD, 4},          {"ddelta_bias", ddelta_bias, 4},
-                  {"dh0", dh0, 16},       {"workspace", workspace, 16}};
+                  {"dh0", dh0, 16},       {"workspace", workspace, 16},
+                  {"cu_seqlens", cu, 4}};
         for (auto& a : al)
             if (a.p && !aligned(a.p, a.align))
                 return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
@@ -611,14 +610,14 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
             region("B", B, bc),           region("C", C, bc),
             region("A", A, dim * dstate * 4), region("D", D, dim * 4),
             region("delta_bias", delta_bias, dim * 4), region("h0", h0, stb),
-            region("dh_final", dh_final, stb),
+            region("dh_final", dh_final, stb), region("cu_seqlens", cu, (nseq + 1) * 4),
             // outputs from here on: each may overlap nothing
             region("dx", dx, io),         region("ddelta", ddelta, io),
             region("dz", dz, io),         region("dA", dA, dim * dstate * 4),
             region("dB", dB, bc32),       region("dC", dC, bc32),
             region("dD", dD, dim * 4),    region("ddelta_bias", ddelta_bias, dim * 4),
             region("dh0", dh0, stb),      region("workspace", workspace, (int64_t)bp.ws_total)};
-        constexpr int kFirstOut = 11;
+        constexpr int kFirstOut = 12;
         constexpr int kN = sizeof(regs) / sizeof(regs[0]);
         for (int i = kFirstOut; i < kN; ++i)
             for (int j = 0; j < kN; ++j)
@@ -651,7 +650,8 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
             bp.fwd.nchunks > 1 ? reinterpret_cast<float*>(fws + bp.fwd.ws_sum) : nullptr;
         fp.chunk_flag =
             bp.fwd.nchunks > 1 ? reinterpret_cast<int32_t*>(fws + bp.fwd.ws_flag) : nullptr;
-        fp.cu = nullptr;
+        fp.cu = cu;
+        fp.nseq = (int32_t)nseq;
         fp.ckpt = reinterpret_cast<float*>(ws + bp.ws_ckpt);
         fp.nckpt = bp.nckpt;
         fp.batch = batch;
@@ -699,6 +699,10 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         prm.part_bias = reinterpret_cast<float*>(ws + bp.ws_bias);
         prm.g_carry = bp.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.ws_gc) : nullptr;
         prm.g_sum = bp.nchunks > 1 ? reinterpret_cast<float*>(ws + bp.ws_gs) : nullptr;
+        prm.cu = cu;
+        prm.nseq = (int32_t)nseq;
+        prm.h0 = h0;
+        prm.chunk_flag = reinterpret_cast<int32_t*>(ws + bp.ws_flag);
         prm.chunk_len = bp.chunk_len;
         prm.nchunks = (int32_t)bp.nchunks;
         prm.chunk_offset = 0;
@@ -728,6 +732,104 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
         return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
     }
 }
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                    ssm_dtype io_dtype, const ssm_scan_options* opts) {
+    BwdPlan bp;
+    if (make_bwd_plan(batch, seqlen, dim, dstate, io_dtype, opts, &bp) != SSM_OK) return 0;
+    return bp.ws_total;
+}
+
+ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z,
+                        const float* delta_bias, int delta_softplus, const float* h0,
+                        const void* dy, const float* dh_final, void* dx, void* ddelta,
+                        void* dz, float* dA, float* dB, float* dC, float* dD,
+                        float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
+                        int64_t dim, int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                        size_t workspace_bytes, const ssm_scan_options* opts, void* stream) {
+    return bwd_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, nullptr, 0, dy,
+                    dh_final, dx, ddelta, dz, dA, dB, dC, dD, ddelta_bias, dh0, batch, seqlen,
+                    dim, dstate, io_dtype, workspace, workspace_bytes, opts, stream);
+}
+
+size_t ssm_scan_varlen_bwd_workspace_bytes(int64_t total, int64_t dim, int64_t dstate,
+                                           ssm_dtype io_dtype, const ssm_scan_options* opts) {
+    if (total == 0) return 0;
+    return ssm_scan_bwd_workspace_bytes(1, total, dim, dstate, io_dtype, opts);
+}
+
+ssm_status ssm_scan_varlen_bwd(const void* x, const void* delta, const float* A, const void* B,
+                               const void* C, const float* D, const void* z,
+                               const float* delta_bias, int delta_softplus,
+                               const int32_t* cu_seqlens, int64_t nseq, const float* h0,
+                               const void* dy, const float* dh_final, void* dx, void* ddelta,
+                               void* dz, float* dA, float* dB, float* dC, float* dD,
+                               float* ddelta_bias, float* dh0, int64_t total, int64_t dim,
+                               int64_t dstate, ssm_dtype io_dtype, void* workspace,
+                               size_t workspace_bytes, const ssm_scan_options* opts,
+                               void* stream) {
+    try {
+        if (!cu_seqlens) return fail(SSM_ERR_INVALID_ARGUMENT, "cu_seqlens is required");
+        if (nseq < 1 || nseq >= (int64_t(1) << 30))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "nseq=%lld must be in [1, 2^30)",
+                        (long long)nseq);
+        if (total < 0 || total >= (int64_t(1) << 31))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "total=%lld must be in [0, 2^31)",
+                        (long long)total);
+        if (total > 0)
+            return bwd_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, cu_seqlens,
+                            nseq, dy, dh_final, dx, ddelta, dz, dA, dB, dC, dD, ddelta_bias,
+                            dh0, 1, total, dim, dstate, io_dtype, workspace, workspace_bytes,
+                            opts, stream);
+        // no tokens: every sequence is empty (dh0 = dh_final) and the sums over tokens are 0
+        BwdPlan bp;
+        ssm_status st = make_bwd_plan(1, 1, dim, dstate, io_dtype, opts, &bp);
+        if (st != SSM_OK) return st;
+        if (delta_softplus != 0 && delta_softplus != 1)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "delta_softplus must be 0 or 1");
+        if (!dA) return fail(SSM_ERR_INVALID_ARGUMENT, "dA is required");
+        if (dD && !D) return fail(SSM_ERR_INVALID_ARGUMENT, "dD needs D");
+        if (ddelta_bias && !delta_bias)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "ddelta_bias needs delta_bias");
+        int64_t stb;
+        if (!bytes4(nseq, dim, dstate, 4, &stb))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "state size overflows");
+        struct {
+            const char* name;
+            const void* p;
+            uintptr_t align;
+        } al[] = {{"dA", dA, 16}, {"dD", dD, 4}, {"ddelta_bias", ddelta_bias, 4},
+                  {"dh0", dh0, 16}, {"dh_final", dh_final, 16}};
+        for (auto& a : al)
+            if (a.p && !aligned(a.p, a.align))
+                return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
+                            (unsigned)a.align);
+        const Region regs[] = {region("dh_final", dh_final, stb), region("dA", dA, dim * dstate * 4),
+                               region("dD", dD, dim * 4), region("ddelta_bias", ddelta_bias, dim * 4),
+                               region("dh0", dh0, stb)};
+        for (int i = 1; i < 5; ++i)
+            for (int j = 0; j < 5; ++j)
+                if (i != j && overlaps(regs[i], regs[j]))
+                    return fail(SSM_ERR_INVALID_ARGUMENT, "%s overlaps %s", regs[i].name,
+                                regs[j].name);
+        hipStream_t strm = static_cast<hipStream_t>(stream);
+        hipError_t e = ssm::launch_copy_state(nullptr, dA, dim * dstate, strm);
+        if (e == hipSuccess && dD) e = ssm::launch_copy_state(nullptr, dD, dim, strm);
+        if (e == hipSuccess && ddelta_bias)
+            e = ssm::launch_copy_state(nullptr, ddelta_bias, dim, strm);
+        if (e == hipSuccess && dh0) e = ssm::launch_copy_state(dh_final, dh0, stb / 4, strm);
+        if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        return SSM_OK;
+    } catch (...) {
+        return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
+    }
+}
+
 
 const char* ssm_status_string(ssm_status s) {
     switch (s) {

@@ -119,7 +119,103 @@ __device__ __forceinline__ float row_sum4(float v0, float v1, float v2, float v3
     return k;
 }
 
-template <typename IO, int CG>
+// Packed sequences: the tokens of [t0, t0 + nvalid) (nvalid <= 16) that are the first
+// (smask) or last (emask) token of a non-empty sequence, as bit masks over the tile.
+__device__ __forceinline__ void tile_events(const int32_t* cu, int nseq, int64_t t0, int nvalid,
+                                            uint32_t* smask, uint32_t* emask) {
+    uint32_t sm = 0, em = 0;
+    const int64_t t1 = t0 + nvalid;
+    for (int s = seq_of(cu, nseq, t0); s < nseq; ++s) {   // the sequences overlapping it
+        const int64_t st = cu[s], en = cu[s + 1];
+        if (st >= t1) break;
+        if (en > st) {
+            if (st >= t0) sm |= 1u << (uint32_t)(st - t0);
+            if (en <= t1) em |= 1u << (uint32_t)(en - 1 - t0);
+        }
+        if (en >= t1) break;
+    }
+    *smask = sm;
+    *emask = em;
+}
+
+// A tile of packed input with sequence boundaries in it, token by token: the recompute
+// restarts from h0[s] at the first token of sequence s; going backwards, the gradient
+// entering the last token of s is dh_final[s] (not what later tokens carried), the state
+// before the first token is h0[s], and after it dh0[s] = a G is written. Otherwise the
+// same arithmetic as the quiet path, in the same order per token.
+template <int CG>
+__device__ __forceinline__ void bwd_event_tile(
+    const BwdParams& p, int64_t t0, int64_t d, bool valid, int pr, int cc, int lane16,
+    uint32_t smask, uint32_t emask, const float* a2, const float* Ar, float hs0, float hs1,
+    const float* cD, const float* cU, const float* cQ, const float* bct, float* p1, float* p2,
+    float* red, float (&hs)[kT][2], float* Gc, float* dA) {
+    constexpr int kLaneRows = CG / 2;
+    auto seq_state = [&](const float* base, int s) {   // base[s][d][2pr..2pr+1] or zeros
+        float2 v = make_float2(0.f, 0.f);
+        if (base && valid)
+            v = *reinterpret_cast<const float2*>(base + ((int64_t)s * p.dim + d) * kDState + 2 * pr);
+        return v;
+    };
+    {
+        float h0 = hs0, h1 = hs1;
+#pragma unroll
+        for (int k = 0; k < kT; ++k) {
+            if (smask & (1u << k)) {
+                const float2 v = seq_state(p.h0, seq_of(p.cu, p.nseq, t0 + k));
+                h0 = v.x;
+                h1 = v.y;
+            }
+            const float Dk = cD[k], Uk = cU[k];
+            const float2 bb = *reinterpret_cast<const float2*>(bct + k * 4);
+            h0 = __builtin_fmaf(fast_exp2(Dk * a2[0]), h0, bb.x * Uk);
+            h1 = __builtin_fmaf(fast_exp2(Dk * a2[1]), h1, bb.y * Uk);
+            hs[k][0] = h0;
+            hs[k][1] = h1;
+        }
+    }
+#pragma unroll
+    for (int k = kT - 1; k >= 0; --k) {
+        if (emask & (1u << k)) {
+            const float2 v = seq_state(p.dh_final, seq_of(p.cu, p.nseq, t0 + k));
+            Gc[0] = v.x;
+            Gc[1] = v.y;
+        }
+        const float Dk = cD[k], Uk = cU[k], Qk = cQ[k];
+        const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
+        const float e0 = fast_exp2(Dk * a2[0]);
+        const float e1 = fast_exp2(Dk * a2[1]);
+        const float G0 = __builtin_fmaf(Qk, q.z, Gc[0]);
+        const float G1 = __builtin_fmaf(Qk, q.w, Gc[1]);
+        float hp0 = k > 0 ? hs[k > 0 ? k - 1 : 0][0] : hs0;
+        float hp1 = k > 0 ? hs[k > 0 ? k - 1 : 0][1] : hs1;
+        const bool first = (smask & (1u << k)) != 0;
+        int s = 0;
+        if (first) {
+            s = seq_of(p.cu, p.nseq, t0 + k);
+            const float2 v = seq_state(p.h0, s);
+            hp0 = v.x;
+            hp1 = v.y;
+        }
+        const float o1 = __builtin_fmaf(G1, q.y, G0 * q.x);          // G.B
+        const float w0 = G0 * hp0 * e0;
+        const float w1 = G1 * hp1 * e1;
+        const float o2 = __builtin_fmaf(w1, Ar[1], w0 * Ar[0]);      // G.h.a.A
+        dA[0] = __builtin_fmaf(w0, Dk, dA[0]);
+        dA[1] = __builtin_fmaf(w1, Dk, dA[1]);
+        const float sr = row_sum4(G0 * Uk, G1 * Uk, Qk * hs[k][0], Qk * hs[k][1], lane16);
+        red[k * kLaneRows * 4] = sr;
+        Gc[0] = e0 * G0;
+        Gc[1] = e1 * G1;
+        if (first && p.dh0 && valid)
+            *reinterpret_cast<float2*>(p.dh0 + ((int64_t)s * p.dim + d) * kDState + 2 * pr) =
+                make_float2(Gc[0], Gc[1]);
+        const int slot = (((k >> 2) ^ (cc & 3)) << 2) + (k & 3);
+        p1[slot] = o1;
+        p2[slot] = o2;
+    }
+}
+
+template <typename IO, int CG, bool PACKED>
 __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
     constexpr int kRowsPerPair = CG / 16;
@@ -166,9 +262,11 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         Ar[1] = av.y;
         a2[0] = av.x * kLog2e;
         a2[1] = av.y * kLog2e;
-        // the gradient reaching the chunk's last token from later ones
+        // the gradient reaching the chunk's last token from later ones (packed: the
+        // last token of a sequence takes its dh_final instead, at that token)
         const float* g = p.g_carry ? p.g_carry + (row * p.nchunks + c) * kDState + 2 * pr
-                                   : (p.dh_final ? p.dh_final + row * kDState + 2 * pr : nullptr);
+                                   : (!PACKED && p.dh_final ? p.dh_final + row * kDState + 2 * pr
+                                                            : nullptr);
         if (g) {
             const float2 gv = *reinterpret_cast<const float2*>(g);
             Gc[0] = gv.x;
@@ -280,9 +378,17 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             store2(reinterpret_cast<IO*>(dzw + at(t0)), vec, nq, dzv[0], dzv[1]);
         __syncthreads();
 
-        // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint
+        // packed: the tile's tokens that start (smask) or end (emask) a sequence; the
+        // same for the whole workgroup, so every branch on them is uniform
+        uint32_t smask = 0, emask = 0;
+        if (PACKED) tile_events(p.cu, p.nseq, t0, nvalid, &smask, &emask);
         const float* bct = sBC + (it & 1) * kBcT + pr * (kT * 4);
         float hs[kT][2];
+        if (PACKED && (smask | emask)) {
+            bwd_event_tile<CG>(p, t0, d, valid, pr, cc, lane16, smask, emask, a2, Ar, hs0, hs1,
+                               cD, cU, cQ, bct, p1, p2, red, hs, Gc, dA);
+        } else {
+        // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint
         {
             float h0 = hs0, h1 = hs1;
 #pragma unroll
@@ -345,6 +451,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             // register count past 3 waves per SIMD
             __builtin_amdgcn_sched_barrier(0);
         }
+        }   // quiet tile
         __syncthreads();
 
         // ---- post: dx, ddelta for (cq, 2 tokens); the workgroup's dB, dC partial sums
@@ -400,7 +507,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     // ---- per-row results: dh0 = a_0 G_0 (the carry after token 0), dA partials
     const int64_t prow = (b * p.nchunks + c) * p.dim;   // partials of (batch row, chunk)
     if (valid) {
-        if (p.dh0 && c == 0)
+        if (!PACKED && p.dh0 && c == 0)
             *reinterpret_cast<float2*>(p.dh0 + row * kDState + 2 * pr) = make_float2(Gc[0], Gc[1]);
         *reinterpret_cast<float2*>(p.part_A + (prow + d) * kDState + 2 * pr) =
             make_float2(dA[0], dA[1]);
@@ -423,7 +530,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
 //   G_loc = sum over its tokens t of (prod_{r from its first token to t} a_r) dq_t C_t,
 // and its sum of Delta (the decay of a gradient crossing the whole chunk is
 // exp(A sum Delta)). The same mapping and tiles as the full kernel, only the G chain.
-template <typename IO, int CG>
+template <typename IO, int CG, bool PACKED>
 __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
     constexpr int kRowsPerPair = CG / 16;
@@ -465,6 +572,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     const IO* zr = p.z ? static_cast<const IO*>(p.z) + rowq * L : nullptr;
     const IO* gr = static_cast<const IO*>(p.dy) + rowq * L;
     float G[2] = {0.f, 0.f}, dsum = 0.0f;
+    bool ended = false;   // packed: a sequence ends inside the chunk
     float* const myD = sD + cq * kRowF + 2 * jq;
     float* const myQ = sQ + cq * kRowF + 2 * jq;
     const float* const cD = sD + cc * kRowF;
@@ -516,8 +624,24 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
         __syncthreads();
         const float* ct = sC + pr * kT * 2;
+        // packed: at the last token of a sequence the gradient restarts from its dh_final,
+        // so the chunk's end value no longer depends on what later chunks carry in
+        uint32_t smask = 0, emask = 0;
+        if (PACKED) {
+            tile_events(p.cu, p.nseq, t0, nvalid, &smask, &emask);
+            ended |= emask != 0;
+        }
 #pragma unroll
         for (int k = kT - 1; k >= 0; --k) {
+            if (PACKED && (emask & (1u << k))) {
+                float2 v = make_float2(0.f, 0.f);
+                if (p.dh_final && valid)
+                    v = *reinterpret_cast<const float2*>(
+                        p.dh_final +
+                        ((int64_t)seq_of(p.cu, p.nseq, t0 + k) * p.dim + d) * kDState + 2 * pr);
+                G[0] = v.x;
+                G[1] = v.y;
+            }
             const float ds = cD[k];
             const float2 cv = *reinterpret_cast<const float2*>(ct + 2 * k);
             const float qk = cQ[k];
@@ -528,6 +652,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         }
         __syncthreads();
     }
+    if (PACKED && gidx == 0 && tid == 0) p.chunk_flag[c] = ended ? 1 : 0;
     if (valid) {
         *reinterpret_cast<float2*>(p.g_carry + (row * p.nchunks + c) * kDState + 2 * pr) =
             make_float2(G[0], G[1]);
@@ -588,16 +713,32 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     }
 }
 
+// dh0 of the empty packed sequences: their dh_final (or zero); one thread per (s, d, n)
+__global__ __launch_bounds__(256) void bwd_empty_seq_kernel(const int32_t* __restrict__ cu,
+                                                            int nseq, int64_t dim,
+                                                            const float* __restrict__ dh_final,
+                                                            float* __restrict__ dh0) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)nseq * dim * kDState) return;
+    const int s = (int)(i / (dim * kDState));
+    if (cu[s] != cu[s + 1]) return;
+    dh0[i] = dh_final ? dh_final[i] : 0.0f;
+}
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
+
 
 hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t stream,
                            hipEvent_t ev_begin, hipEvent_t ev_end) {
     const int64_t ngroups = prm.batch * prm.groups_per_batch;
     hipError_t e;
 #define SSM_BWD(KERNEL, IO, N, GRID, P)                                                    \
-    hipLaunchKernelGGL((KERNEL<IO, N>), GRID, dim3(N * 8), 0, stream, P)
+    if (P.cu)                                                                              \
+        hipLaunchKernelGGL((KERNEL<IO, N, true>), GRID, dim3(N * 8), 0, stream, P);        \
+    else                                                                                   \
+        hipLaunchKernelGGL((KERNEL<IO, N, false>), GRID, dim3(N * 8), 0, stream, P)
 #define SSM_BWD_ALL(KERNEL, GRID, P)                                                       \
     switch (cg * 2 + (bf16 ? 1 : 0)) {                                                     \
         case 65: SSM_BWD(KERNEL, uint16_t, 32, GRID, P); break;                            \
@@ -617,8 +758,11 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         SSM_BWD_ALL(scan_bwd_local_kernel, g1, p1)
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = launch_carry(prm.A, prm.dh_final, prm.g_carry, prm.g_sum, nullptr,
-                         prm.batch * prm.dim, prm.dim, prm.nchunks, 1, stream);
+        // (packed: the carry starts from zero and takes a chunk's local value as is where a
+        // sequence ends inside it; the last tokens of sequences bring in dh_final)
+        e = launch_carry(prm.A, prm.cu ? nullptr : prm.dh_final, prm.g_carry, prm.g_sum,
+                         prm.cu ? prm.chunk_flag : nullptr, prm.batch * prm.dim, prm.dim,
+                         prm.nchunks, 1, stream);
         if (e != hipSuccess) return e;
     }
     if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipGetLastError();
@@ -644,6 +788,12 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
     hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)cdiv(prm.dim * kDState, 256)),
                        dim3(256), 0, stream, prm.part_A, prm.part_D, prm.part_bias, prm.dA,
                        prm.dD, prm.dbias, prm.batch * prm.nchunks, prm.dim);
+    e = hipGetLastError();
+    if (e != hipSuccess || !prm.cu || !prm.dh0) return e;
+    // packed: an empty sequence's final state is its initial state, so dh0 = dh_final
+    const int64_t n = (int64_t)prm.nseq * prm.dim * kDState;
+    hipLaunchKernelGGL(bwd_empty_seq_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
+                       prm.cu, prm.nseq, prm.dim, prm.dh_final, prm.dh0);
     return hipGetLastError();
 }
 

@@ -73,5 +73,17 @@ __device__ __forceinline__ float dsilu_f(float z) {
     return s * __builtin_fmaf(z, 1.0f - s, 1.0f);
 }
 
+// Index of the packed sequence that holds token t: the largest s in [0, nseq) with
+// cu[s] <= t (0 when there is none). Reads only cu[0..nseq-1], whatever cu holds.
+__device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int64_t t) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 }  // namespace dev
 }  // namespace ssm

@@ -82,7 +82,7 @@ struct BwdParams {
     const float* A;
     const float* D;
     const float* bias;
-    const float* dh_final;   // [batch*dim][16] or null
+    const float* dh_final;   // [batch*dim][16] or null (packed: see below)
     const float* ckpt;       // [batch*dim][nckpt][16]: the state before every 16th token
     const void* q;           // [batch][dim][seqlen] io: the forward output before the gate
     const float* bcq;        // B and C widened, as for the forward
@@ -102,6 +102,13 @@ struct BwdParams {
     float* g_carry;          // chunked: [batch*dim][nchunks][16], the gradient reaching the
                              // end of each chunk from later tokens (pass 1: local values)
     float* g_sum;            // chunked: [batch*dim][nchunks], the sum of Delta per chunk
+    // packed sequences (batch = 1, seqlen = total tokens): cu_seqlens [nseq+1]; h0,
+    // dh_final and dh0 are then per sequence, [nseq][dim][16]; chunk_flag [nchunks]
+    // (chunked: 1 where a sequence ends inside the chunk)
+    const int32_t* cu;
+    const float* h0;
+    int32_t* chunk_flag;
+    int32_t nseq;
     int64_t batch, seqlen, dim, lpad, nckpt, chunk_len;
     int32_t groups_per_batch, nchunks, chunk_offset, softplus, aligned;
 };

@@ -146,18 +146,6 @@ constexpr int kTile = 32;                 // tokens per tile
 constexpr int kLdsRow = kTile + 4;        // padded [channel][token] LDS row (floats)
 constexpr int kBcTile = 8 * kTile * 4;    // floats of widened B/C per tile (8 state pairs)
 
-// Index of the packed sequence that holds token t: the largest s in [0, nseq) with
-// cu[s] <= t (0 when there is none). Reads only cu[0..nseq-1], whatever cu holds.
-__device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int64_t t) {
-    int lo = 0, hi = nseq - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)cu[mid] <= t) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
 // One workgroup = CG channels (a multiple of 16) of one batch row x all 16 states,
 // CG*8 threads = CG/8 waves.
 //  core mapping: each 16-lane row holds one state pair p (states 2p, 2p+1) of 16
@@ -185,7 +173,7 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int64_t t) {
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
-    static_assert(!CKPT || (!LOCAL && !REV && !PACKED), "checkpoints: causal, final pass");
+    static_assert(!CKPT || (!LOCAL && !REV), "checkpoints: causal, final pass");
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
     __shared__ float sD[CG * kLdsRow];
@@ -430,6 +418,10 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                 const int k = REV ? kTile - 1 - kk : kk;
                 const int64_t t = t0 + k;
                 const bool real = k < nvalid;
+                // checkpoints: the state before tokens t0 and t0 + 16, before any reset
+                // there (the backward applies the resets itself)
+                if (CKPT && valid && (k == 0 || (k == 16 && real)))
+                    *reinterpret_cast<float2*>(ck + (t / 16) * kDState) = make_float2(h[0], h[1]);
                 if (real && t == (REV ? hi - 1 : lo)) {     // first token of sequence s
                     float2 hv = make_float2(0.f, 0.f);
                     if (p.h0 && valid)
@@ -633,7 +625,8 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
 template <typename IO, bool LOCAL>
 hipError_t launch_scan_dir(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
     if (!LOCAL && prm.ckpt)
-        return launch_scan_kernel<IO, false, false, false, true>(cg, grid, stream, prm);
+        return prm.cu ? launch_scan_kernel<IO, false, false, true, true>(cg, grid, stream, prm)
+                      : launch_scan_kernel<IO, false, false, false, true>(cg, grid, stream, prm);
     if (prm.cu)
         return prm.reverse
                    ? launch_scan_kernel<IO, LOCAL, true, true, false>(cg, grid, stream, prm)

@@ -283,3 +283,45 @@ def test_backward_sequence_length_limit(b):
     assert b.ssm_scan_bwd_workspace_bytes(1, 1 << 25, 16, 16, bf16) > 0          # 48 or 32
     assert b.ssm_scan_bwd_workspace_bytes(1, 1 << 25, 16, 16, bf16, bwd_group_channels=64) == 0
     assert b.ssm_scan_bwd_workspace_bytes(1, 1 << 26, 16, 16, bf16) == 0
+
+
+def varlen_bwd(b, total=100, dim=64, nseq=3, io=1, ws_bytes=None, opts=None, **over):
+    p = dict(P, cu=0x7e0000000000, dy=P["z"] + (1 << 35), dhf=P["hf"] + (1 << 35), dx=P["y"],
+             dd=P["y"] + (1 << 34), dz=P["hf"] + (1 << 34), dA=P["ws"] + (1 << 35),
+             dB=P["ws"] + (1 << 34), dC=P["ws"] + (3 << 33), dD=P["D"] + (1 << 34),
+             dbias=P["bias"] + (1 << 34), dh0=P["h0"] + (1 << 34))
+    p.update(over)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return b.lib.ssm_scan_varlen_bwd(
+        p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["bias"], 1, p["cu"], nseq,
+        p["h0"], p["dy"], p["dhf"], p["dx"], p["dd"], p["dz"], p["dA"], p["dB"], p["dC"],
+        p["dD"], p["dbias"], p["dh0"], total, dim, 16, io, p["ws"], ws_bytes, opts, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), 1), (dict(nseq=0), 1), (dict(total=-1), 1), (dict(total=1 << 31), 1),
+    (dict(cu=0x7e0000000002), 2), (dict(dim=0), 1), (dict(ws=None), 3), (dict(ws_bytes=64), 3),
+    (dict(dy=None), 1), (dict(dz=None), 1), (dict(dx=P["x"]), 1), (dict(dB=P["ws"] + (3 << 33)), 1),
+    (dict(dh0=P["h0"] + 4), 2), (dict(dh0=P["h0"]), 1),
+    # dh0 [nseq][dim][16] overlapping dh_final, with no tokens and with tokens
+    (dict(total=0, dh0=P["hf"] + (1 << 35) + 64), 1), (dict(dh0=P["hf"] + (1 << 35) + 64), 1),
+    (dict(total=0, dA=P["hf"] + (1 << 35)), 1), (dict(total=0, dh0=P["h0"] + 8), 2),
+    (dict(total=0, dim=0), 1), (dict(total=0, dA=None), 1),
+    # one fp32 row of the backward must span less than 4 GiB even at 32 channels per group
+    (dict(total=1 << 25, io=0), 2),
+])
+def test_varlen_bwd_rejects(b, kw, status):
+    assert varlen_bwd(b, **kw) == status
+    assert b.ssm_last_error() != ""
+
+
+def test_varlen_bwd_workspace_and_options(b):
+    assert b.ssm_scan_varlen_bwd_workspace_bytes(0, 64, 16, 1) == 0
+    for kw in ({}, dict(bwd_chunk_len=64), dict(plan=2, chunk_len=64, bwd_group_channels=32)):
+        assert (b.ssm_scan_varlen_bwd_workspace_bytes(1000, 64, 16, 1, **kw)
+                == b.ssm_scan_bwd_workspace_bytes(1, 1000, 64, 16, 1, **kw))
+    # the checkpoints are always recomputed: saved=1 is refused; reverse likewise
+    assert varlen_bwd(b, opts=_save_opts(b, None, 0, saved=1)) == 2
+    assert varlen_bwd(b, opts=_save_opts(b, None, 0, reverse=1)) == 2
+    assert varlen_bwd(b, opts=_save_opts(b, 0x7d0000000000, 1 << 30)) == 1

@@ -1,0 +1,219 @@
+"""GPU parity of the packed-sequence backward (ssm_scan_varlen_bwd, through the C ABI)
+against the fp64 oracle's per-sequence gradients: length mixes with empty, one-token
+and tile/chunk-edge sequences in each backward plan, an integer-exact case that checks
+every boundary reset bit for bit, the Mamba-2.8B layer width over 8192 packed tokens,
+and the no-token call."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+OUTS = ["dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"]
+OKEY = {"ddelta_bias": "dbias"}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_53_amd import binding  # noqa: F401  (fails loudly if unbuilt)
+
+
+def _randn(shape, seed, dtype=torch.float32):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype).to(DEV)
+
+
+def _compare(g, ref, lens, io):
+    """Per-token gradients per channel row, as y; dB and dC normwise over each sequence
+    (one token's sum over channels can cancel far below its terms); dA, dD, ddelta_bias
+    over the tensor; dh0 per (sequence, channel) row."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    errs = {}
+    for k in OUTS:
+        if g.get(k) is None:
+            continue
+        r = np.asarray(ref[OKEY.get(k, k)])
+        got = oracle.f64(g[k])
+        if k in ("dB", "dC"):
+            e = 0.0
+            for a, b in zip(cu[:-1], cu[1:]):
+                if b > a:
+                    e = max(e, parity.rowwise_err(got[a:b].reshape(1, -1),
+                                                  r[a:b].reshape(1, -1)))
+            errs[k] = e
+            continue
+        if k in ("dA", "dD", "ddelta_bias"):
+            got, r = got.reshape(1, -1), r.reshape(1, -1)
+        errs[k] = parity.rowwise_err(got, r)
+    say("   " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= parity.TOL[io]}
+    assert not bad, bad
+
+
+def _run(inp, dy, cu, use_z=True, use_D=True, use_bias=True, h0=None, dhf=None, **plan):
+    from selective_state_space_53_amd import binding
+    g = binding.ssm_scan_varlen_bwd(
+        inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy, cu,
+        D=inp["D"] if use_D else None, z=inp["z"] if use_z else None,
+        delta_bias=inp["delta_bias"] if use_bias else None, h0=h0, dh_final=dhf,
+        want_dh0=True, **plan)
+    torch.cuda.synchronize()
+    ref = oracle.Oracle().scan_varlen_bwd(
+        inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+        oracle.f64(cu).astype(np.int64), D=inp["D"] if use_D else None,
+        z=inp["z"] if use_z else None, delta_bias=inp["delta_bias"] if use_bias else None,
+        h0=h0, dh_final=dhf, nthreads=parity.threads())
+    return g, ref
+
+
+PACKED = [
+    # (lengths, dim, io): empty and one-token sequences, boundaries on and next to the
+    # backward's 16-token tiles and the forward's 32-token tiles
+    ([5, 0, 1, 17, 0, 0, 40, 2, 31, 32, 33, 1], 70, "f32"),
+    ([300, 1, 1, 64, 0, 700, 3], 160, "bf16"),
+    ([1] * 37, 32, "f32"),
+    ([15, 16, 17, 0, 48, 1, 63, 64, 65], 96, "f32"),
+    ([4103], 130, "bf16"),
+    ([0, 0, 1000, 0], 96, "bf16"),
+]
+# (checkpoint-pass plan, its chunk, backward group, backward chunk)
+BWD_PLANS = [dict(), dict(plan=1, bwd_group_channels=32),
+             dict(plan=2, chunk_len=64, bwd_chunk_len=32),
+             dict(plan=2, chunk_len=96, bwd_group_channels=48, bwd_chunk_len=64)]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=lambda c: "n{}_T{}_d{}_{}".format(
+    len(c[0]), sum(c[0]), c[1], c[2]))
+@pytest.mark.parametrize("plan", BWD_PLANS, ids=["auto", "single_g32", "c64_b32", "c96_g48_b64"])
+def test_packed_bwd_all_outputs(case, plan):
+    lens, dim, io = case
+    total = sum(lens)
+    nseq = len(lens)
+    cfg = synth.ScanConfig("packedbwd", 1, total, dim, io=io, seed=1900 + total)
+    say("case packed bwd", nseq, total, dim, io, plan)
+    inp = synth.packed_inputs(cfg, total, DEV)
+    cu = synth.cu_seqlens(lens, DEV)
+    dy = _randn((dim, total), total, cfg.io_dtype)
+    h0 = _randn((nseq, dim, 16), 7)
+    dhf = _randn((nseq, dim, 16), 8)
+    for var in [dict(use_z=True, use_D=True, use_bias=True, h0=h0, dhf=dhf),
+                dict(use_z=False, use_D=False, use_bias=False, h0=None, dhf=None),
+                dict(use_z=True, use_D=True, use_bias=False, h0=None, dhf=dhf)]:
+        say("  variant", {k: (v is not None) if not isinstance(v, bool) else v
+                          for k, v in var.items()})
+        g, ref = _run(inp, dy, cu, **var, **plan)
+        _compare(g, ref, lens, io)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_packed_bwd_integer_exact(io):
+    """A = 0, Delta = 1 (softplus off), no gate, small integers: every intermediate is
+    an exact integer, so the gradients equal the oracle's bit for bit -- every reset of
+    the adjoint at a sequence's last token (to its dh_final), every h0 at a first token,
+    dh0 of each sequence, with boundaries on and next to tile (16, 32) and chunk edges."""
+    from selective_state_space_53_amd import binding
+    lens = [31, 1, 32, 0, 33, 64, 63, 65, 1, 0, 96, 127, 5, 16, 15, 17]
+    total, nseq, dim = sum(lens), len(lens), 40
+    rng = np.random.default_rng(12 if io == "f32" else 13)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    x = np.zeros((dim, total))
+    for d in range(dim):
+        idx = rng.choice(total, size=10, replace=False)
+        x[d, idx] = rng.choice([-1.0, 1.0], size=10)
+    t = lambda a, dtype=dt: torch.tensor(a, dtype=dtype, device=DEV)
+    inp = {"x": t(x), "delta": torch.ones((dim, total), dtype=dt, device=DEV),
+           "B": t(rng.integers(-1, 2, size=(total, 16))),
+           "C": t(rng.integers(-1, 2, size=(total, 16))),
+           "A": torch.zeros((dim, 16), device=DEV),
+           "D": t(rng.integers(-2, 3, size=dim), torch.float32)}
+    dy = t(rng.integers(-1, 2, size=(dim, total)))
+    h0 = t(rng.integers(-2, 3, size=(nseq, dim, 16)), torch.float32)
+    dhf = t(rng.integers(-2, 3, size=(nseq, dim, 16)), torch.float32)
+    cu = synth.cu_seqlens(lens, DEV)
+    ref = oracle.Oracle().scan_varlen_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                          dy, oracle.f64(cu).astype(np.int64), D=inp["D"],
+                                          delta_softplus=False, h0=h0, dh_final=dhf)
+    for plan in BWD_PLANS + [dict(bwd_group_channels=64, bwd_chunk_len=96)]:
+        say("case packed bwd integer", io, plan)
+        g = binding.ssm_scan_varlen_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                        dy, cu, D=inp["D"], delta_softplus=False, h0=h0,
+                                        dh_final=dhf, want_dh0=True, **plan)
+        torch.cuda.synchronize()
+        for k in ["dx", "ddelta", "dA", "dB", "dC", "dD", "dh0"]:
+            assert np.array_equal(oracle.f64(g[k]), ref[k]), k
+        assert g["ddelta_bias"] is None and g["dz"] is None
+
+
+def test_packed_bwd_full_size():
+    """The Mamba-2.8B layer width (d_inner 5120, bf16) over 8192 packed tokens with a
+    log-uniform length mix (16..2048) and empty sequences, in the library's own plan:
+    every output against the full fp64 oracle."""
+    cfg = synth.CONFIGS["m2p8"]
+    total = cfg.batch * cfg.seqlen
+    lens = synth.length_mix(total, 16, 2048, seed=cfg.seed, empties=3)
+    nseq = len(lens)
+    say("case packed bwd full size", nseq, total)
+    inp = synth.packed_inputs(cfg, total, DEV)
+    cu = synth.cu_seqlens(lens, DEV)
+    dy = _randn((cfg.dim, total), 21, cfg.io_dtype)
+    h0 = _randn((nseq, cfg.dim, 16), 22)
+    dhf = _randn((nseq, cfg.dim, 16), 23)
+    g, ref = _run(inp, dy, cu, h0=h0, dhf=dhf)
+    _compare(g, ref, lens, cfg.io)
+
+
+def test_packed_bwd_no_tokens():
+    """total = 0: every sequence is empty, so dh0 = dh_final (zeros without it) and the
+    parameter gradients are zero."""
+    from selective_state_space_53_amd import binding
+    dim, nseq = 24, 3
+    x = torch.empty((dim, 0), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((0, 16), dtype=torch.bfloat16, device=DEV)
+    A = -torch.ones((dim, 16), device=DEV)
+    D = torch.ones(dim, device=DEV)
+    bias = torch.ones(dim, device=DEV)
+    cu = torch.zeros(nseq + 1, dtype=torch.int32, device=DEV)
+    dhf = _randn((nseq, dim, 16), 3)
+    g = binding.ssm_scan_varlen_bwd(x, x, A, B, B, x, cu, D=D, delta_bias=bias, dh_final=dhf,
+                                    want_dh0=True)
+    gz = binding.ssm_scan_varlen_bwd(x, x, A, B, B, x, cu, want_dh0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dhf)
+    assert torch.count_nonzero(gz["dh0"]) == 0
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert torch.count_nonzero(g[k]) == 0, k
+    assert g["dx"].shape == (dim, 0) and g["dB"].shape == (0, 16)
+
+
+def test_packed_bwd_deterministic():
+    lens = [300, 0, 1, 700, 17]
+    total, dim = sum(lens), 200
+    cfg = synth.ScanConfig("packedbwddet", 1, total, dim, io="bf16", seed=6)
+    inp = synth.packed_inputs(cfg, total, DEV)
+    cu = synth.cu_seqlens(lens, DEV)
+    dy = _randn((dim, total), 6, torch.bfloat16)
+    from selective_state_space_53_amd import binding
+    kw = dict(D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], want_dh0=True,
+              bwd_chunk_len=64)
+    a = binding.ssm_scan_varlen_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                                    cu, **kw)
+    b = binding.ssm_scan_varlen_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                                    cu, **kw)
+    torch.cuda.synchronize()
+    for k in OUTS:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
