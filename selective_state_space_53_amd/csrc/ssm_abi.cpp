@@ -426,7 +426,8 @@ struct BwdPlan {
     int64_t nckpt, chunk_len, nchunks;
     // workspace offsets: the checkpoints and q first (what a training forward saves;
     // their place depends on the shape only), then the forward's own workspace
-    size_t ws_ckpt, ws_q, ws_fwd, ws_bc, ws_A, ws_D, ws_bias, ws_gc, ws_gs, ws_flag, ws_total;
+    size_t ws_ckpt, ws_q, ws_fwd, ws_bc, ws_A, ws_D, ws_bias, ws_gc, ws_gs, ws_flag, ws_ev,
+        ws_seq, ws_total;
 };
 
 // Where the checkpoints ([batch*dim][ceil(L/16)][16] fp32, offset 0) and q ([batch][dim][L]
@@ -544,7 +545,9 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
     bp->ws_gc = align_up(bp->ws_bias + (size_t)pd, 256);
     bp->ws_gs = align_up(bp->ws_gc + (size_t)gc, 256);
     bp->ws_flag = align_up(bp->ws_gs + (size_t)gs, 256);   // [K] int32 (packed input)
-    bp->ws_total = align_up(bp->ws_flag + (size_t)K * 4, 256);
+    bp->ws_ev = align_up(bp->ws_flag + (size_t)K * 4, 256);  // [ceil(L/16)] u32 (packed)
+    bp->ws_seq = align_up(bp->ws_ev + (size_t)bp->nckpt * 4, 256);   // [L] int32 (packed)
+    bp->ws_total = align_up(bp->ws_seq + (size_t)seqlen * 4, 256);
     return SSM_OK;
 }
 
@@ -703,6 +706,8 @@ ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void
         prm.nseq = (int32_t)nseq;
         prm.h0 = h0;
         prm.chunk_flag = reinterpret_cast<int32_t*>(ws + bp.ws_flag);
+        prm.tile_ev = reinterpret_cast<uint32_t*>(ws + bp.ws_ev);
+        prm.tok_seq = reinterpret_cast<int32_t*>(ws + bp.ws_seq);
         prm.chunk_len = bp.chunk_len;
         prm.nchunks = (int32_t)bp.nchunks;
         prm.chunk_offset = 0;

@@ -161,7 +161,7 @@ __device__ __forceinline__ void bwd_event_tile(
 #pragma unroll
         for (int k = 0; k < kT; ++k) {
             if (smask & (1u << k)) {
-                const float2 v = seq_state(p.h0, seq_of(p.cu, p.nseq, t0 + k));
+                const float2 v = seq_state(p.h0, p.tok_seq[t0 + k]);
                 h0 = v.x;
                 h1 = v.y;
             }
@@ -176,7 +176,7 @@ __device__ __forceinline__ void bwd_event_tile(
 #pragma unroll
     for (int k = kT - 1; k >= 0; --k) {
         if (emask & (1u << k)) {
-            const float2 v = seq_state(p.dh_final, seq_of(p.cu, p.nseq, t0 + k));
+            const float2 v = seq_state(p.dh_final, p.tok_seq[t0 + k]);
             Gc[0] = v.x;
             Gc[1] = v.y;
         }
@@ -191,7 +191,7 @@ __device__ __forceinline__ void bwd_event_tile(
         const bool first = (smask & (1u << k)) != 0;
         int s = 0;
         if (first) {
-            s = seq_of(p.cu, p.nseq, t0 + k);
+            s = p.tok_seq[t0 + k];
             const float2 v = seq_state(p.h0, s);
             hp0 = v.x;
             hp1 = v.y;
@@ -212,6 +212,9 @@ __device__ __forceinline__ void bwd_event_tile(
         const int slot = (((k >> 2) ^ (cc & 3)) << 2) + (k & 3);
         p1[slot] = o1;
         p2[slot] = o2;
+        // one scheduling region per token, as the quiet path has one per 4 tokens:
+        // hoisting across tokens raises the register count of the whole kernel
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -314,6 +317,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     Raw2<IO> rx, rd, rz, rg, rq;
     float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
     float2 rck = make_float2(0.f, 0.f);
+    uint32_t rev = 0;   // packed: the tile's event masks (starts | ends << 16)
     // ti: tile of the chunk; its checkpoint is the global tile t0 / 16
     auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kT;
@@ -331,6 +335,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         }
         if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
         if (valid) rck = *reinterpret_cast<const float2*>(ck + (t0 / kT) * kDState);
+        if (PACKED) rev = p.tile_ev[t0 / kT];
     };
     rx.zero();
     rd.zero();
@@ -357,6 +362,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         rg.widen(gv);
         rq.widen(qv);
         const float hs0 = rck.x, hs1 = rck.y;   // the state before the tile's first token
+        const uint32_t ev = rev;
         if (it + 1 < ntiles) load_tile(ti - 1);
         float dl[2], sg[2], dqv[2], uu[2], dzv[2];
 #pragma unroll
@@ -380,11 +386,11 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
 
         // packed: the tile's tokens that start (smask) or end (emask) a sequence; the
         // same for the whole workgroup, so every branch on them is uniform
-        uint32_t smask = 0, emask = 0;
-        if (PACKED) tile_events(p.cu, p.nseq, t0, nvalid, &smask, &emask);
+        const uint32_t smask = PACKED ? (ev & 0xffffu) : 0u, emask = PACKED ? (ev >> 16) : 0u;
         const float* bct = sBC + (it & 1) * kBcT + pr * (kT * 4);
         float hs[kT][2];
-        if (PACKED && (smask | emask)) {
+        // (tiles with events are the rare case: laid out away from the quiet path)
+        if (__builtin_expect(PACKED && (smask | emask) != 0, 0)) {
             bwd_event_tile<CG>(p, t0, d, valid, pr, cc, lane16, smask, emask, a2, Ar, hs0, hs1,
                                cD, cU, cQ, bct, p1, p2, red, hs, Gc, dA);
         } else {
@@ -547,7 +553,18 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     const int64_t L = p.seqlen;
     const int64_t t_beg = (int64_t)c * p.chunk_len;
     const int64_t t_end = (t_beg + p.chunk_len < L) ? t_beg + p.chunk_len : L;
-    const int ntiles = (int)((t_end - t_beg + kT - 1) / kT);
+    int ntiles = (int)((t_end - t_beg + kT - 1) / kT);
+    // packed: once the chain (walked from the chunk's end) reaches the last token of the
+    // sequence holding the chunk's first token, it restarts from that sequence's dh_final;
+    // nothing after that token can reach the chunk's first token, so start there
+    bool ended = false;   // a sequence ends inside the chunk
+    if (PACKED) {
+        const int64_t e = (int64_t)p.cu[p.tok_seq[t_beg] + 1] - 1;
+        if (e >= t_beg && e < t_end) {
+            ended = true;
+            ntiles = (int)((e - t_beg) / kT) + 1;
+        }
+    }
 
     const int r = tid >> 4;
     const int pr = r / kRowsPerPair;
@@ -572,7 +589,6 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     const IO* zr = p.z ? static_cast<const IO*>(p.z) + rowq * L : nullptr;
     const IO* gr = static_cast<const IO*>(p.dy) + rowq * L;
     float G[2] = {0.f, 0.f}, dsum = 0.0f;
-    bool ended = false;   // packed: a sequence ends inside the chunk
     float* const myD = sD + cq * kRowF + 2 * jq;
     float* const myQ = sQ + cq * kRowF + 2 * jq;
     const float* const cD = sD + cc * kRowF;
@@ -581,6 +597,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     // 2 tokens) and, for threads 0..127, C of one (state pair, token)
     Raw2<IO> rd, rz, rg;
     float4 rc = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t rev = 0;   // packed: the tile's event masks (starts | ends << 16)
     auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
@@ -597,6 +614,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         if (tid < 128)
             rc = *reinterpret_cast<const float4*>(
                 p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + t0 + (tid & 15)) * 4);
+        if (PACKED) rev = p.tile_ev[t0 / kT];
     };
     load_tile(ntiles - 1);
     for (int it = 0; it < ntiles; ++it) {
@@ -609,6 +627,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         rz.widen(zv);
         rg.widen(gv);
         const float4 cv4 = rc;
+        const uint32_t emask = PACKED ? (rev >> 16) : 0u;
         if (it + 1 < ntiles) load_tile(ti - 1);
         // C of the tile, per state pair: threads 0..127 move (pair, token)
         if (tid < 128) *reinterpret_cast<float2*>(sC + tid * 2) = make_float2(cv4.z, cv4.w);
@@ -626,11 +645,6 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         const float* ct = sC + pr * kT * 2;
         // packed: at the last token of a sequence the gradient restarts from its dh_final,
         // so the chunk's end value no longer depends on what later chunks carry in
-        uint32_t smask = 0, emask = 0;
-        if (PACKED) {
-            tile_events(p.cu, p.nseq, t0, nvalid, &smask, &emask);
-            ended |= emask != 0;
-        }
 #pragma unroll
         for (int k = kT - 1; k >= 0; --k) {
             if (PACKED && (emask & (1u << k))) {
@@ -638,7 +652,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
                 if (p.dh_final && valid)
                     v = *reinterpret_cast<const float2*>(
                         p.dh_final +
-                        ((int64_t)seq_of(p.cu, p.nseq, t0 + k) * p.dim + d) * kDState + 2 * pr);
+                        ((int64_t)p.tok_seq[t0 + k] * p.dim + d) * kDState + 2 * pr);
                 G[0] = v.x;
                 G[1] = v.y;
             }
@@ -656,6 +670,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     if (valid) {
         *reinterpret_cast<float2*>(p.g_carry + (row * p.nchunks + c) * kDState + 2 * pr) =
             make_float2(G[0], G[1]);
+        // (packed chunks in which a sequence ends: a partial sum, which the carry ignores)
         if (pr == 0) p.g_sum[row * p.nchunks + c] = dsum;
     }
 }
@@ -713,6 +728,27 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     }
 }
 
+// Packed input: per 16-token tile of the row, the tokens that start a non-empty sequence
+// (bits 0..15) and those that end one (bits 16..31); per token, the sequence holding it
+// (the largest s with cu[s] <= t, so never an empty one). One thread per tile.
+__global__ __launch_bounds__(256) void bwd_tile_events_kernel(const int32_t* __restrict__ cu,
+                                                              int nseq, int64_t L,
+                                                              uint32_t* __restrict__ ev,
+                                                              int32_t* __restrict__ tok_seq) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t0 = i * kT;
+    if (t0 >= L) return;
+    const int nvalid = (L - t0 < kT) ? (int)(L - t0) : kT;
+    uint32_t sm, em;
+    tile_events(cu, nseq, t0, nvalid, &sm, &em);
+    ev[i] = sm | (em << 16);
+    int s = seq_of(cu, nseq, t0);
+    for (int k = 0; k < nvalid; ++k) {
+        while (s + 1 < nseq && (int64_t)cu[s + 1] <= t0 + k) ++s;
+        tok_seq[t0 + k] = s;
+    }
+}
+
 // dh0 of the empty packed sequences: their dh_final (or zero); one thread per (s, d, n)
 __global__ __launch_bounds__(256) void bwd_empty_seq_kernel(const int32_t* __restrict__ cu,
                                                             int nseq, int64_t dim,
@@ -748,6 +784,13 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         case 96: SSM_BWD(KERNEL, float, 48, GRID, P); break;                               \
         case 128: SSM_BWD(KERNEL, float, 64, GRID, P); break;                              \
         default: return hipErrorInvalidValue;                                              \
+    }
+    if (prm.cu) {
+        hipLaunchKernelGGL(bwd_tile_events_kernel,
+                           dim3((unsigned)cdiv(cdiv(prm.seqlen, kT), 256)), dim3(256), 0, stream,
+                           prm.cu, prm.nseq, prm.seqlen, prm.tile_ev, prm.tok_seq);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     if (prm.nchunks > 1) {
         // pass 1: every chunk but the first, from a zero gradient; then the carry from the

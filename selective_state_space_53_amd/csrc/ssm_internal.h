@@ -108,6 +108,9 @@ struct BwdParams {
     const int32_t* cu;
     const float* h0;
     int32_t* chunk_flag;
+    uint32_t* tile_ev;       // [ceil(seqlen/16)]: per 16-token tile, sequence starts (bits
+                             // 0..15) and ends (bits 16..31)
+    int32_t* tok_seq;        // [seqlen]: the sequence holding each token
     int32_t nseq;
     int64_t batch, seqlen, dim, lpad, nckpt, chunk_len;
     int32_t groups_per_batch, nchunks, chunk_offset, softplus, aligned;
