@@ -198,6 +198,26 @@ class Oracle:
                           delta_softplus=delta_softplus, h0=h0, nthreads=nthreads)
         return np.ascontiguousarray(y[:, :, ::-1]), hf
 
+    def scan_reverse_bwd(self, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                         delta_softplus=True, h0=None, dh_final=None, nthreads=1):
+        """Gradients through scan_reverse. That scan is the forward scan of the
+        time-reversed inputs with y reversed back, so its gradients are scan_bwd of the
+        reversed inputs and the reversed dy, with the per-token gradients (dx, ddelta,
+        dz, dB, dC) reversed back. dA, dD, dbias are sums over tokens, and h0 (the state
+        entering at the last token) and h_final (the state after token 0) keep their
+        meaning, so dh0 and dh_final need no relabelling."""
+        rt = lambda v: None if v is None else np.ascontiguousarray(f64(v)[:, :, ::-1])
+        rl = lambda v: np.ascontiguousarray(f64(v)[:, ::-1])
+        g = self.scan_bwd(rt(x), rt(delta), A, rl(B), rl(C), rt(dy), D=D, z=rt(z),
+                          delta_bias=delta_bias, delta_softplus=delta_softplus, h0=h0,
+                          dh_final=dh_final, nthreads=nthreads)
+        for k in ("dx", "ddelta", "dz"):
+            if g[k] is not None:
+                g[k] = np.ascontiguousarray(g[k][:, :, ::-1])
+        g["dB"] = np.ascontiguousarray(g["dB"][:, ::-1])
+        g["dC"] = np.ascontiguousarray(g["dC"][:, ::-1])
+        return g
+
     def scan_varlen_bwd(self, x, delta, A, B, C, dy, cu_seqlens, D=None, z=None,
                         delta_bias=None, delta_softplus=True, h0=None, dh_final=None,
                         nthreads=1):

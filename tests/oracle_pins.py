@@ -734,6 +734,93 @@ def pin_varlen_bwd_equals_batched(orc):
         assert _rel(g[k], gb[k]) < 1e-13, k
 
 
+def _torch_forward_reverse(x, delta, A, B, C, D, z, delta_bias, softplus, h0):
+    """The anti-causal scan written directly in torch fp64 ops: the state runs from
+    h_L = h0 down the tokens, h_t = exp(Delta_t A) h_{t+1} + Delta_t x_t B_t, and y_t is
+    read from h_t (no reversal of arrays anywhere)."""
+    import torch
+    import torch.nn.functional as F
+    b, d, L = x.shape
+    v = delta + (0 if delta_bias is None else delta_bias[None, :, None])
+    dl = torch.logaddexp(v, torch.zeros_like(v)) if softplus else v
+    h = h0 if h0 is not None else torch.zeros((b, d, A.shape[1]), dtype=x.dtype)
+    ys = [None] * L
+    for t in range(L - 1, -1, -1):
+        h = torch.exp(dl[:, :, t, None] * A[None]) * h + \
+            (dl[:, :, t] * x[:, :, t])[..., None] * B[:, None, t, :]
+        s = (C[:, None, t, :] * h).sum(-1)
+        if D is not None:
+            s = s + D[None, :] * x[:, :, t]
+        if z is not None:
+            s = s * F.silu(z[:, :, t])
+        ys[t] = s
+    return torch.stack(ys, dim=-1), h
+
+
+def pin_reverse_bwd_autograd(orc):
+    """Gradients through the anti-causal scan against torch.autograd of the anti-causal
+    forward written directly in torch (loss sum(dy y) + sum(dh_final h_final)), with
+    and without gate, skip, softplus, h0 and dh_final."""
+    import torch
+    p, dy, dhf = _bwd_problem(71, L=21)
+    for use_z, use_D, sp, use_h, use_dhf in [(True, True, True, True, True),
+                                             (False, False, False, False, True),
+                                             (True, False, True, True, False)]:
+        q = dict(p)
+        if not sp:
+            q["delta"] = np.abs(p["delta"]) * 0.3
+            q["delta_bias"] = None
+        names = ["x", "delta", "A", "B", "C"] + (["D"] if use_D else []) + \
+                (["z"] if use_z else []) + (["delta_bias"] if sp else []) + \
+                (["h0"] if use_h else [])
+        tt = {k: torch.tensor(q[k], requires_grad=True) for k in names}
+        y, hf = _torch_forward_reverse(tt["x"], tt["delta"], tt["A"], tt["B"], tt["C"],
+                                       tt.get("D"), tt.get("z"), tt.get("delta_bias"), sp,
+                                       tt.get("h0"))
+        loss = (y * torch.tensor(dy)).sum()
+        if use_dhf:
+            loss = loss + (hf * torch.tensor(dhf)).sum()
+        loss.backward()
+        g = orc.scan_reverse_bwd(q["x"], q["delta"], q["A"], q["B"], q["C"], dy,
+                                 D=q["D"] if use_D else None, z=q["z"] if use_z else None,
+                                 delta_bias=q["delta_bias"] if sp else None,
+                                 delta_softplus=sp, h0=q["h0"] if use_h else None,
+                                 dh_final=dhf if use_dhf else None)
+        pairs = [("dx", "x"), ("ddelta", "delta"), ("dA", "A"), ("dB", "B"), ("dC", "C")]
+        pairs += [("dD", "D")] if use_D else []
+        pairs += [("dz", "z")] if use_z else []
+        pairs += [("dbias", "delta_bias")] if sp else []
+        pairs += [("dh0", "h0")] if use_h else []
+        for gk, tk in pairs:
+            assert _rel(g[gk], tt[tk].grad.numpy()) < 1e-11, (gk, _rel(g[gk], tt[tk].grad.numpy()))
+
+
+def pin_reverse_bwd_finite_differences(orc):
+    """Directional derivatives of the (pinned) anti-causal forward oracle by central
+    differences, for every input, against the reverse gradients."""
+    p, dy, dhf = _bwd_problem(72, batch=2, dim=2, L=15, N=3)
+    rng = np.random.default_rng(73)
+
+    def loss(q):
+        y, hf = orc.scan_reverse(q["x"], q["delta"], q["A"], q["B"], q["C"], D=q["D"],
+                                 z=q["z"], delta_bias=q["delta_bias"], h0=q["h0"])
+        return float(np.sum(y * dy) + np.sum(hf * dhf))
+
+    g = orc.scan_reverse_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dy, D=p["D"],
+                             z=p["z"], delta_bias=p["delta_bias"], h0=p["h0"], dh_final=dhf)
+    for gk, pk in [("dx", "x"), ("ddelta", "delta"), ("dz", "z"), ("dA", "A"), ("dB", "B"),
+                   ("dC", "C"), ("dD", "D"), ("dbias", "delta_bias"), ("dh0", "h0")]:
+        V = rng.standard_normal(p[pk].shape)
+        eps = 1e-6
+        qp = dict(p)
+        qm = dict(p)
+        qp[pk] = p[pk] + eps * V
+        qm[pk] = p[pk] - eps * V
+        fd = (loss(qp) - loss(qm)) / (2 * eps)
+        an = float(np.sum(g[gk] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gk, fd, an)
+
+
 ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response,
             pin_free_decay, pin_brute_force, pin_chunked_equals_unchunked,
             pin_decode_equals_scan, pin_linearity_and_causality, pin_elementwise,
@@ -741,4 +828,5 @@ ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response
             pin_varlen_equals_batched, pin_varlen_isolation, pin_conv_library,
             pin_conv_np_convolve, pin_conv_impulse, pin_conv_state_continuation,
             pin_conv_decode_equals_prefill, pin_bwd_autograd, pin_bwd_finite_differences,
-            pin_bwd_cumsum_closed_form, pin_varlen_bwd_autograd, pin_varlen_bwd_equals_batched]
+            pin_bwd_cumsum_closed_form, pin_varlen_bwd_autograd, pin_varlen_bwd_equals_batched,
+            pin_reverse_bwd_autograd, pin_reverse_bwd_finite_differences]

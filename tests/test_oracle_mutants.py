@@ -130,6 +130,12 @@ PY_MUTANTS = [
     ("varlen_bwd_dA_not_summed", 'out["dA"] += g["dA"]', 'out["dA"] = g["dA"]'),
     ("varlen_bwd_dB_at_row_start", 'out["dB"][a:b] = g["dB"][0]', 'out["dB"][0:b - a] = g["dB"][0]'),
     ("varlen_bwd_B_from_row_start", "Bf[None, a:b, :]", "Bf[None, 0:b - a, :]"),
+    ("reverse_bwd_dy_not_reversed", "rl(C), rt(dy), D=D", "rl(C), f64(dy), D=D"),
+    ("reverse_bwd_dB_not_reversed_back", 'g["dB"] = np.ascontiguousarray(g["dB"][:, ::-1])',
+     'g["dB"] = np.ascontiguousarray(g["dB"])'),
+    ("reverse_bwd_dx_not_reversed_back", 'g[k] = np.ascontiguousarray(g[k][:, :, ::-1])',
+     'g[k] = np.ascontiguousarray(g[k])'),
+    ("reverse_bwd_B_not_reversed", "rt(delta), A, rl(B), rl(C)", "rt(delta), A, f64(B), rl(C)"),
     ("varlen_reverse_ignored", "fn = self.scan_reverse if reverse else self.scan",
      "fn = self.scan"),
     ("conv_taps_reversed", "acc += w[None, :, k, None] * xp[:, :, k:k + L]",
