@@ -101,17 +101,17 @@ typedef struct {
                            before every 16th token and q, the output before the gate --
                            in the layout that starts every backward workspace (see
                            ssm_scan_bwd_workspace_bytes). Allocate the backward's
-                           workspace, pass it here, then to ssm_scan_bwd with saved = 1.
-                           Causal scans only (SSM_ERR_UNSUPPORTED with reverse,
-                           accumulate or packed sequences).                               */
+                           workspace, pass it here, then to ssm_scan_bwd with saved = 1
+                           (and the same reverse). Batch rows without accumulate only
+                           (SSM_ERR_UNSUPPORTED with accumulate or packed sequences).      */
     size_t save_workspace_bytes; /* its size; the forward writes its first
                            S = round_up(batch*dim*ceil(seqlen/16)*64, 256)
                                + batch*dim*seqlen*sizeof(io) bytes and returns
                            SSM_ERR_WORKSPACE_TOO_SMALL when it is smaller than S           */
     int32_t saved;      /* ssm_scan_bwd: 1 = the workspace holds the checkpoints and q
                            written by ssm_scan_fwd (save_workspace = this workspace) for
-                           the same x, delta, A, B, C, D, delta_bias, delta_softplus and
-                           h0, and the backward skips its own forward pass; nothing
+                           the same x, delta, A, B, C, D, delta_bias, delta_softplus, h0
+                           and reverse, and the backward skips its own forward pass; nothing
                            checks that they match (stale contents give wrong gradients).
                            0 = the backward recomputes them.                              */
 } ssm_scan_options;
@@ -181,8 +181,9 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
  *   ddelta_t = (x_t (G_t . B_t) + sum_n G_t h_{t-1} a_t A) * softplus'(v_t)
  *   dA = sum_{b,t} G_t h_{t-1} a_t Delta_t   dD = sum dq_t x_t   ddelta_bias = sum ddelta
  *   dh0 = a_0 G_0
- * The states are recomputed from checkpoints: the state before every 16th token and
- * q, kept at the start of the workspace. Either the call writes them itself (a forward
+ * The states are recomputed from checkpoints: the state entering every 16-token block
+ * in scan order (causal: before its first token; reverse: after the token that follows
+ * it) and q, kept at the start of the workspace. Either the call writes them itself (a forward
  * pass in checkpoint mode; the forward's outputs are not needed), or, with
  * opts->saved = 1, they were written there by the training forward (ssm_scan_fwd with
  * opts->save_workspace = this workspace) and the backward starts from them.
@@ -207,9 +208,12 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
  *                for bf16; SSM_ERR_UNSUPPORTED beyond): the backward addresses the rows of
  *                one workgroup with 32-bit offsets, and picks its channels per workgroup
  *                so that they span less than 4 GiB
- *   opts         as for ssm_scan_fwd (the plan of the checkpoint pass); reverse and
- *                accumulate must be 0 (SSM_ERR_UNSUPPORTED otherwise), save_workspace
- *                NULL; saved as described above
+ *   opts         as for ssm_scan_fwd (the plan of the checkpoint pass); reverse = 1
+ *                gives the gradients of the anti-causal scan (time runs from L-1 down
+ *                to 0, so the adjoint runs from token 0 up, dh_final enters at token 0
+ *                and dh0 = a G at token L-1); accumulate must be 0
+ *                (SSM_ERR_UNSUPPORTED otherwise), save_workspace NULL; saved as
+ *                described above
  * Every output overlaps nothing. Sums over channels and batch rows are finished in a
  * fixed order, so results are deterministic. timing events, when given, bracket the
  * backward kernel itself.

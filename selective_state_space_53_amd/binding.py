@@ -231,12 +231,13 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
 def ssm_scan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=True,
                  h0=None, dh_final=None, want_dh0=False, workspace=None, plan=0, chunk_len=0,
                  stream=None, timing_events=None, group_channels=0, bwd_group_channels=0,
-                 bwd_chunk_len=0, saved=False):
+                 bwd_chunk_len=0, saved=False, reverse=False):
     """Gradients of the forward scan with the same arguments, given dy [batch][dim][L]
     (and dh_final [batch][dim][16]). Returns a dict: dx, ddelta, dz (x's dtype), dA,
     dB, dC, dD, ddelta_bias, dh0 (fp32; None where the input is absent / not asked).
     saved=True: workspace is the save_for_backward tensor of the training forward on
-    the same inputs, and its checkpoint pass is skipped."""
+    the same inputs, and its checkpoint pass is skipped. reverse=True: the gradients of
+    the anti-causal scan (ssm_scan_fwd with reverse=True)."""
     _dev(x, "x")
     io = x.dtype
     batch, dim, seqlen = x.shape
@@ -263,7 +264,7 @@ def ssm_scan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_s
         "dh0": torch.empty((batch, dim, N), **f32) if want_dh0 else None,
     }
     code = _dtype_code(x)
-    opts = _options(plan, chunk_len, timing_events, group_channels,
+    opts = _options(plan, chunk_len, timing_events, group_channels, reverse=reverse,
                     bwd_group_channels=bwd_group_channels, bwd_chunk_len=bwd_chunk_len,
                     saved=saved)
     ws_bytes = lib.ssm_scan_bwd_workspace_bytes(batch, seqlen, dim, N, code, opts)

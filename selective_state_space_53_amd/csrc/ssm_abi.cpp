@@ -327,9 +327,10 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
         return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.saved is an option of ssm_scan_bwd");
     size_t save_q = 0, save_total = 0;
     if (save) {
-        if (packed || opts->reverse || opts->accumulate)
+        if (packed || opts->accumulate)
             return fail(SSM_ERR_UNSUPPORTED,
-                        "save_workspace: causal scans of ssm_scan_fwd without accumulate only");
+                        "save_workspace: scans of ssm_scan_fwd (batch rows) without accumulate "
+                        "only");
         if (!saved_layout(batch, seqlen, dim, io_dtype, &save_q, &save_total))
             return fail(SSM_ERR_INVALID_ARGUMENT, "save_workspace size overflows");
         if (!aligned(save, 16))
@@ -494,9 +495,8 @@ bool choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t elem, i
 
 ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                          ssm_dtype io_dtype, const ssm_scan_options* opts, BwdPlan* bp) {
-    if (opts && (opts->reverse || opts->accumulate))
-        return fail(SSM_ERR_UNSUPPORTED,
-                    "the backward scan supports the causal scan without accumulate only");
+    if (opts && opts->accumulate)
+        return fail(SSM_ERR_UNSUPPORTED, "the backward scan takes no accumulate option");
     if (opts && opts->save_workspace)
         return fail(SSM_ERR_INVALID_ARGUMENT,
                     "ssm_scan_options.save_workspace is an option of ssm_scan_fwd");
@@ -586,6 +586,10 @@ ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void
         if (cu && opts && opts->saved)
             return fail(SSM_ERR_UNSUPPORTED,
                         "ssm_scan_varlen_bwd recomputes its checkpoints (saved must be 0)");
+        if (cu && opts && opts->reverse)
+            return fail(SSM_ERR_UNSUPPORTED,
+                        "ssm_scan_varlen_bwd takes the causal scan only (reverse must be 0)");
+        const int32_t reverse = opts ? opts->reverse : 0;
         struct {
             const char* name;
             const void* p;
@@ -655,6 +659,7 @@ ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void
             bp.fwd.nchunks > 1 ? reinterpret_cast<int32_t*>(fws + bp.fwd.ws_flag) : nullptr;
         fp.cu = cu;
         fp.nseq = (int32_t)nseq;
+        fp.reverse = reverse;
         fp.ckpt = reinterpret_cast<float*>(ws + bp.ws_ckpt);
         fp.nckpt = bp.nckpt;
         fp.batch = batch;
@@ -706,6 +711,7 @@ ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void
         prm.nseq = (int32_t)nseq;
         prm.h0 = h0;
         prm.chunk_flag = reinterpret_cast<int32_t*>(ws + bp.ws_flag);
+        prm.reverse = reverse;
         prm.tile_ev = reinterpret_cast<uint32_t*>(ws + bp.ws_ev);
         prm.tok_seq = reinterpret_cast<int32_t*>(ws + bp.ws_seq);
         prm.chunk_len = bp.chunk_len;
@@ -786,6 +792,9 @@ ssm_status ssm_scan_varlen_bwd(const void* x, const void* delta, const float* A,
         if (total < 0 || total >= (int64_t(1) << 31))
             return fail(SSM_ERR_INVALID_ARGUMENT, "total=%lld must be in [0, 2^31)",
                         (long long)total);
+        if (opts && opts->reverse)
+            return fail(SSM_ERR_UNSUPPORTED,
+                        "ssm_scan_varlen_bwd takes the causal scan only (reverse must be 0)");
         if (total > 0)
             return bwd_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, cu_seqlens,
                             nseq, dy, dh_final, dx, ddelta, dz, dA, dB, dC, dD, ddelta_bias,

@@ -218,9 +218,10 @@ __device__ __forceinline__ void bwd_event_tile(
     }
 }
 
-template <typename IO, int CG, bool PACKED>
+template <typename IO, int CG, bool PACKED, bool REV>
 __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
+    static_assert(!(PACKED && REV), "the anti-causal backward takes batch rows");
     constexpr int kRowsPerPair = CG / 16;
     constexpr int kLaneRows = CG / 2;           // 16-lane rows in the workgroup
     __shared__ float sD[CG * kRowF];            // Delta
@@ -342,13 +343,13 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     rz.zero();
     rg.zero();
     rq.zero();
-    load_tile(ntiles - 1);
+    load_tile(REV ? 0 : ntiles - 1);
 
     if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
 
     float dDacc = 0.0f, dbacc = 0.0f;
     for (int it = 0; it < ntiles; ++it) {
-        const int ti = ntiles - 1 - it;
+        const int ti = REV ? it : ntiles - 1 - it;   // the adjoint runs against the scan
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
@@ -361,9 +362,11 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         rz.widen(zv);
         rg.widen(gv);
         rq.widen(qv);
-        const float hs0 = rck.x, hs1 = rck.y;   // the state before the tile's first token
+        // the state entering the tile in scan order (causal: before its first token; REV:
+        // after the token that follows it)
+        const float hs0 = rck.x, hs1 = rck.y;
         const uint32_t ev = rev;
-        if (it + 1 < ntiles) load_tile(ti - 1);
+        if (it + 1 < ntiles) load_tile(REV ? ti + 1 : ti - 1);
         float dl[2], sg[2], dqv[2], uu[2], dzv[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -394,17 +397,20 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             bwd_event_tile<CG>(p, t0, d, valid, pr, cc, lane16, smask, emask, a2, Ar, hs0, hs1,
                                cD, cU, cQ, bct, p1, p2, red, hs, Gc, dA);
         } else {
-        // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint
+        // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint,
+        // in scan order
         {
             float h0 = hs0, h1 = hs1;
 #pragma unroll
-            for (int g4 = 0; g4 < kT; g4 += 4) {
+            for (int gi = 0; gi < kT / 4; ++gi) {
+                const int g4 = REV ? kT - 4 - 4 * gi : 4 * gi;
                 const float4 D4 = *reinterpret_cast<const float4*>(cD + g4);
                 const float4 U4 = *reinterpret_cast<const float4*>(cU + g4);
                 const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
                 const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = REV ? 3 - jj : jj;
                     const int k = g4 + j;
                     const float2 bb = *reinterpret_cast<const float2*>(bct + k * 4);
                     h0 = __builtin_fmaf(fast_exp2(Ds[j] * a2[0]), h0, bb.x * Us[j]);
@@ -415,9 +421,11 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             }
         }
 
-        // ---- bwd: the adjoint recurrence over the tile, last token first
+        // ---- bwd: the adjoint recurrence over the tile, against the scan order (causal:
+        // last token first)
 #pragma unroll
-        for (int g4 = kT - 4; g4 >= 0; g4 -= 4) {
+        for (int gi = 0; gi < kT / 4; ++gi) {
+            const int g4 = REV ? 4 * gi : kT - 4 - 4 * gi;
             const float4 D4 = *reinterpret_cast<const float4*>(cD + g4);
             const float4 U4 = *reinterpret_cast<const float4*>(cU + g4);
             const float4 Q4 = *reinterpret_cast<const float4*>(cQ + g4);
@@ -426,15 +434,20 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             const float Qs[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
             float o1[4], o2[4];
 #pragma unroll
-            for (int j = 3; j >= 0; --j) {
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = REV ? jj : 3 - jj;
                 const int k = g4 + j;
                 const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
                 const float e0 = fast_exp2(Ds[j] * a2[0]);
                 const float e1 = fast_exp2(Ds[j] * a2[1]);
                 const float G0 = __builtin_fmaf(Qs[j], q.z, Gc[0]);
                 const float G1 = __builtin_fmaf(Qs[j], q.w, Gc[1]);
-                const float hp0 = k > 0 ? hs[k > 0 ? k - 1 : 0][0] : hs0;
-                const float hp1 = k > 0 ? hs[k > 0 ? k - 1 : 0][1] : hs1;
+                // the state before token k in scan order
+                constexpr int kLast = kT - 1;
+                const float hp0 = REV ? (k < kLast ? hs[k < kLast ? k + 1 : kLast][0] : hs0)
+                                      : (k > 0 ? hs[k > 0 ? k - 1 : 0][0] : hs0);
+                const float hp1 = REV ? (k < kLast ? hs[k < kLast ? k + 1 : kLast][1] : hs1)
+                                      : (k > 0 ? hs[k > 0 ? k - 1 : 0][1] : hs1);
                 o1[j] = __builtin_fmaf(G1, q.y, G0 * q.x);          // G.B
                 const float w0 = G0 * hp0 * e0;
                 const float w1 = G1 * hp1 * e1;
@@ -510,10 +523,11 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcT) = rbc;
     }
 
-    // ---- per-row results: dh0 = a_0 G_0 (the carry after token 0), dA partials
+    // ---- per-row results: dh0 = a G at the last token of the scan (the carry after it:
+    // causal token 0, REV token L-1), dA partials
     const int64_t prow = (b * p.nchunks + c) * p.dim;   // partials of (batch row, chunk)
     if (valid) {
-        if (!PACKED && p.dh0 && c == 0)
+        if (!PACKED && p.dh0 && c == (REV ? p.nchunks - 1 : 0))
             *reinterpret_cast<float2*>(p.dh0 + row * kDState + 2 * pr) = make_float2(Gc[0], Gc[1]);
         *reinterpret_cast<float2*>(p.part_A + (prow + d) * kDState + 2 * pr) =
             make_float2(dA[0], dA[1]);
@@ -531,14 +545,17 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     }
 }
 
-// Pass 1 of the chunked backward: for every chunk but the first, the gradient the chunk
-// passes to the token before it when nothing reaches it from later tokens,
-//   G_loc = sum over its tokens t of (prod_{r from its first token to t} a_r) dq_t C_t,
+// Pass 1 of the chunked backward: for every chunk but the first in the adjoint's order
+// (causal: the last chunk; REV: the first), the gradient the chunk passes on to the
+// next token in that order when nothing reaches it from the other side,
+//   G_loc = sum over its tokens t of (prod of a_r over the tokens from t to the chunk's
+//           edge) dq_t C_t,
 // and its sum of Delta (the decay of a gradient crossing the whole chunk is
 // exp(A sum Delta)). The same mapping and tiles as the full kernel, only the G chain.
-template <typename IO, int CG, bool PACKED>
+template <typename IO, int CG, bool PACKED, bool REV>
 __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
+    static_assert(!(PACKED && REV), "the anti-causal backward takes batch rows");
     constexpr int kRowsPerPair = CG / 16;
     __shared__ float sD[CG * kRowF];
     __shared__ float sQ[CG * kRowF];
@@ -616,9 +633,9 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
                 p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + t0 + (tid & 15)) * 4);
         if (PACKED) rev = p.tile_ev[t0 / kT];
     };
-    load_tile(ntiles - 1);
+    load_tile(REV ? 0 : ntiles - 1);
     for (int it = 0; it < ntiles; ++it) {
-        const int ti = ntiles - 1 - it;
+        const int ti = REV ? it : ntiles - 1 - it;
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
@@ -628,7 +645,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         rg.widen(gv);
         const float4 cv4 = rc;
         const uint32_t emask = PACKED ? (rev >> 16) : 0u;
-        if (it + 1 < ntiles) load_tile(ti - 1);
+        if (it + 1 < ntiles) load_tile(REV ? ti + 1 : ti - 1);
         // C of the tile, per state pair: threads 0..127 move (pair, token)
         if (tid < 128) *reinterpret_cast<float2*>(sC + tid * 2) = make_float2(cv4.z, cv4.w);
         float dl[2], dqv[2];
@@ -646,7 +663,8 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         // packed: at the last token of a sequence the gradient restarts from its dh_final,
         // so the chunk's end value no longer depends on what later chunks carry in
 #pragma unroll
-        for (int k = kT - 1; k >= 0; --k) {
+        for (int kk = 0; kk < kT; ++kk) {
+            const int k = REV ? kk : kT - 1 - kk;
             if (PACKED && (emask & (1u << k))) {
                 float2 v = make_float2(0.f, 0.f);
                 if (p.dh_final && valid)
@@ -772,9 +790,11 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
     hipError_t e;
 #define SSM_BWD(KERNEL, IO, N, GRID, P)                                                    \
     if (P.cu)                                                                              \
-        hipLaunchKernelGGL((KERNEL<IO, N, true>), GRID, dim3(N * 8), 0, stream, P);        \
+        hipLaunchKernelGGL((KERNEL<IO, N, true, false>), GRID, dim3(N * 8), 0, stream, P); \
+    else if (P.reverse)                                                                    \
+        hipLaunchKernelGGL((KERNEL<IO, N, false, true>), GRID, dim3(N * 8), 0, stream, P); \
     else                                                                                   \
-        hipLaunchKernelGGL((KERNEL<IO, N, false>), GRID, dim3(N * 8), 0, stream, P)
+        hipLaunchKernelGGL((KERNEL<IO, N, false, false>), GRID, dim3(N * 8), 0, stream, P)
 #define SSM_BWD_ALL(KERNEL, GRID, P)                                                       \
     switch (cg * 2 + (bf16 ? 1 : 0)) {                                                     \
         case 65: SSM_BWD(KERNEL, uint16_t, 32, GRID, P); break;                            \
@@ -793,10 +813,11 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         if (e != hipSuccess) return e;
     }
     if (prm.nchunks > 1) {
-        // pass 1: every chunk but the first, from a zero gradient; then the carry from the
-        // last chunk backwards, starting from dh_final
+        // pass 1: every chunk but the first in the adjoint's order, from a zero gradient;
+        // then the carry in that order (causal: from the last chunk backwards), starting
+        // from dh_final
         BwdParams p1 = prm;
-        p1.chunk_offset = 1;
+        p1.chunk_offset = prm.reverse ? 0 : 1;
         const dim3 g1((unsigned)(ngroups * (prm.nchunks - 1)));
         SSM_BWD_ALL(scan_bwd_local_kernel, g1, p1)
         e = hipGetLastError();
@@ -805,7 +826,7 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         // sequence ends inside it; the last tokens of sequences bring in dh_final)
         e = launch_carry(prm.A, prm.cu ? nullptr : prm.dh_final, prm.g_carry, prm.g_sum,
                          prm.cu ? prm.chunk_flag : nullptr, prm.batch * prm.dim, prm.dim,
-                         prm.nchunks, 1, stream);
+                         prm.nchunks, prm.reverse ? 0 : 1, stream);
         if (e != hipSuccess) return e;
     }
     if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipGetLastError();

@@ -114,6 +114,7 @@ struct BwdParams {
     int32_t nseq;
     int64_t batch, seqlen, dim, lpad, nckpt, chunk_len;
     int32_t groups_per_batch, nchunks, chunk_offset, softplus, aligned;
+    int32_t reverse;         // 1: the backward of the anti-causal scan (batch rows)
 };
 
 // ev_begin / ev_end (may be null) are recorded around the launch of the scan kernel

@@ -164,8 +164,10 @@ constexpr int kBcTile = 8 * kTile * 4;    // floats of widened B/C per tile (8 s
 // REV = anti-causal: tiles, and tokens inside a tile, are taken from the last to the
 // first; the tiles stay where they are in memory, so loads and stores are the same.
 // CKPT = a forward that keeps what the backward needs: as the last pass, and it also
-// stores the state before every 16th token (the backward recomputes its tiles from
-// them) and, when p.q is set, the output before the gate.
+// stores, for every 16-token block of the row, the state entering the block in scan
+// order (causal: the state before its first token; REV: the state after the token
+// that follows it) -- the backward recomputes its tiles from them -- and, when p.q is
+// set, the output before the gate.
 // PACKED = packed sequences (p.cu set): the state is reset to the sequence's initial state
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
@@ -173,7 +175,8 @@ constexpr int kBcTile = 8 * kTile * 4;    // floats of widened B/C per tile (8 s
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
-    static_assert(!CKPT || (!LOCAL && !REV), "checkpoints: causal, final pass");
+    static_assert(!CKPT || !LOCAL, "checkpoints: final pass");
+    static_assert(!CKPT || !(REV && PACKED), "checkpoints: causal packed, or batch rows");
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
     __shared__ float sD[CG * kLdsRow];
@@ -374,8 +377,13 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         const bool quiet = !packed || (REV ? (hi - 1 != tlast && lo < t0)
                                            : (lo != t0 && hi > tlast + 1));
         if (quiet) {
-            if (CKPT && valid)
-                *reinterpret_cast<float2*>(ck + (t0 / 16) * kDState) = make_float2(h[0], h[1]);
+            // CKPT: the state entering each 16-token block of the tile, in scan order
+            // (a block past the end of the row has none)
+            auto checkpoint = [&](int64_t blk) {
+                if (CKPT && valid && blk * 16 < p.seqlen)
+                    *reinterpret_cast<float2*>(ck + blk * kDState) = make_float2(h[0], h[1]);
+            };
+            checkpoint(REV ? t0 / 16 + 1 : t0 / 16);
             // the LDS operands of 4 tokens, read one group ahead of their use
             float4 nD, nU, n0, n1, n2, n3;
             auto fetch = [&](int tq) {
@@ -390,9 +398,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
 #pragma unroll
             for (int gq = 0; gq < kTile; gq += 4) {
                 const int tq = REV ? kTile - 4 - gq : gq;
-                if (CKPT && gq == 16 && valid && t0 + 16 < p.seqlen)
-                    *reinterpret_cast<float2*>(ck + (t0 / 16 + 1) * kDState) =
-                        make_float2(h[0], h[1]);
+                if (gq == 16) checkpoint(REV ? t0 / 16 : t0 / 16 + 1);
                 const float4 D4 = nD, U4 = nU, q0 = n0, q1 = n1, q2 = n2, q3 = n3;
                 if (gq + 4 < kTile) fetch(REV ? kTile - 8 - gq : gq + 4);
                 __builtin_amdgcn_sched_barrier(0);
@@ -624,9 +630,12 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
 
 template <typename IO, bool LOCAL>
 hipError_t launch_scan_dir(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
-    if (!LOCAL && prm.ckpt)
-        return prm.cu ? launch_scan_kernel<IO, false, false, true, true>(cg, grid, stream, prm)
-                      : launch_scan_kernel<IO, false, false, false, true>(cg, grid, stream, prm);
+    if (!LOCAL && prm.ckpt) {   // (packed input: causal only; the host checks)
+        if (prm.cu) return launch_scan_kernel<IO, false, false, true, true>(cg, grid, stream, prm);
+        return prm.reverse
+                   ? launch_scan_kernel<IO, false, true, false, true>(cg, grid, stream, prm)
+                   : launch_scan_kernel<IO, false, false, false, true>(cg, grid, stream, prm);
+    }
     if (prm.cu)
         return prm.reverse
                    ? launch_scan_kernel<IO, LOCAL, true, true, false>(cg, grid, stream, prm)

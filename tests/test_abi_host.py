@@ -219,7 +219,7 @@ def test_bwd_workspace_and_rejects(b):
     assert call(dB=p["dC"]) == 1               # outputs overlap each other
     assert call(dx=P["y"] + 8) == 2            # misaligned
     assert call(ws=None) == 3
-    opts = b.ScanOptions(0, 0, 0, None, None, 1, 0, 0, 0)
+    opts = b.ScanOptions(0, 0, 0, None, None, 0, 1, 0, 0)   # accumulate: no backward
     q = dict(p)
     assert b.lib.ssm_scan_bwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"],
                               q["bias"], 1, q["h0"], q["dy"], None, q["dx"], q["dd"], q["dz"],
@@ -241,7 +241,8 @@ def test_training_forward_save_rejects(b):
     # one byte fewer than the header's formula is refused (every call here fails a check
     # before any launch: the addresses are not real)
     assert scan(b, opts=_save_opts(b, sv, need - 1)) == 3
-    assert scan(b, opts=_save_opts(b, sv, need, reverse=1)) == 2
+    # the anti-causal scan saves too, the same bytes (one byte short is refused)
+    assert scan(b, opts=_save_opts(b, sv, need - 1, reverse=1)) == 3
     assert scan(b, opts=_save_opts(b, sv, need, accumulate=1)) == 2
     assert scan(b, opts=_save_opts(b, sv + 8, need)) == 2             # misaligned
     assert scan(b, opts=_save_opts(b, P["x"], need)) == 1             # overlaps an input
@@ -325,3 +326,11 @@ def test_varlen_bwd_workspace_and_options(b):
     assert varlen_bwd(b, opts=_save_opts(b, None, 0, saved=1)) == 2
     assert varlen_bwd(b, opts=_save_opts(b, None, 0, reverse=1)) == 2
     assert varlen_bwd(b, opts=_save_opts(b, 0x7d0000000000, 1 << 30)) == 1
+
+
+def test_reverse_backward_workspace(b):
+    """The anti-causal backward uses the causal backward's workspace layout and size."""
+    rev = ctypes.byref(b.ScanOptions(0, 0, 0, None, None, 1, 0, 0, 0))
+    for L in (100, 4103):
+        assert (b.lib.ssm_scan_bwd_workspace_bytes(2, L, 64, 16, 1, rev)
+                == b.ssm_scan_bwd_workspace_bytes(2, L, 64, 16, 1) > 0)
