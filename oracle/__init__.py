@@ -220,9 +220,10 @@ class Oracle:
 
     def scan_varlen_bwd(self, x, delta, A, B, C, dy, cu_seqlens, D=None, z=None,
                         delta_bias=None, delta_softplus=True, h0=None, dh_final=None,
-                        nthreads=1):
-        """Gradients through scan_varlen (causal): every sequence is its own scan, so its
-        gradients are scan_bwd of that sequence alone (with its h0 and dh_final); the
+                        reverse=False, nthreads=1):
+        """Gradients through scan_varlen: every sequence is its own scan, so its
+        gradients are scan_bwd (reverse: scan_reverse_bwd) of that sequence alone (with
+        its h0 and dh_final); the
         per-token gradients (dx, ddelta, dz [dim][total], dB, dC [total][N]) are placed
         at its tokens, the per-channel ones (dA, dD, dbias) summed over sequences, and
         dh0 [nseq][dim][N] is per sequence (an empty sequence passes dh_final through:
@@ -247,11 +248,12 @@ class Oracle:
             if b == a:
                 out["dh0"][i] = 0.0 if dhf is None else dhf[i]
                 continue
-            g = self.scan_bwd(x[None, :, a:b], dl[None, :, a:b], A, Bf[None, a:b, :], Cf[None, a:b, :],
-                              dyf[None, :, a:b], D=D, z=None if zf is None else zf[None, :, a:b],
-                              delta_bias=delta_bias, delta_softplus=delta_softplus,
-                              h0=None if h0f is None else h0f[i][None],
-                              dh_final=None if dhf is None else dhf[i][None], nthreads=nthreads)
+            fn = self.scan_reverse_bwd if reverse else self.scan_bwd
+            g = fn(x[None, :, a:b], dl[None, :, a:b], A, Bf[None, a:b, :], Cf[None, a:b, :],
+                   dyf[None, :, a:b], D=D, z=None if zf is None else zf[None, :, a:b],
+                   delta_bias=delta_bias, delta_softplus=delta_softplus,
+                   h0=None if h0f is None else h0f[i][None],
+                   dh_final=None if dhf is None else dhf[i][None], nthreads=nthreads)
             for k in ("dx", "ddelta") + (("dz",) if z is not None else ()):
                 out[k][:, a:b] = g[k][0]
             out["dB"][a:b] = g["dB"][0]

@@ -711,6 +711,44 @@ def pin_varlen_bwd_autograd(orc):
     assert _rel(g["dh0"], th0.grad.numpy()) < 1e-11
 
 
+def pin_varlen_reverse_bwd_autograd(orc):
+    """Packed gradients of the anti-causal scan against torch.autograd of the packed
+    anti-causal forward written in torch ops (each sequence through the direct
+    anti-causal torch forward from its own h0), with empty and one-token sequences."""
+    import torch
+    lens = [5, 0, 1, 9, 0, 3]
+    p, cu, h0 = _packed_problem(65, lens, dim=3, N=4)
+    rng = np.random.default_rng(66)
+    dim, total = p["x"].shape
+    dy = rng.standard_normal((dim, total))
+    dhf = rng.standard_normal((len(lens), dim, 4))
+    names = ["x", "delta", "A", "B", "C", "D", "z", "delta_bias"]
+    tt = {k: torch.tensor(p[k], requires_grad=True) for k in names}
+    th0 = torch.tensor(h0, requires_grad=True)
+    ys, hfs = [], []
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if a == b:
+            hfs.append(th0[i])
+            continue
+        y, hf = _torch_forward_reverse(tt["x"][None, :, a:b], tt["delta"][None, :, a:b],
+                                       tt["A"], tt["B"][None, a:b], tt["C"][None, a:b],
+                                       tt["D"], tt["z"][None, :, a:b], tt["delta_bias"], True,
+                                       th0[i][None])
+        ys.append(y[0])
+        hfs.append(hf[0])
+    loss = (torch.cat(ys, dim=1) * torch.tensor(dy)).sum() + \
+        (torch.stack(hfs) * torch.tensor(dhf)).sum()
+    loss.backward()
+    g = orc.scan_varlen_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dy, cu, D=p["D"],
+                            z=p["z"], delta_bias=p["delta_bias"], h0=h0, dh_final=dhf,
+                            reverse=True)
+    for gk, tk in [("dx", "x"), ("ddelta", "delta"), ("dA", "A"), ("dB", "B"), ("dC", "C"),
+                   ("dD", "D"), ("dz", "z"), ("dbias", "delta_bias")]:
+        assert _rel(g[gk], tt[tk].grad.numpy()) < 1e-11, gk
+    assert _rel(g["dh0"], th0.grad.numpy()) < 1e-11
+
+
 def pin_varlen_bwd_equals_batched(orc):
     """Equal lengths: the packed gradients are the batch gradients, relayouted."""
     batch, L = 3, 13
@@ -829,4 +867,5 @@ ALL_PINS = [pin_hand_example, pin_cumsum, pin_lti_convolution, pin_step_response
             pin_conv_np_convolve, pin_conv_impulse, pin_conv_state_continuation,
             pin_conv_decode_equals_prefill, pin_bwd_autograd, pin_bwd_finite_differences,
             pin_bwd_cumsum_closed_form, pin_varlen_bwd_autograd, pin_varlen_bwd_equals_batched,
-            pin_reverse_bwd_autograd, pin_reverse_bwd_finite_differences]
+            pin_reverse_bwd_autograd, pin_reverse_bwd_finite_differences,
+            pin_varlen_reverse_bwd_autograd]

@@ -136,6 +136,8 @@ PY_MUTANTS = [
     ("reverse_bwd_dx_not_reversed_back", 'g[k] = np.ascontiguousarray(g[k][:, :, ::-1])',
      'g[k] = np.ascontiguousarray(g[k])'),
     ("reverse_bwd_B_not_reversed", "rt(delta), A, rl(B), rl(C)", "rt(delta), A, f64(B), rl(C)"),
+    ("varlen_bwd_reverse_ignored", "fn = self.scan_reverse_bwd if reverse else self.scan_bwd",
+     "fn = self.scan_bwd"),
     ("varlen_reverse_ignored", "fn = self.scan_reverse if reverse else self.scan",
      "fn = self.scan"),
     ("conv_taps_reversed", "acc += w[None, :, k, None] * xp[:, :, k:k + L]",
