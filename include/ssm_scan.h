@@ -267,11 +267,12 @@ ssm_status ssm_scan_varlen_fwd(const void* x, const void* delta, const float* A,
                                void* stream);
 
 /*
- * The backward of ssm_scan_varlen_fwd (causal): the gradients of ssm_scan_bwd, taken
- * per packed sequence. Inside a sequence the recurrence and its adjoint are those of
- * ssm_scan_bwd; at a boundary nothing crosses: the adjoint entering the last token of
- * sequence i is dh_final[i] (not what its successor carries back), and the state
- * before the first token of sequence i is h0[i], so dh0[i] = a G at that first token.
+ * The backward of ssm_scan_varlen_fwd: the gradients of ssm_scan_bwd, taken per packed
+ * sequence, in either direction (opts->reverse as for ssm_scan_varlen_fwd). Inside a
+ * sequence the recurrence and its adjoint are those of ssm_scan_bwd; at a boundary
+ * nothing crosses: the adjoint entering the sequence's last token in scan order is
+ * dh_final[i] (not what the neighbouring sequence carries back), and the state before
+ * its first token in scan order is h0[i], so dh0[i] = a G at that token.
  * An empty sequence passes dh_final[i] to dh0[i] unchanged. dA, dD and ddelta_bias sum
  * over every token of every sequence.
  *
@@ -284,8 +285,8 @@ ssm_status ssm_scan_varlen_fwd(const void* x, const void* delta, const float* A,
  *   h0, dh_final                      [nseq][dim][dstate] fp32 or NULL (zero)
  *   dh0                               [nseq][dim][dstate] fp32 out or NULL
  *   A, D, delta_bias, delta_softplus, dA, dD, ddelta_bias   as for ssm_scan_bwd
- *   opts                              as for ssm_scan_bwd; saved must be 0 (the call
- *                                     recomputes its checkpoints)
+ *   opts                              as for ssm_scan_bwd (reverse included); saved
+ *                                     must be 0 (the call recomputes its checkpoints)
  * total >= 0 (0: dh0 = dh_final, and dA, dD, ddelta_bias are zero), nseq >= 1,
  * dim >= 1, dstate == 16. The workspace is ssm_scan_varlen_bwd_workspace_bytes(...)
  * bytes (0 when total == 0), laid out as for ssm_scan_bwd with batch = 1 and

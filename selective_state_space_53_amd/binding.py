@@ -343,8 +343,9 @@ def ssm_scan_varlen_bwd_workspace_bytes(total, dim, dstate, io_dtype, plan=0, ch
 def ssm_scan_varlen_bwd(x, delta, A, B, C, dy, cu_seqlens, D=None, z=None, delta_bias=None,
                         delta_softplus=True, h0=None, dh_final=None, want_dh0=False,
                         workspace=None, plan=0, chunk_len=0, stream=None, timing_events=None,
-                        group_channels=0, bwd_group_channels=0, bwd_chunk_len=0):
-    """Gradients of ssm_scan_varlen_fwd (causal). x, delta, z, dy: [dim][total];
+                        group_channels=0, bwd_group_channels=0, bwd_chunk_len=0, reverse=False):
+    """Gradients of ssm_scan_varlen_fwd (reverse=True: of its anti-causal scan).
+    x, delta, z, dy: [dim][total];
     B, C: [total][16]; cu_seqlens: int32 [nseq+1] on the device; h0, dh_final:
     [nseq][dim][16]. Returns a dict like ssm_scan_bwd's (dB, dC [total][16]; dh0
     [nseq][dim][16])."""
@@ -378,7 +379,7 @@ def ssm_scan_varlen_bwd(x, delta, A, B, C, dy, cu_seqlens, D=None, z=None, delta
         "dh0": torch.empty((nseq, dim, N), **f32) if want_dh0 else None,
     }
     code = _dtype_code(x)
-    opts = _options(plan, chunk_len, timing_events, group_channels,
+    opts = _options(plan, chunk_len, timing_events, group_channels, reverse=reverse,
                     bwd_group_channels=bwd_group_channels, bwd_chunk_len=bwd_chunk_len)
     ws_bytes = lib.ssm_scan_varlen_bwd_workspace_bytes(total, dim, N, code, opts)
     if workspace is None and ws_bytes > 0:

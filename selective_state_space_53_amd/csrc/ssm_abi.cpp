@@ -586,9 +586,6 @@ ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void
         if (cu && opts && opts->saved)
             return fail(SSM_ERR_UNSUPPORTED,
                         "ssm_scan_varlen_bwd recomputes its checkpoints (saved must be 0)");
-        if (cu && opts && opts->reverse)
-            return fail(SSM_ERR_UNSUPPORTED,
-                        "ssm_scan_varlen_bwd takes the causal scan only (reverse must be 0)");
         const int32_t reverse = opts ? opts->reverse : 0;
         struct {
             const char* name;
@@ -792,9 +789,6 @@ ssm_status ssm_scan_varlen_bwd(const void* x, const void* delta, const float* A,
         if (total < 0 || total >= (int64_t(1) << 31))
             return fail(SSM_ERR_INVALID_ARGUMENT, "total=%lld must be in [0, 2^31)",
                         (long long)total);
-        if (opts && opts->reverse)
-            return fail(SSM_ERR_UNSUPPORTED,
-                        "ssm_scan_varlen_bwd takes the causal scan only (reverse must be 0)");
         if (total > 0)
             return bwd_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, cu_seqlens,
                             nseq, dy, dh_final, dx, ddelta, dz, dA, dB, dC, dD, ddelta_bias,

@@ -138,18 +138,21 @@ __device__ __forceinline__ void tile_events(const int32_t* cu, int nseq, int64_t
     *emask = em;
 }
 
-// A tile of packed input with sequence boundaries in it, token by token: the recompute
-// restarts from h0[s] at the first token of sequence s; going backwards, the gradient
-// entering the last token of s is dh_final[s] (not what later tokens carried), the state
-// before the first token is h0[s], and after it dh0[s] = a G is written. Otherwise the
-// same arithmetic as the quiet path, in the same order per token.
-template <int CG>
+// A tile of packed input with sequence boundaries in it, token by token. In scan order
+// (REV: from a sequence's last token to its first) the recompute restarts from h0[s] at
+// the first token of sequence s; the adjoint, which runs against the scan order, enters
+// the last token of s as dh_final[s] (not what the neighbouring sequence carried), takes
+// h0[s] as the state before the first token, and writes dh0[s] = a G after it. Otherwise
+// the same arithmetic as the quiet path, in the same order per token.
+template <int CG, bool REV>
 __device__ __forceinline__ void bwd_event_tile(
     const BwdParams& p, int64_t t0, int64_t d, bool valid, int pr, int cc, int lane16,
     uint32_t smask, uint32_t emask, const float* a2, const float* Ar, float hs0, float hs1,
     const float* cD, const float* cU, const float* cQ, const float* bct, float* p1, float* p2,
     float* red, float (&hs)[kT][2], float* Gc, float* dA) {
     constexpr int kLaneRows = CG / 2;
+    // the first and last tokens of sequences in scan order
+    const uint32_t fmask = REV ? emask : smask, lmask = REV ? smask : emask;
     auto seq_state = [&](const float* base, int s) {   // base[s][d][2pr..2pr+1] or zeros
         float2 v = make_float2(0.f, 0.f);
         if (base && valid)
@@ -159,8 +162,9 @@ __device__ __forceinline__ void bwd_event_tile(
     {
         float h0 = hs0, h1 = hs1;
 #pragma unroll
-        for (int k = 0; k < kT; ++k) {
-            if (smask & (1u << k)) {
+        for (int kk = 0; kk < kT; ++kk) {
+            const int k = REV ? kT - 1 - kk : kk;
+            if (fmask & (1u << k)) {
                 const float2 v = seq_state(p.h0, p.tok_seq[t0 + k]);
                 h0 = v.x;
                 h1 = v.y;
@@ -174,8 +178,9 @@ __device__ __forceinline__ void bwd_event_tile(
         }
     }
 #pragma unroll
-    for (int k = kT - 1; k >= 0; --k) {
-        if (emask & (1u << k)) {
+    for (int kk = 0; kk < kT; ++kk) {
+        const int k = REV ? kk : kT - 1 - kk;
+        if (lmask & (1u << k)) {
             const float2 v = seq_state(p.dh_final, p.tok_seq[t0 + k]);
             Gc[0] = v.x;
             Gc[1] = v.y;
@@ -186,9 +191,13 @@ __device__ __forceinline__ void bwd_event_tile(
         const float e1 = fast_exp2(Dk * a2[1]);
         const float G0 = __builtin_fmaf(Qk, q.z, Gc[0]);
         const float G1 = __builtin_fmaf(Qk, q.w, Gc[1]);
-        float hp0 = k > 0 ? hs[k > 0 ? k - 1 : 0][0] : hs0;
-        float hp1 = k > 0 ? hs[k > 0 ? k - 1 : 0][1] : hs1;
-        const bool first = (smask & (1u << k)) != 0;
+        // the state before token k in scan order
+        constexpr int kLast = kT - 1;
+        float hp0 = REV ? (k < kLast ? hs[k < kLast ? k + 1 : kLast][0] : hs0)
+                        : (k > 0 ? hs[k > 0 ? k - 1 : 0][0] : hs0);
+        float hp1 = REV ? (k < kLast ? hs[k < kLast ? k + 1 : kLast][1] : hs1)
+                        : (k > 0 ? hs[k > 0 ? k - 1 : 0][1] : hs1);
+        const bool first = (fmask & (1u << k)) != 0;
         int s = 0;
         if (first) {
             s = p.tok_seq[t0 + k];
@@ -221,7 +230,6 @@ __device__ __forceinline__ void bwd_event_tile(
 template <typename IO, int CG, bool PACKED, bool REV>
 __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
-    static_assert(!(PACKED && REV), "the anti-causal backward takes batch rows");
     constexpr int kRowsPerPair = CG / 16;
     constexpr int kLaneRows = CG / 2;           // 16-lane rows in the workgroup
     __shared__ float sD[CG * kRowF];            // Delta
@@ -394,8 +402,8 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         float hs[kT][2];
         // (tiles with events are the rare case: laid out away from the quiet path)
         if (__builtin_expect(PACKED && (smask | emask) != 0, 0)) {
-            bwd_event_tile<CG>(p, t0, d, valid, pr, cc, lane16, smask, emask, a2, Ar, hs0, hs1,
-                               cD, cU, cQ, bct, p1, p2, red, hs, Gc, dA);
+            bwd_event_tile<CG, REV>(p, t0, d, valid, pr, cc, lane16, smask, emask, a2, Ar, hs0,
+                                    hs1, cD, cU, cQ, bct, p1, p2, red, hs, Gc, dA);
         } else {
         // ---- fwd: recompute the 16 states of (channel cc, pair pr) from the checkpoint,
         // in scan order
@@ -555,7 +563,6 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
 template <typename IO, int CG, bool PACKED, bool REV>
 __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
-    static_assert(!(PACKED && REV), "the anti-causal backward takes batch rows");
     constexpr int kRowsPerPair = CG / 16;
     __shared__ float sD[CG * kRowF];
     __shared__ float sQ[CG * kRowF];
@@ -570,16 +577,28 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     const int64_t L = p.seqlen;
     const int64_t t_beg = (int64_t)c * p.chunk_len;
     const int64_t t_end = (t_beg + p.chunk_len < L) ? t_beg + p.chunk_len : L;
-    int ntiles = (int)((t_end - t_beg + kT - 1) / kT);
-    // packed: once the chain (walked from the chunk's end) reaches the last token of the
-    // sequence holding the chunk's first token, it restarts from that sequence's dh_final;
-    // nothing after that token can reach the chunk's first token, so start there
-    bool ended = false;   // a sequence ends inside the chunk
+    const int ntiles = (int)((t_end - t_beg + kT - 1) / kT);
+    // packed: the chain restarts from a sequence's dh_final at the sequence's last token
+    // in scan order (causal: its last token; REV: its first). Walking against the scan,
+    // once the chain reaches such a token of the sequence holding the chunk's far edge
+    // (causal: its first token; REV: its last), nothing walked before it matters: start
+    // there. The tiles run are tfirst .. tfirst + tcount - 1.
+    bool ended = false;   // a sequence's last token in scan order lies inside the chunk
+    int tfirst = 0, tcount = ntiles;
     if (PACKED) {
-        const int64_t e = (int64_t)p.cu[p.tok_seq[t_beg] + 1] - 1;
-        if (e >= t_beg && e < t_end) {
-            ended = true;
-            ntiles = (int)((e - t_beg) / kT) + 1;
+        if (!REV) {
+            const int64_t e = (int64_t)p.cu[p.tok_seq[t_beg] + 1] - 1;
+            if (e >= t_beg && e < t_end) {
+                ended = true;
+                tcount = (int)((e - t_beg) / kT) + 1;
+            }
+        } else {
+            const int64_t st = p.cu[p.tok_seq[t_end - 1]];
+            if (st >= t_beg && st < t_end) {
+                ended = true;
+                tfirst = (int)((st - t_beg) / kT);
+                tcount = ntiles - tfirst;
+            }
         }
     }
 
@@ -633,9 +652,9 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
                 p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + t0 + (tid & 15)) * 4);
         if (PACKED) rev = p.tile_ev[t0 / kT];
     };
-    load_tile(REV ? 0 : ntiles - 1);
-    for (int it = 0; it < ntiles; ++it) {
-        const int ti = REV ? it : ntiles - 1 - it;
+    load_tile(REV ? tfirst : tcount - 1);
+    for (int it = 0; it < tcount; ++it) {
+        const int ti = REV ? tfirst + it : tcount - 1 - it;
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
@@ -644,8 +663,10 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         rz.widen(zv);
         rg.widen(gv);
         const float4 cv4 = rc;
-        const uint32_t emask = PACKED ? (rev >> 16) : 0u;
-        if (it + 1 < ntiles) load_tile(REV ? ti + 1 : ti - 1);
+        // packed: the tile's last tokens of sequences in scan order (causal: ends; REV:
+        // starts)
+        const uint32_t lmask = PACKED ? (REV ? (rev & 0xffffu) : (rev >> 16)) : 0u;
+        if (it + 1 < tcount) load_tile(REV ? ti + 1 : ti - 1);
         // C of the tile, per state pair: threads 0..127 move (pair, token)
         if (tid < 128) *reinterpret_cast<float2*>(sC + tid * 2) = make_float2(cv4.z, cv4.w);
         float dl[2], dqv[2];
@@ -660,12 +681,12 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
         __syncthreads();
         const float* ct = sC + pr * kT * 2;
-        // packed: at the last token of a sequence the gradient restarts from its dh_final,
-        // so the chunk's end value no longer depends on what later chunks carry in
+        // packed: at a sequence's last token in scan order the gradient restarts from its
+        // dh_final, so the chunk's value no longer depends on what the other chunks carry
 #pragma unroll
         for (int kk = 0; kk < kT; ++kk) {
             const int k = REV ? kk : kT - 1 - kk;
-            if (PACKED && (emask & (1u << k))) {
+            if (PACKED && (lmask & (1u << k))) {
                 float2 v = make_float2(0.f, 0.f);
                 if (p.dh_final && valid)
                     v = *reinterpret_cast<const float2*>(
@@ -789,7 +810,9 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
     const int64_t ngroups = prm.batch * prm.groups_per_batch;
     hipError_t e;
 #define SSM_BWD(KERNEL, IO, N, GRID, P)                                                    \
-    if (P.cu)                                                                              \
+    if (P.cu && P.reverse)                                                                 \
+        hipLaunchKernelGGL((KERNEL<IO, N, true, true>), GRID, dim3(N * 8), 0, stream, P);  \
+    else if (P.cu)                                                                         \
         hipLaunchKernelGGL((KERNEL<IO, N, true, false>), GRID, dim3(N * 8), 0, stream, P); \
     else if (P.reverse)                                                                    \
         hipLaunchKernelGGL((KERNEL<IO, N, false, true>), GRID, dim3(N * 8), 0, stream, P); \

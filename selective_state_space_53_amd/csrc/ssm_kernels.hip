@@ -176,7 +176,6 @@ template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
     static_assert(!CKPT || !LOCAL, "checkpoints: final pass");
-    static_assert(!CKPT || !(REV && PACKED), "checkpoints: causal packed, or batch rows");
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
     __shared__ float sD[CG * kLdsRow];
@@ -424,9 +423,10 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                 const int k = REV ? kTile - 1 - kk : kk;
                 const int64_t t = t0 + k;
                 const bool real = k < nvalid;
-                // checkpoints: the state before tokens t0 and t0 + 16, before any reset
-                // there (the backward applies the resets itself)
-                if (CKPT && valid && (k == 0 || (k == 16 && real)))
+                // checkpoints: the state entering each 16-token block in scan order, before
+                // any reset there (the backward applies the resets itself)
+                if (CKPT && valid &&
+                    (REV ? ((k == kTile - 1 && nvalid > 16) || k == 15) : (k == 0 || (k == 16 && real))))
                     *reinterpret_cast<float2*>(ck + (t / 16) * kDState) = make_float2(h[0], h[1]);
                 if (real && t == (REV ? hi - 1 : lo)) {     // first token of sequence s
                     float2 hv = make_float2(0.f, 0.f);
@@ -630,8 +630,11 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
 
 template <typename IO, bool LOCAL>
 hipError_t launch_scan_dir(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
-    if (!LOCAL && prm.ckpt) {   // (packed input: causal only; the host checks)
-        if (prm.cu) return launch_scan_kernel<IO, false, false, true, true>(cg, grid, stream, prm);
+    if (!LOCAL && prm.ckpt) {
+        if (prm.cu)
+            return prm.reverse
+                       ? launch_scan_kernel<IO, false, true, true, true>(cg, grid, stream, prm)
+                       : launch_scan_kernel<IO, false, false, true, true>(cg, grid, stream, prm);
         return prm.reverse
                    ? launch_scan_kernel<IO, false, true, false, true>(cg, grid, stream, prm)
                    : launch_scan_kernel<IO, false, false, false, true>(cg, grid, stream, prm);

@@ -322,9 +322,13 @@ def test_varlen_bwd_workspace_and_options(b):
     for kw in ({}, dict(bwd_chunk_len=64), dict(plan=2, chunk_len=64, bwd_group_channels=32)):
         assert (b.ssm_scan_varlen_bwd_workspace_bytes(1000, 64, 16, 1, **kw)
                 == b.ssm_scan_bwd_workspace_bytes(1, 1000, 64, 16, 1, **kw))
-    # the checkpoints are always recomputed: saved=1 is refused; reverse likewise
+    # the checkpoints are always recomputed: saved=1 is refused; the anti-causal
+    # backward takes the same workspace (one short of it is refused)
     assert varlen_bwd(b, opts=_save_opts(b, None, 0, saved=1)) == 2
-    assert varlen_bwd(b, opts=_save_opts(b, None, 0, reverse=1)) == 2
+    rev = _save_opts(b, None, 0, reverse=1)
+    need = b.lib.ssm_scan_varlen_bwd_workspace_bytes(100, 64, 16, 1, rev)
+    assert need == b.ssm_scan_varlen_bwd_workspace_bytes(100, 64, 16, 1) > 0
+    assert varlen_bwd(b, opts=rev, ws_bytes=need - 1) == 3
     assert varlen_bwd(b, opts=_save_opts(b, 0x7d0000000000, 1 << 30)) == 1
 
 
