@@ -450,6 +450,11 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             }
         }
 #undef SSM_TOKEN
+        // pass 1 keeps its results in registers only, so the compiler may sink the whole
+        // recurrence below the barrier and then has to hold every LDS operand of the tile
+        // at once (~160 VGPRs); an empty asm that claims to update the state keeps the
+        // recurrence above it
+        if (LOCAL) asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(dsum));
         __syncthreads();
 
         // ---- post: this thread's 4 tokens: sum the 8 pairs' partials, skip, gate, store

@@ -108,6 +108,28 @@ def test_bidirectional_sum(shape, plan, chunk):
     assert e <= parity.TOL[io]
 
 
+def test_bidirectional_full_size_sampled_rows():
+    """The Mamba-2.8B layer as the bidirectional benchmark runs it (causal scan into y,
+    then the anti-causal scan accumulated into the same bf16 y, library plans): sampled
+    rows, each over the whole sequence, against the sum of the two oracles."""
+    cfg = synth.CONFIGS["m2p8"]
+    say("case bidirectional full size")
+    inp = synth.scan_inputs(cfg, DEV)
+    y = parity.gpu_scan(inp, final=False)
+    from selective_state_space_53_amd import binding
+    binding.ssm_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                         z=inp["z"], delta_bias=inp["delta_bias"], y=y, reverse=True,
+                         accumulate=True)
+    torch.cuda.synchronize()
+    rb, rd = parity.sample_rows(cfg.batch, cfg.dim, 64, seed=cfg.seed + 2)
+    yf, _ = parity.oracle_rows(inp, rb, rd)
+    yb, _ = parity.oracle_reverse_rows(inp, rb, rd)
+    sel = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
+    e = parity.rowwise_err(y[sel], yf + yb)
+    say(f"  bidirectional m2p8: rows {len(rb)} y {e:.3e}")
+    assert e <= parity.TOL[cfg.io]
+
+
 # ------------------------------------------------------------- packed sequences
 PACKED = [
     # (lengths, dim, io)
