@@ -554,13 +554,13 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
 // The backward of ssm_scan_bwd (cu == nullptr: batch rows) and of ssm_scan_varlen_bwd
 // (cu set: batch = 1, seqlen = total, h0 / dh_final / dh0 per sequence).
 ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void* B,
-                        const void* C, const float* D, const void* z,
-                        const float* delta_bias, int delta_softplus, const float* h0,
-                        const int32_t* cu, int64_t nseq, const void* dy, const float* dh_final, void* dx, void* ddelta,
-                        void* dz, float* dA, float* dB, float* dC, float* dD,
-                        float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
-                        int64_t dim, int64_t dstate, ssm_dtype io_dtype, void* workspace,
-                        size_t workspace_bytes, const ssm_scan_options* opts, void* stream) {
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int delta_softplus, const float* h0, const int32_t* cu, int64_t nseq,
+                    const void* dy, const float* dh_final, void* dx, void* ddelta, void* dz,
+                    float* dA, float* dB, float* dC, float* dD, float* ddelta_bias, float* dh0,
+                    int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                    ssm_dtype io_dtype, void* workspace, size_t workspace_bytes,
+                    const ssm_scan_options* opts, void* stream) {
     try {
         BwdPlan bp;
         ssm_status st = make_bwd_plan(batch, seqlen, dim, dstate, io_dtype, opts, &bp);
