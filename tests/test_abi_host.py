@@ -50,11 +50,20 @@ P = {k: 0x7f0000000000 + i * (1 << 36) for i, k in enumerate(
     ["x", "delta", "A", "B", "C", "D", "z", "bias", "h0", "y", "hf", "ws"])}
 
 
+def _chunked(b):
+    """Forced chunked plan (chunks of 32 tokens): the forward then needs a workspace, so
+    every call here that should be refused has a workspace region to check against (the
+    single-pass plan needs none)."""
+    return ctypes.byref(b.ScanOptions(32, 2, 0))
+
+
 def scan(b, batch=2, seqlen=64, dim=64, dstate=16, io=1, ws_bytes=None, opts=None, **over):
     p = dict(P)
     p.update(over)
     if ws_bytes is None:
         ws_bytes = 1 << 40
+    if opts is None:
+        opts = _chunked(b)
     return b.lib.ssm_scan_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
                               p["bias"], p.get("softplus", 1), p["h0"], p["y"], p["hf"], batch,
                               seqlen, dim, dstate, io, p["ws"], ws_bytes, opts, None)
@@ -129,7 +138,7 @@ def varlen(b, total=100, dim=64, nseq=3, io=1, ws_bytes=None, **over):
         ws_bytes = 1 << 40
     return b.lib.ssm_scan_varlen_fwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
                                      p["bias"], 1, p["cu"], nseq, p["h0"], p["y"], p["hf"], total,
-                                     dim, 16, io, p["ws"], ws_bytes, None, None)
+                                     dim, 16, io, p["ws"], ws_bytes, _chunked(b), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -228,7 +237,8 @@ def test_bwd_workspace_and_rejects(b):
 
 
 def _save_opts(b, save, nbytes, saved=0, reverse=0, accumulate=0):
-    return ctypes.byref(b.ScanOptions(0, 0, 0, None, None, reverse, accumulate, 0, 0, save,
+    # (chunked plan, so that the forward's own workspace is not empty: see _chunked)
+    return ctypes.byref(b.ScanOptions(32, 2, 0, None, None, reverse, accumulate, 0, 0, save,
                                       nbytes, saved))
 
 
@@ -327,7 +337,8 @@ def test_varlen_bwd_workspace_and_options(b):
     assert varlen_bwd(b, opts=_save_opts(b, None, 0, saved=1)) == 2
     rev = _save_opts(b, None, 0, reverse=1)
     need = b.lib.ssm_scan_varlen_bwd_workspace_bytes(100, 64, 16, 1, rev)
-    assert need == b.ssm_scan_varlen_bwd_workspace_bytes(100, 64, 16, 1) > 0
+    assert need == b.ssm_scan_varlen_bwd_workspace_bytes(100, 64, 16, 1, plan=2,
+                                                          chunk_len=32) > 0
     assert varlen_bwd(b, opts=rev, ws_bytes=need - 1) == 3
     assert varlen_bwd(b, opts=_save_opts(b, 0x7d0000000000, 1 << 30)) == 1
 
