@@ -129,3 +129,63 @@ def test_decode_equals_scan_on_gpu():
     y_dec = torch.stack(ys, dim=2)
     assert parity.rowwise_err(y_dec, y_scan) <= 1e-5
     assert parity.rowwise_err(st, h_scan) <= 1e-5
+
+
+def test_decode_steps_in_a_hip_graph():
+    """The library allocates nothing and never synchronizes inside a call, so a run of
+    decode steps (the conv update, then the scan's state update, per token) can be
+    captured once into a HIP graph and replayed. Every replay, with eager work and a
+    synchronization between replays, must give the states and outputs of the same steps
+    run eagerly, bit for bit."""
+    from selective_state_space_53_amd import binding
+    batch, dim, T = 64, 1024, 6
+    g = torch.Generator().manual_seed(41)
+    A = -torch.rand((dim, 16), generator=g).add(0.1).to(DEV)
+    D = torch.randn(dim, generator=g).to(DEV)
+    bias = torch.randn(dim, generator=g).mul(0.3).to(DEV)
+    w = torch.randn((dim, 4), generator=g).mul(0.5).to(DEV)
+    cb = torch.randn(dim, generator=g).mul(0.2).to(DEV)
+    bf = torch.bfloat16
+    toks = [{k: torch.randn(shape, generator=g).to(bf).to(DEV)
+             for k, shape in (("x", (batch, dim)), ("delta", (batch, dim)), ("z", (batch, dim)),
+                              ("B", (batch, 16)), ("C", (batch, 16)))} for _ in range(T)]
+    state0 = torch.randn((batch, dim, 16), generator=g).to(DEV)
+    conv0 = torch.randn((batch, dim, 3), generator=g).to(bf).to(DEV)
+    ys = [torch.empty((batch, dim), dtype=bf, device=DEV) for _ in range(T)]
+    xc = [torch.empty((batch, dim), dtype=bf, device=DEV) for _ in range(T)]
+
+    def steps(state, conv):
+        for t, tok in enumerate(toks):
+            binding.ssm_causal_conv1d_update(conv, tok["x"], w, cb, y=xc[t])
+            binding.ssm_state_update(state, xc[t], tok["delta"], A, tok["B"], tok["C"], D=D,
+                                     z=tok["z"], delta_bias=bias, y=ys[t])
+
+    # eager reference
+    st_e, cv_e = state0.clone(), conv0.clone()
+    steps(st_e, cv_e)
+    torch.cuda.synchronize()
+    y_e = [y.clone() for y in ys]
+    # capture (on a side stream, as torch requires), then replay three times
+    st_g, cv_g = state0.clone(), conv0.clone()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        steps(st_g.clone(), cv_g.clone())       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        steps(st_g, cv_g)
+    for rep in range(3):
+        st_g.copy_(state0)
+        cv_g.copy_(conv0)
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  graph replay {rep}")
+        assert torch.equal(st_g, st_e) and torch.equal(cv_g, cv_e), rep
+        for t in range(T):
+            assert torch.equal(ys[t], y_e[t]), (rep, t)
+        _ = (torch.randn(1000, device=DEV) * 2).sum().item()   # eager work between replays
