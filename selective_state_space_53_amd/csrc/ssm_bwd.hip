@@ -28,6 +28,12 @@
 // Sums over channels across workgroups (dB, dC) and over batch rows (dA, dD, dbias)
 // are finished by small reduction kernels in a fixed order: no float atomics, the
 // result does not depend on scheduling.
+// Variants: REV, the anti-causal scan (time relabelled: tiles and tokens walked the
+// other way, h_{t+1} as the state before token t); PACKED, sequences laid end to end
+// in one row (per 16-token tile, bit masks of sequence starts and ends from a small
+// kernel; tiles with one run token by token and restart the recurrence and its adjoint
+// at the boundaries); and the chunked plan (a local pass per chunk, a carry, then
+// every chunk from its carried-in gradient).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
