@@ -245,6 +245,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     __shared__ float sP2[8 * CG * kRowP];       // per state pair: G.h.a.A
     __shared__ float sBC[2 * kBcT];             // [buffer][pair][token][B0 B1 C0 C1]
     __shared__ float sRed[kT * kLaneRows * 4];  // [token][lane row][dB0 dB1 dC0 dC1]
+    __shared__ uint32_t sEv;                    // packed: the tile's event masks
 
     const int tid = threadIdx.x;
     const int64_t ngroups = p.batch * p.groups_per_batch;
@@ -332,7 +333,11 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     Raw2<IO> rx, rd, rz, rg, rq;
     float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
     float2 rck = make_float2(0.f, 0.f);
-    uint32_t rev = 0;   // packed: the tile's event masks (starts | ends << 16)
+    // packed: the tile's event masks (starts | ends << 16), loaded by thread 0 with the
+    // tile's inputs and passed to the workgroup through LDS. (A uniform load would be
+    // moved to a scalar register right away, and the wait for it would also wait for the
+    // next tile's prefetched inputs issued before it.)
+    uint32_t rev = 0;
     // ti: tile of the chunk; its checkpoint is the global tile t0 / 16
     auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kT;
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         }
         if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
         if (valid) rck = *reinterpret_cast<const float2*>(ck + (t0 / kT) * kDState);
-        if (PACKED) rev = p.tile_ev[t0 / kT];
+        if (PACKED && tid == 0) rev = p.tile_ev[t0 / kT];
     };
     rx.zero();
     rd.zero();
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         // the state entering the tile in scan order (causal: before its first token; REV:
         // after the token that follows it)
         const float hs0 = rck.x, hs1 = rck.y;
-        const uint32_t ev = rev;
+        if (PACKED && tid == 0) sEv = rev;
         if (it + 1 < ntiles) load_tile(REV ? ti + 1 : ti - 1);
         float dl[2], sg[2], dqv[2], uu[2], dzv[2];
 #pragma unroll
@@ -403,7 +408,8 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
 
         // packed: the tile's tokens that start (smask) or end (emask) a sequence; the
         // same for the whole workgroup, so every branch on them is uniform
-        const uint32_t smask = PACKED ? (ev & 0xffffu) : 0u, emask = PACKED ? (ev >> 16) : 0u;
+        const uint32_t ev = PACKED ? sEv : 0u;
+        const uint32_t smask = ev & 0xffffu, emask = ev >> 16;
         const float* bct = sBC + (it & 1) * kBcT + pr * (kT * 4);
         float hs[kT][2];
         // (tiles with events are the rare case: laid out away from the quiet path)
@@ -573,6 +579,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     __shared__ float sD[CG * kRowF];
     __shared__ float sQ[CG * kRowF];
     __shared__ float sC[8 * kT * 2];            // [pair][token][C0 C1]
+    __shared__ uint32_t sEv;                    // packed: the tile's event masks
 
     const int tid = threadIdx.x;
     const int64_t ngroups = p.batch * p.groups_per_batch;
@@ -639,7 +646,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
     // 2 tokens) and, for threads 0..127, C of one (state pair, token)
     Raw2<IO> rd, rz, rg;
     float4 rc = make_float4(0.f, 0.f, 0.f, 0.f);
-    uint32_t rev = 0;   // packed: the tile's event masks (starts | ends << 16)
+    uint32_t rev = 0;   // packed: the tile's event masks, via thread 0 and LDS as above
     auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         if (tid < 128)
             rc = *reinterpret_cast<const float4*>(
                 p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + t0 + (tid & 15)) * 4);
-        if (PACKED) rev = p.tile_ev[t0 / kT];
+        if (PACKED && tid == 0) rev = p.tile_ev[t0 / kT];
     };
     load_tile(REV ? tfirst : tcount - 1);
     for (int it = 0; it < tcount; ++it) {
@@ -669,9 +676,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         rz.widen(zv);
         rg.widen(gv);
         const float4 cv4 = rc;
-        // packed: the tile's last tokens of sequences in scan order (causal: ends; REV:
-        // starts)
-        const uint32_t lmask = PACKED ? (REV ? (rev & 0xffffu) : (rev >> 16)) : 0u;
+        if (PACKED && tid == 0) sEv = rev;
         if (it + 1 < tcount) load_tile(REV ? ti + 1 : ti - 1);
         // C of the tile, per state pair: threads 0..127 move (pair, token)
         if (tid < 128) *reinterpret_cast<float2*>(sC + tid * 2) = make_float2(cv4.z, cv4.w);
@@ -686,6 +691,9 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_local_kernel(const BwdParams 
         *reinterpret_cast<float2*>(myD) = make_float2(dl[0], dl[1]);
         *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
         __syncthreads();
+        // packed: the tile's last tokens of sequences in scan order (causal: ends; REV:
+        // starts)
+        const uint32_t lmask = PACKED ? (REV ? (sEv & 0xffffu) : (sEv >> 16)) : 0u;
         const float* ct = sC + pr * kT * 2;
         // packed: at a sequence's last token in scan order the gradient restarts from its
         // dh_final, so the chunk's value no longer depends on what the other chunks carry
