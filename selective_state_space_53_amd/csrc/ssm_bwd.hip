@@ -365,6 +365,7 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
     load_tile(REV ? 0 : ntiles - 1);
 
     if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
+    wait_vmem();   // nothing in flight at the loop's entry: no wait at its top
 
     float dDacc = 0.0f, dbacc = 0.0f;
     for (int it = 0; it < ntiles; ++it) {
@@ -492,6 +493,12 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
         }
         }   // quiet tile
         __syncthreads();
+        // the next tile's B/C into the other buffer (last read before the barrier above),
+        // after a wait for its loads -- issued before the recompute, so short -- taken
+        // before this tile's stores, so that it does not wait for them
+        wait_vmem();
+        if (bc_mover && it + 1 < ntiles)
+            *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcT) = rbc;
 
         // ---- post: dx, ddelta for (cq, 2 tokens); the workgroup's dB, dC partial sums
         {
@@ -538,9 +545,6 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 4 + which * 2 + (n & 1)];
             if (k < nvalid) pbc[(t0 + k) * 32 + v] = sum;
         }
-        // the next tile's B/C into the other buffer (last read before the barrier above)
-        if (bc_mover && it + 1 < ntiles)
-            *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcT) = rbc;
     }
 
     // ---- per-row results: dh0 = a G at the last token of the scan (the carry after it:

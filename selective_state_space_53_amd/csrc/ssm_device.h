@@ -1,5 +1,6 @@
 // ssm_device.h - element-wise device helpers shared by the library's HIP sources
-// (softplus, SiLU and their derivatives on the hardware exp2/log2/rcp, bf16 <-> fp32).
+// (softplus, SiLU and their derivatives on the hardware exp2/log2/rcp, bf16 <-> fp32,
+// streaming accesses, a wait for outstanding memory accesses).
 // Not installed, not part of the ABI.
 #pragma once
 
@@ -61,6 +62,15 @@ __device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_one(uint16_t* p, float v) {
     *p = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
+
+// Wait until every vector-memory access the wave has issued is complete (vmcnt 0; the
+// export and LDS/scalar counters untouched: their fields at the maximum). gfx950 counts
+// loads and stores with one counter, so once stores are in flight behind prefetched
+// loads, the wait the compiler puts before a use of those loads waits for the stores
+// too -- and it also keeps such a wait at the top of a loop whose entry has loads in
+// flight. The tile loops take this wait themselves, where only accesses issued long
+// before are outstanding.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // sigma(v) = 1 / (1 + e^-v): the derivative of softplus
 __device__ __forceinline__ float sigmoid_f(float v) {

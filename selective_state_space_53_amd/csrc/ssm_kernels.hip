@@ -323,6 +323,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     rz.zero();
     load_tile(tile_of(0));
     if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
+    wait_vmem();   // nothing in flight at the loop's entry: no wait at its top
 
     for (int it = 0; it < nt; ++it) {
         const int ti = tile_of(it);
@@ -456,6 +457,13 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // recurrence above it
         if (LOCAL) asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(dsum));
         __syncthreads();
+        // the next tile's B/C into the other LDS buffer (its last readers finished before
+        // the barrier above; its next readers come after the next barrier). The loads were
+        // issued before the core, so the wait is short; taken here, before this tile's
+        // stores, it does not wait for them.
+        wait_vmem();
+        if (bc_mover && it + 1 < nt)
+            *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile) = rbc;
 
         // ---- post: this thread's 4 tokens: sum the 8 pairs' partials, skip, gate, store
         if (kOut) {
@@ -485,10 +493,6 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                 Store4<IO>::store(yr + t0 + 4 * jq, vec, nq, yv);
             }
         }
-        // the next tile's B/C into the other LDS buffer (its last readers finished
-        // before the barrier above; its next readers come after the next barrier)
-        if (bc_mover && it + 1 < nt)
-            *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile) = rbc;
     }
 
     if (LOCAL) {
