@@ -241,9 +241,17 @@ __device__ __forceinline__ void bwd_event_tile(
     }
 }
 
+// (3 waves per SIMD: the register budget of 168 that lets two workgroups of 48 channels,
+// or three of 32, share a CU; 64 channels fill a CU's LDS with one workgroup of 8 waves)
 template <typename IO, int CG, bool PACKED, bool REV>
-__global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(CG * 8) __attribute__((amdgpu_waves_per_eu(CG == 64 ? 2 : 3)))
+void scan_bwd_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
+    // causal: the recomputation leaves each token's decays exp(Delta A) in the tile's
+    // partial rows, where the adjoint reads them back (and then overwrites them with its
+    // partials) instead of evaluating the exp a second time. The anti-causal order needs
+    // more registers around it, past the budget above, and evaluates them again.
+    constexpr bool kKeepDecay = !REV;
     constexpr int kRowsPerPair = CG / 16;
     constexpr int kLaneRows = CG / 2;           // 16-lane rows in the workgroup
     __shared__ float sD[CG * kRowF];            // Delta
@@ -437,16 +445,25 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 const float4 U4 = *reinterpret_cast<const float4*>(cU + g4);
                 const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
                 const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
+                const int slot = ((g4 >> 2) ^ swz(cc)) << 2;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = REV ? 3 - jj : jj;
                     const int k = g4 + j;
                     const float2 bb = *reinterpret_cast<const float2*>(bct + k * 4);
-                    h0 = __builtin_fmaf(fast_exp2(Ds[j] * a2[0]), h0, bb.x * Us[j]);
-                    h1 = __builtin_fmaf(fast_exp2(Ds[j] * a2[1]), h1, bb.y * Us[j]);
+                    const float e0 = fast_exp2(Ds[j] * a2[0]);
+                    const float e1 = fast_exp2(Ds[j] * a2[1]);
+                    h0 = __builtin_fmaf(e0, h0, bb.x * Us[j]);
+                    h1 = __builtin_fmaf(e1, h1, bb.y * Us[j]);
                     hs[k][0] = h0;
                     hs[k][1] = h1;
+                    // the pair's decays of token k: tokens 4g, 4g+1 in the p1 slot of
+                    // group g, 4g+2, 4g+3 in its p2 slot
+                    if (kKeepDecay)
+                        *reinterpret_cast<float2*>((j < 2 ? p1 : p2) + slot + 2 * (j & 1)) =
+                            make_float2(e0, e1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
@@ -461,14 +478,23 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
             const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
             const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
             const float Qs[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
+            const int slot = ((g4 >> 2) ^ swz(cc)) << 2;
             float o1[4], o2[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int j = REV ? jj : 3 - jj;
                 const int k = g4 + j;
                 const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
-                const float e0 = fast_exp2(Ds[j] * a2[0]);
-                const float e1 = fast_exp2(Ds[j] * a2[1]);
+                float e0, e1;
+                if (kKeepDecay) {
+                    const float2 ee =
+                        *reinterpret_cast<const float2*>((j < 2 ? p1 : p2) + slot + 2 * (j & 1));
+                    e0 = ee.x;
+                    e1 = ee.y;
+                } else {
+                    e0 = fast_exp2(Ds[j] * a2[0]);
+                    e1 = fast_exp2(Ds[j] * a2[1]);
+                }
                 const float G0 = __builtin_fmaf(Qs[j], q.z, Gc[0]);
                 const float G1 = __builtin_fmaf(Qs[j], q.w, Gc[1]);
                 // the state before token k in scan order
@@ -492,7 +518,6 @@ __global__ __launch_bounds__(CG * 8) void scan_bwd_kernel(const BwdParams p) {
                 Gc[0] = e0 * G0;
                 Gc[1] = e1 * G1;
             }
-            const int slot = ((g4 >> 2) ^ swz(cc)) << 2;
             *reinterpret_cast<float4*>(p1 + slot) = make_float4(o1[0], o1[1], o1[2], o1[3]);
             *reinterpret_cast<float4*>(p2 + slot) = make_float4(o2[0], o2[1], o2[2], o2[3]);
             // keep the scheduler's hoisting inside the group: across groups it raises the
