@@ -409,16 +409,22 @@ int64_t bwd_lds_bytes(int cg) { return (int64_t)(348 * cg + 1024) * 4; }
 
 // Relative time of one backward pass: `groups` workgroups of cg channels over `tiles`
 // 16-token tiles (as pass_cost, with the backward's LDS and its <= 168 VGPRs: 3 waves
-// per SIMD).
+// per SIMD). A workgroup's cg/8 waves are counted as dealt to the CU's four SIMDs from
+// the first one, so it puts ceil(cg/32) of them on its busiest SIMD, and a second
+// 6-wave workgroup (cg = 48) does not fit beside the first: measured on the 2.8B layer,
+// the backward kernel takes 1039 us with 48 channels per workgroup, 773 us with 64 (one
+// 8-wave workgroup per CU) and 728 us with 32 (three 4-wave workgroups per CU); on the
+// 130M layer 536, 458 and 380 us.
 double bwd_pass_cost(int64_t groups, int64_t tiles, int cg) {
+    const int64_t per_simd = (cg / 8 + 3) / 4;
     int64_t k = kLdsPerCU / bwd_lds_bytes(cg);
-    const int64_t kw = 4 * 3 / (cg / 8);
+    const int64_t kw = 3 / per_simd;
     if (kw < k) k = kw;
     const int64_t per_cu = (groups + kCUs - 1) / kCUs;
     if (k > per_cu) k = per_cu;
     if (k < 1) k = 1;
     const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
-    const int64_t w = (k * (cg / 8) + 3) / 4;
+    const int64_t w = k * per_simd;
     return (double)rounds * (double)(tiles + 1) * (double)w * wave_cost(w);
 }
 
