@@ -85,16 +85,20 @@ constexpr int64_t kLdsPerCU = 160 * 1024;
 constexpr int64_t kMaxWavesFull = 4, kMaxWavesLocal = 5;
 
 // Relative time of one pass: `groups` workgroups of cg channels, `tiles` tiles each.
+// A workgroup's cg/8 waves are counted as dealt to the CU's four SIMDs from the first,
+// ceil(cg/32) on the busiest (as for the backward, where a second 6-wave workgroup was
+// measured not to join the first; here, with CG = 48 on the 2.8B layer, 349 us against
+// 249 us at CG = 80).
 double pass_cost(int64_t groups, int64_t tiles, int cg, bool local) {
-    const int64_t waves = cg / 8;
+    const int64_t per_simd = (cg / 8 + 3) / 4;
     int64_t k = kLdsPerCU / scan_lds_bytes(cg, local);                  // by LDS
-    const int64_t kw = 4 * (local ? kMaxWavesLocal : kMaxWavesFull) / waves;  // by registers
+    const int64_t kw = (local ? kMaxWavesLocal : kMaxWavesFull) / per_simd;  // by registers
     if (kw < k) k = kw;
     const int64_t per_cu = (groups + kCUs - 1) / kCUs;
     if (k > per_cu) k = per_cu;
     if (k < 1) k = 1;
     const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
-    const int64_t w = (k * waves + 3) / 4;                               // busiest SIMD
+    const int64_t w = k * per_simd;                                      // busiest SIMD
     // pass 1 skips the readout and the output stage; a workgroup's set-up costs about
     // one tile
     return (double)rounds * (double)(tiles + 1) * (double)w * wave_cost(w) * (local ? 0.85 : 1.0);
