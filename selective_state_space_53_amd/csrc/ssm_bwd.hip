@@ -446,6 +446,7 @@ void scan_bwd_kernel(const BwdParams p) {
                 const float Ds[4] = {D4.x, D4.y, D4.z, D4.w};
                 const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
                 const int slot = ((g4 >> 2) ^ swz(cc)) << 2;
+                float ek[4][2];
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = REV ? 3 - jj : jj;
@@ -457,11 +458,13 @@ void scan_bwd_kernel(const BwdParams p) {
                     h1 = __builtin_fmaf(e1, h1, bb.y * Us[j]);
                     hs[k][0] = h0;
                     hs[k][1] = h1;
-                    // the pair's decays of token k: tokens 4g, 4g+1 in the p1 slot of
-                    // group g, 4g+2, 4g+3 in its p2 slot
-                    if (kKeepDecay)
-                        *reinterpret_cast<float2*>((j < 2 ? p1 : p2) + slot + 2 * (j & 1)) =
-                            make_float2(e0, e1);
+                    ek[j][0] = e0;
+                    ek[j][1] = e1;
+                    // the pair's decays: tokens 4g, 4g+1 in the p1 slot of group g, 4g+2,
+                    // 4g+3 in its p2 slot, one 16-byte write per two tokens
+                    if (kKeepDecay && (j & 1))
+                        *reinterpret_cast<float4*>((j < 2 ? p1 : p2) + slot) =
+                            make_float4(ek[j - 1][0], ek[j - 1][1], ek[j][0], ek[j][1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -479,6 +482,7 @@ void scan_bwd_kernel(const BwdParams p) {
             const float Us[4] = {U4.x, U4.y, U4.z, U4.w};
             const float Qs[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
             const int slot = ((g4 >> 2) ^ swz(cc)) << 2;
+            float4 epair = make_float4(0.f, 0.f, 0.f, 0.f);
             float o1[4], o2[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -487,10 +491,11 @@ void scan_bwd_kernel(const BwdParams p) {
                 const float4 q = *reinterpret_cast<const float4*>(bct + k * 4);
                 float e0, e1;
                 if (kKeepDecay) {
-                    const float2 ee =
-                        *reinterpret_cast<const float2*>((j < 2 ? p1 : p2) + slot + 2 * (j & 1));
-                    e0 = ee.x;
-                    e1 = ee.y;
+                    // causal: j runs 3..0, so the odd token of a pair comes first and
+                    // reads both
+                    if (j & 1) epair = *reinterpret_cast<const float4*>((j < 2 ? p1 : p2) + slot);
+                    e0 = (j & 1) ? epair.z : epair.x;
+                    e1 = (j & 1) ? epair.w : epair.y;
                 } else {
                     e0 = fast_exp2(Ds[j] * a2[0]);
                     e1 = fast_exp2(Ds[j] * a2[1]);
