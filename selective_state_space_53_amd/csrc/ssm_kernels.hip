@@ -357,6 +357,11 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         *reinterpret_cast<float4*>(myUq) = make_float4(uu[0], uu[1], uu[2], uu[3]);
         __syncthreads();
 
+        // With 32 channels a CU holds several workgroups, out of phase: the core runs at
+        // raised wave priority so that the others' load and store phases do not take its
+        // issue slots (million-token forward 13.02 -> 12.76 ms, packed 339 -> 335 us in a
+        // same-box A/B; with one workgroup per CU, as at 80 channels, it gains nothing)
+        if (CG == 32) __builtin_amdgcn_s_setprio(1);
         // ---- core: the recurrence over the 32 tokens for (channel cc, states 2pr, 2pr+1).
         // Every lane of a row reads the same (B0, B1, C0, C1) of a token from LDS, so B
         // and C arrive in VGPRs and every op below is a plain VOP2 with VGPR operands
@@ -456,6 +461,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // at once (~160 VGPRs); an empty asm that claims to update the state keeps the
         // recurrence above it
         if (LOCAL) asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(dsum));
+        if (CG == 32) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         // the next tile's B/C into the other LDS buffer (its last readers finished before
         // the barrier above; its next readers come after the next barrier). The loads were
