@@ -188,8 +188,11 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     // Channels per workgroup and chunking: the choice with the lowest modelled time
     // (pass_cost above) among group sizes 32..96 and chunk counts 1 (single pass), 2,
     // 3, 4, 6, 8, 12, ... A requested group size, plan or chunk length restricts the
-    // search. Ties go to fewer chunks, then to larger groups.
-    static const int kCands[] = {96, 80, 64, 48, 32};
+    // search. Ties go to fewer chunks, then to larger groups -- except that 32 channels
+    // come before 48: several 4-wave workgroups per CU, out of phase and with the core at
+    // raised priority, beat one 6-wave workgroup whose SIMDs hold 2, 2, 1, 1 waves (the
+    // 130M layer: 167 us at 32 against 181 us at 48, which the model ties).
+    static const int kCands[] = {96, 80, 64, 32, 48};
     PlanChoice best{0, 0, 0, 1e300, 0};
     for (int c : kCands) {
         if (req_cg && c != req_cg) continue;
