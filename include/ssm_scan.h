@@ -247,7 +247,9 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
  *   h0              [nseq][dim][dstate] fp32 or NULL: initial state of each sequence
  *   h_final         [nseq][dim][dstate] fp32 out or NULL: final state of each sequence
  *                   (an empty sequence's final state is its initial state). May be
- *                   exactly h0.
+ *                   exactly h0: the call then runs the single-pass plan (one sweep over
+ *                   the tokens per channel group), whatever the shape; with
+ *                   opts->plan = 2 (chunked) it returns SSM_ERR_UNSUPPORTED.
  *   A, D, delta_bias, delta_softplus, opts (including reverse: each sequence is
  *   scanned from its last token to its first) as for ssm_scan_fwd.
  * total >= 0 (0: only h_final is written), nseq >= 1, dim >= 1, dstate == 16.

@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssmscan.so")
+# hardware probes used by the benchmark (copy bandwidth, VALU issue costs); not the ABI
+PROBE_LIB = os.path.join(PKG, "libssmprobe.so")
+PROBE_SOURCE = "ssm_probe.hip"
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -63,6 +66,10 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     _run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *k_objs, a_obj, "-o", tmp],
          verbose)
     os.replace(tmp, LIB)
+    ptmp = PROBE_LIB + ".tmp"
+    _run(["hipcc", "-shared", *DEVICE_FLAGS, *inc, os.path.join(CSRC, PROBE_SOURCE), "-o", ptmp],
+         verbose)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 

@@ -264,6 +264,22 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
     ssm::ScanPlan plan;
     ssm_status st = make_plan(batch, seqlen, dim, dstate, io_dtype, opts, &plan);
     if (st != SSM_OK) return st;
+    // Packed sequences resumed in place (h_final == h0): in the chunked plan the workgroup
+    // of a sequence's last chunk writes its final state while the workgroup of its first
+    // chunk, in the same launch, may still read its initial state. The single pass reads
+    // a sequence's h0 before it writes its h_final, in the same thread; its workspace is
+    // no larger than the chunked plan's, so the caller's buffer still fits.
+    if (packed && h_final && (const void*)h_final == (const void*)h0 && plan.nchunks > 1) {
+        if (opts && opts->plan == 2)
+            return fail(SSM_ERR_UNSUPPORTED,
+                        "packed sequences with h_final == h0 (in place) run in the single-pass "
+                        "plan only; ssm_scan_options.plan = 2 asks for the chunked plan");
+        ssm_scan_options one = opts ? *opts : ssm_scan_options{};
+        one.plan = 1;
+        one.chunk_len = 0;
+        st = make_plan(batch, seqlen, dim, dstate, io_dtype, &one, &plan);
+        if (st != SSM_OK) return st;
+    }
     if (delta_softplus != 0 && delta_softplus != 1)
         return fail(SSM_ERR_INVALID_ARGUMENT, "delta_softplus must be 0 or 1");
     if (!x || !delta || !A || !B || !C || !y)

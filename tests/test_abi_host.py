@@ -146,7 +146,7 @@ def varlen(b, total=100, dim=64, nseq=3, io=1, ws_bytes=None, **over):
     (dict(cu=0x7e0000000002), 2), (dict(dim=0), 1), (dict(ws=None), 3),
     (dict(hf=P["h0"] + 16), 1), (dict(y=P["x"]), 1), (dict(h0=P["h0"] + 4), 2),
     (dict(total=0, hf=P["h0"] + 16), 1), (dict(total=0, hf=P["hf"] + 4), 2),
-    (dict(total=0, dim=0), 1),
+    (dict(total=0, dim=0), 1), (dict(hf=P["h0"]), 2),
 ])
 def test_varlen_rejects(b, kw, status):
     assert varlen(b, **kw) == status

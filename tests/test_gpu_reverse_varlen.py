@@ -230,6 +230,51 @@ def test_packed_integer_exact(io, reverse):
         assert np.array_equal(oracle.f64(hf), hr)
 
 
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_packed_in_place_resume(reverse):
+    """h_final == h0 on packed input whose sequences cross chunk boundaries: with several
+    chunks, one workgroup would write a sequence's final state while another still read its
+    initial state, so the library runs the single-pass plan in place (bit for bit the
+    oracle on integer-exact inputs, also where its own choice for the shape is chunked)
+    and refuses a forced chunked plan before launching anything."""
+    from selective_state_space_53_amd import binding
+    lens = [300, 1, 700, 0, 64, 1500, 33, 2, 900]
+    total = sum(lens)
+    dim = 48
+    rng = np.random.default_rng(11 if reverse else 12)
+    x = np.zeros((dim, total))
+    for d in range(dim):
+        idx = rng.choice(total, size=20, replace=False)
+        x[d, idx] = rng.choice([-1.0, 1.0], size=20)
+    dt = torch.bfloat16
+    xs = torch.tensor(x, dtype=dt, device=DEV)
+    dl = torch.ones((dim, total), dtype=dt, device=DEV)
+    B = torch.tensor(rng.integers(-1, 2, size=(total, 16)), dtype=dt, device=DEV)
+    C = torch.tensor(rng.integers(-1, 2, size=(total, 16)), dtype=dt, device=DEV)
+    A = torch.zeros((dim, 16), dtype=torch.float32, device=DEV)
+    D = torch.tensor(rng.integers(-2, 3, size=dim), dtype=torch.float32, device=DEV)
+    cu = synth.cu_seqlens(lens, DEV)
+    h0 = torch.tensor(rng.integers(-3, 4, size=(len(lens), dim, 16)), dtype=torch.float32,
+                      device=DEV)
+    yr, hr = oracle.Oracle().scan_varlen(xs, dl, A, B, C, oracle.f64(cu).astype(np.int64), D=D,
+                                         delta_softplus=False, h0=h0, reverse=reverse)
+    say("case packed in place", reverse)
+    with pytest.raises(binding.SSMError) as ei:
+        binding.ssm_scan_varlen_fwd(xs, dl, A, B, C, cu, D=D, delta_softplus=False, h0=h0,
+                                    h_final=h0, return_final_state=True, plan=2, chunk_len=64,
+                                    reverse=reverse)
+    assert ei.value.status == binding.SSM_ERR_UNSUPPORTED
+    for plan in (0, 1):
+        hs = h0.clone()
+        y, hf = binding.ssm_scan_varlen_fwd(xs, dl, A, B, C, cu, D=D, delta_softplus=False,
+                                            h0=hs, h_final=hs, return_final_state=True,
+                                            plan=plan, reverse=reverse)
+        torch.cuda.synchronize()
+        assert hf.data_ptr() == hs.data_ptr()
+        assert np.array_equal(oracle.f64(y), yr)
+        assert np.array_equal(oracle.f64(hs), hr)
+
+
 def test_packed_no_tokens():
     """total = 0: every sequence is empty; h_final = h0 (or zeros), also in place."""
     from selective_state_space_53_amd import binding
