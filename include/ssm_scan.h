@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 4
+#define SSM_SCAN_ABI_VERSION 5
 
 typedef enum {
     SSM_OK = 0,
@@ -165,6 +165,31 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
                         void* y, float* h_final, int64_t batch, int64_t seqlen, int64_t dim,
                         int64_t dstate, ssm_dtype io_dtype, void* workspace,
                         size_t workspace_bytes, const ssm_scan_options* opts, void* stream);
+
+/*
+ * ssm_scan_fwd without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The call itself allocates nothing: the workspace is a static scratch array
+ * of SSM_SCAN_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held by each
+ * GPU the library runs on until the process ends (its address is looked up once per
+ * device, at the first call whose stream runs there).
+ *  - Arguments, results and errors are those of ssm_scan_fwd (same kernels, same plan:
+ *    results are bit-identical to ssm_scan_fwd on the same inputs and options).
+ *  - A shape whose plan needs more workspace than the scratch holds returns
+ *    SSM_ERR_UNSUPPORTED (the Mamba-2.8B and 130M layer shapes need 1 and 2 MB; a
+ *    million-token sequence needs more: use ssm_scan_fwd there).
+ *  - Every call on one GPU shares that GPU's scratch, and it keeps what the last call
+ *    left there (each call writes every byte it later reads): calls that can overlap on
+ *    one GPU -- on different streams, or from different threads -- race on it, so
+ *    serialize them.
+ */
+#define SSM_SCAN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ssm_status ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* D, const void* z,
+                                const float* delta_bias, int delta_softplus, const float* h0,
+                                void* y, float* h_final, int64_t batch, int64_t seqlen,
+                                int64_t dim, int64_t dstate, ssm_dtype io_dtype,
+                                const ssm_scan_options* opts, void* stream);
 
 /*
  * Backward selective scan (training): the gradients of a loss through

@@ -21,7 +21,8 @@ if not os.path.exists(_LIB_PATH):
 SSM_OK, SSM_ERR_INVALID_ARGUMENT, SSM_ERR_UNSUPPORTED, SSM_ERR_WORKSPACE_TOO_SMALL, \
     SSM_ERR_HIP = range(5)
 SSM_F32, SSM_BF16 = 0, 1
-EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_scan_bwd_workspace_bytes",
+EXPORTS = ("ssm_scan_workspace_bytes", "ssm_scan_fwd", "ssm_scan_fwd_noalloc",
+           "ssm_scan_bwd_workspace_bytes",
            "ssm_scan_bwd", "ssm_scan_varlen_workspace_bytes",
            "ssm_scan_varlen_fwd", "ssm_scan_varlen_bwd_workspace_bytes", "ssm_scan_varlen_bwd",
            "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
@@ -48,6 +49,10 @@ lib.ssm_scan_fwd.restype = ctypes.c_int
 lib.ssm_scan_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                              _i64, _i64, _i64, _i64, ctypes.c_int, _vp, ctypes.c_size_t,
                              ctypes.POINTER(ScanOptions), _vp]
+lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
+lib.ssm_scan_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                     _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                     ctypes.POINTER(ScanOptions), _vp]
 lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
 lib.ssm_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
                                              ctypes.POINTER(ScanOptions)]
@@ -89,7 +94,7 @@ lib.ssm_abi_version.argtypes = []
 # SSM_SCAN_ABI_VERSION this binding's argument lists and ScanOptions follow; a library
 # built from other sources (a stale .so) is refused rather than called with the wrong
 # layout.
-ABI_VERSION = 4
+ABI_VERSION = 5
 if lib.ssm_abi_version() != ABI_VERSION:
     raise ImportError(f"{_LIB_PATH} has ABI version {lib.ssm_abi_version()}, this binding "
                       f"expects {ABI_VERSION}: rebuild the library")
@@ -225,6 +230,48 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
             _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, N,
             code, _ptr(workspace), 0 if workspace is None else workspace.numel(), opts, s))
+    return (y, h_final) if return_final_state else y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def ssm_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                         delta_softplus=True, h0=None, return_final_state=False, y=None,
+                         h_final=None, plan=0, chunk_len=0, stream=None, group_channels=0,
+                         reverse=False, accumulate=False):
+    """ssm_scan_fwd with the library's static scratch as its workspace (no workspace
+    argument; the C call allocates nothing). The outputs y / h_final are allocated here
+    only when not given."""
+    _dev(x, "x")
+    io = x.dtype
+    batch, dim, seqlen = x.shape
+    N = A.shape[-1]
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(A, "A", torch.float32, (dim, N))
+    _dev(B, "B", io, (batch, seqlen, N))
+    _dev(C, "C", io, (batch, seqlen, N))
+    _dev(D, "D", torch.float32, (dim,))
+    _dev(delta_bias, "delta_bias", torch.float32, (dim,))
+    _dev(h0, "h0", torch.float32, (batch, dim, N))
+    code = _dtype_code(x)
+    dev = x.device
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the y to add into")
+        y = torch.empty_like(x)
+    _dev(y, "y", io, x.shape)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _dev(h_final, "h_final", torch.float32, (batch, dim, N))
+    opts = _options(plan, chunk_len, None, group_channels, reverse, accumulate)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+        _check(lib.ssm_scan_fwd_noalloc(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(h_final), batch, seqlen, dim, N,
+            code, opts, s))
     return (y, h_final) if return_final_state else y
 
 

@@ -259,7 +259,8 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
                      int delta_softplus, const int32_t* cu_seqlens, int64_t nseq,
                      const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen,
                      int64_t dim, int64_t dstate, ssm_dtype io_dtype, void* workspace,
-                     size_t workspace_bytes, const ssm_scan_options* opts, void* stream) {
+                     size_t workspace_bytes, const ssm_scan_options* opts, void* stream,
+                     bool use_scratch = false) {
     const bool packed = cu_seqlens != nullptr;
     ssm::ScanPlan plan;
     ssm_status st = make_plan(batch, seqlen, dim, dstate, io_dtype, opts, &plan);
@@ -308,10 +309,21 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
         if (a.p && !aligned(a.p, a.align))
             return fail(SSM_ERR_UNSUPPORTED, "%s=%p is not %u-byte aligned", a.name, a.p,
                         (unsigned)a.align);
-    if (plan.ws_total > 0 && (!workspace || workspace_bytes < plan.ws_total))
+    // use_scratch (ssm_scan_fwd_noalloc): the workspace is the library's static scratch,
+    // looked up after every check below; it overlaps no caller buffer
+    if (use_scratch && plan.ws_total > ssm::kScratchBytes)
+        return fail(SSM_ERR_UNSUPPORTED,
+                    "this shape and plan need %zu bytes of workspace; the static scratch of "
+                    "ssm_scan_fwd_noalloc holds %zu (call ssm_scan_fwd with a workspace)",
+                    plan.ws_total, ssm::kScratchBytes);
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+    } else if (plan.ws_total > 0 && (!workspace || workspace_bytes < plan.ws_total)) {
         return fail(SSM_ERR_WORKSPACE_TOO_SMALL,
                     "workspace needs %zu bytes (got %zu at %p)", plan.ws_total,
                     workspace_bytes, workspace);
+    }
     const Region ry = region("y", y, io);
     const Region rhf = region("h_final", h_final, st_b);
     const Region rws = region("workspace", workspace, (int64_t)plan.ws_total);
@@ -371,6 +383,11 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
                         "save_workspace overlaps y, h_final or the workspace");
     }
 
+    if (use_scratch) {
+        const hipError_t e = ssm::scratch_address(static_cast<hipStream_t>(stream), &workspace);
+        if (e != hipSuccess)
+            return fail(SSM_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+    }
     ssm::ScanParams prm{};
     char* ws = static_cast<char*>(workspace);
     prm.x = x;
@@ -901,6 +918,21 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
         return scan_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, 0, h0, y,
                          h_final, batch, seqlen, dim, dstate, io_dtype, workspace,
                          workspace_bytes, opts, stream);
+    } catch (...) {
+        return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
+    }
+}
+
+ssm_status ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* D, const void* z,
+                                const float* delta_bias, int delta_softplus, const float* h0,
+                                void* y, float* h_final, int64_t batch, int64_t seqlen,
+                                int64_t dim, int64_t dstate, ssm_dtype io_dtype,
+                                const ssm_scan_options* opts, void* stream) {
+    try {
+        return scan_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, nullptr, 0, h0, y,
+                         h_final, batch, seqlen, dim, dstate, io_dtype, nullptr, 0, opts, stream,
+                         /*use_scratch=*/true);
     } catch (...) {
         return fail(SSM_ERR_INVALID_ARGUMENT, "internal error (exception)");
     }

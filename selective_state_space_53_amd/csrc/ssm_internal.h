@@ -9,6 +9,8 @@ namespace ssm {
 
 constexpr int kDState = 16;        // states per channel supported by the kernels
 constexpr int kTokenTile = 32;     // tokens per scan tile (chunk lengths are multiples)
+// Bytes of the static device scratch behind ssm_scan_fwd_noalloc (one copy per GPU).
+constexpr size_t kScratchBytes = size_t(32) << 20;
 
 struct ScanPlan {
     int group_channels = 64;  // channels per scan workgroup (32, 48, 64, 80 or 96)
@@ -136,6 +138,9 @@ hipError_t launch_carry(const float* A, const float* init, float* chunk_state,
 // The backward kernel (ev_begin / ev_end around it) and its reductions.
 hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t stream,
                            hipEvent_t ev_begin, hipEvent_t ev_end);
+// Device address of the static scratch (kScratchBytes) on the device of `stream` (the
+// current device for the null stream): looked up once per device, then kept.
+hipError_t scratch_address(hipStream_t stream, void** out);
 hipError_t launch_conv1d_fwd(const ConvParams& prm, bool bf16, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvParams& prm, bool bf16, hipStream_t stream);
 

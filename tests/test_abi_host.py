@@ -95,6 +95,32 @@ def test_scan_rejects_bad_options(b):
     assert scan(b, opts=ctypes.byref(b.ScanOptions(-32, 2, 0))) == 1
 
 
+def noalloc(b, batch=2, seqlen=64, dim=64, dstate=16, io=1, opts=None, **over):
+    p = dict(P)
+    p.update(over)
+    if opts == "chunks of 64":
+        opts = ctypes.byref(b.ScanOptions(64, 2, 0))
+    return b.lib.ssm_scan_fwd_noalloc(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                      p["z"], p["bias"], p.get("softplus", 1), p["h0"], p["y"],
+                                      p["hf"], batch, seqlen, dim, dstate, io, opts, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(dstate=8), 2), (dict(x=None), 1), (dict(y=None), 1),
+    (dict(softplus=2), 1), (dict(x=P["x"] + 8), 2), (dict(y=P["x"]), 1),
+    (dict(hf=P["h0"] + 16), 1),
+    # workspaces beyond the 32 MiB scratch: a million-token row (B/C widened: 128 MiB),
+    # and a forced chunked plan whose chunk states do not fit
+    (dict(batch=1, seqlen=1 << 20, dim=1536), 2),
+    (dict(batch=64, seqlen=4096, dim=1024, opts="chunks of 64"), 2),
+])
+def test_noalloc_rejects(b, kw, status):
+    """ssm_scan_fwd_noalloc: the checks of ssm_scan_fwd, and shapes whose workspace would not
+    fit the static scratch, are refused on the host before the scratch is looked up."""
+    assert noalloc(b, **kw) == status
+    assert b.ssm_last_error() != ""
+
+
 def test_workspace_query(b):
     # single pass: B and C widened to fp32, per state quad, tokens padded to 32
     assert b.ssm_scan_workspace_bytes(4, 2048, 5120, 16, 1) == 4 * 2048 * 32 * 4
