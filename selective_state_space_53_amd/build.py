@@ -27,7 +27,8 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
-KERNEL_SOURCES = ["ssm_kernels.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_noalloc.hip"]
+KERNEL_SOURCES = ["ssm_kernels.hip", "ssm_wavescan.hip", "ssm_conv.hip", "ssm_bwd.hip",
+                  "ssm_noalloc.hip"]
 
 
 def _run(cmd, verbose):

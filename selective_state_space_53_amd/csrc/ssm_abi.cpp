@@ -165,8 +165,8 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
             return fail(SSM_ERR_INVALID_ARGUMENT,
                         "ssm_scan_options.group_channels=%d not in {0, 32, 48, 64, 80, 96}",
                         (int)req_cg);
-        if (opts->plan < 0 || opts->plan > 2)
-            return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.plan=%d not in {0,1,2}",
+        if (opts->plan < 0 || opts->plan > 3)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.plan=%d not in {0,1,2,3}",
                         (int)opts->plan);
         if (opts->chunk_len < 0 || opts->chunk_len % ssm::kTokenTile != 0)
             return fail(SSM_ERR_INVALID_ARGUMENT,
@@ -183,6 +183,14 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     }
     if (batch * ((dim + 31) / 32) >= (int64_t(1) << 30))
         return fail(SSM_ERR_INVALID_ARGUMENT, "batch*dim too large");
+    if (req_plan == 3) {
+        // the wave-scan plan: one launch over every (batch, channel) row, no workspace
+        *plan = ssm::ScanPlan{};
+        plan->wavescan = 1;
+        plan->nchunks = 1;
+        plan->chunk_len = seqlen;
+        return SSM_OK;
+    }
     const int64_t lpad = (seqlen + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
 
     // Channels per workgroup and chunking: the choice with the lowest modelled time
@@ -357,6 +365,10 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
     if (h_final && overlaps(rws, rhf))
         return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps h_final");
 
+    if (plan.wavescan && (packed || (opts && opts->save_workspace)))
+        return fail(SSM_ERR_UNSUPPORTED,
+                    "ssm_scan_options.plan = 3 (wave scan) takes batch rows without "
+                    "save_workspace");
     // training: also save the checkpoints and q for the backward
     void* const save = opts ? opts->save_workspace : nullptr;
     if (opts && opts->saved)
@@ -430,12 +442,16 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
                 (long long)batch, (long long)seqlen, (long long)dim,
                 io_dtype == SSM_BF16 ? "bf16" : "f32", packed ? " packed" : "",
                 prm.reverse ? " reverse" : "", prm.accumulate ? " accumulate" : "",
-                plan.nchunks > 1 ? "chunked" : "single pass", plan.group_channels,
+                plan.wavescan ? "wave scan" : plan.nchunks > 1 ? "chunked" : "single pass",
+                plan.group_channels,
                 (long long)plan.ngroups, plan.nchunks, (long long)plan.chunk_len);
     hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->timing_begin) : nullptr;
     hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->timing_end) : nullptr;
-    const hipError_t e = ssm::launch_scan(plan, prm, B, C, io_dtype == SSM_BF16,
-                                          static_cast<hipStream_t>(stream), ev0, ev1);
+    const hipError_t e =
+        plan.wavescan ? ssm::launch_wavescan(prm, B, C, io_dtype == SSM_BF16,
+                                             static_cast<hipStream_t>(stream), ev0, ev1)
+                      : ssm::launch_scan(plan, prm, B, C, io_dtype == SSM_BF16,
+                                         static_cast<hipStream_t>(stream), ev0, ev1);
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return SSM_OK;
 }
@@ -544,6 +560,9 @@ ssm_status make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dst
                          ssm_dtype io_dtype, const ssm_scan_options* opts, BwdPlan* bp) {
     if (opts && opts->accumulate)
         return fail(SSM_ERR_UNSUPPORTED, "the backward scan takes no accumulate option");
+    if (opts && opts->plan == 3)
+        return fail(SSM_ERR_UNSUPPORTED,
+                    "the backward's checkpoint pass runs plan 1 or 2, not the wave scan (3)");
     if (opts && opts->save_workspace)
         return fail(SSM_ERR_INVALID_ARGUMENT,
                     "ssm_scan_options.save_workspace is an option of ssm_scan_fwd");

@@ -13,6 +13,8 @@ constexpr int kTokenTile = 32;     // tokens per scan tile (chunk lengths are mu
 constexpr size_t kScratchBytes = size_t(32) << 20;
 
 struct ScanPlan {
+    int wavescan = 0;         // 1: the lanes-over-time kernel with the wave prefix combine
+                              // (ssm_wavescan.hip; no workspace); 0: the plans below
     int group_channels = 64;  // channels per scan workgroup (32, 48, 64, 80 or 96)
     int64_t ngroups = 0;      // batch * ceil(dim / group_channels)
     int nchunks = 1;        // 1 = single pass
@@ -123,6 +125,9 @@ struct BwdParams {
 // that writes y.
 hipError_t launch_scan(const ScanPlan& plan, const ScanParams& prm, const void* B, const void* C,
                        bool bf16, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+// The wave-scan plan: one launch, B and C read directly (ev_begin / ev_end around it).
+hipError_t launch_wavescan(const ScanParams& prm, const void* B, const void* C, bool bf16,
+                           hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
 // B and C widened to fp32 into bcq ([batch][8][lpad][4], the scan's layout) on its own:
 // the backward runs it when the training forward saved the checkpoints.
 hipError_t launch_bc_widen(const void* B, const void* C, float* bcq, int64_t batch,

@@ -89,7 +89,7 @@ def test_scan_rejects_bad_options(b):
     assert scan(b, opts=ctypes.byref(b.ScanOptions(48, 2, 0))) == 1   # not a multiple of 32
     assert scan(b, opts=ctypes.byref(b.ScanOptions(0, 0, 0, None, None, 2, 0))) == 1  # reverse
     assert scan(b, opts=ctypes.byref(b.ScanOptions(0, 0, 0, None, None, 0, -1))) == 1  # accumulate
-    assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 3, 0))) == 1   # unknown plan
+    assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 4, 0))) == 1   # unknown plan
     assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 2, 40))) == 1  # group size
     assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 2, 112))) == 1
     assert scan(b, opts=ctypes.byref(b.ScanOptions(-32, 2, 0))) == 1

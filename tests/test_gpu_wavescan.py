@@ -1,0 +1,188 @@
+"""GPU parity of the wave-scan plan (ssm_scan_options.plan = 3: the lanes of a wave split
+the sequence and are joined by a DPP prefix combine of (decay, input) pairs), through the
+C ABI, against the fp64 oracle.
+
+Every row of ragged shapes in both directions, with and without h0, gate and skip; the
+Mamba-2.8B and 130M layer shapes on every row; the million-token row on sampled rows;
+integer-exact inputs bit for bit at every lane (8-token) and segment (512-token) edge;
+the bidirectional sum; determinism, causality and in-place resume.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+from tests.test_gpu_scan import _integer_problem
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+WAVE = 3        # ssm_scan_options.plan of the wave scan
+SEG = 512       # tokens per segment (64 lanes x 8)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_53_amd import binding  # noqa: F401  (fails loudly if unbuilt)
+
+
+VARIANTS = [dict(use_z=True, use_D=True), dict(use_z=False, use_D=False)]
+
+
+def _oracle(inp, reverse, **kw):
+    if not reverse:
+        return parity.oracle_full(inp, **kw)
+    use_z, use_D = kw.get("use_z", True), kw.get("use_D", True)
+    return oracle.Oracle().scan_reverse(
+        inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"] if use_D else None,
+        z=inp["z"] if use_z else None, delta_bias=inp["delta_bias"], h0=kw.get("h0"),
+        nthreads=parity.threads())
+
+
+RAGGED = [
+    # (batch, seqlen, dim, io)
+    (1, 256, 16, "f32"),      # the small configuration: one partial segment
+    (2, 1000, 200, "bf16"),   # two segments, the second ragged; 13 groups of 16 rows
+    (1, 333, 70, "bf16"),     # rows not 16-byte aligned: element-wise loads and stores
+    (3, 1, 5, "f32"),
+    (1, 33, 65, "f32"),
+    (2, 1537, 40, "bf16"),    # four segments, one token in the last
+    (1, 4103, 130, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_wavescan_ragged_all_rows(shape, reverse):
+    batch, L, dim, io = shape
+    cfg = synth.ScanConfig("wave", batch, L, dim, io=io, seed=800 + L)
+    say("case wavescan ragged", shape, "reverse" if reverse else "causal")
+    inp = synth.scan_inputs(cfg, DEV)
+    gen = torch.Generator(device="cpu").manual_seed(L)
+    h0 = torch.randn((batch, dim, 16), generator=gen).to(DEV)
+    for var in VARIANTS:
+        for hh in (None, h0):
+            y, hf = parity.gpu_scan(inp, h0=hh, plan=WAVE, reverse=reverse, **var)
+            torch.cuda.synchronize()
+            yr, hr = _oracle(inp, reverse, h0=hh, **var)
+            ey, eh = parity.rowwise_err(y, yr), parity.rowwise_err(hf, hr)
+            say(f"  {var} h0={hh is not None}: y {ey:.3e} h {eh:.3e}")
+            assert ey <= parity.TOL[io] and eh <= parity.TOL[io]
+
+
+@pytest.mark.parametrize("name", ["m2p8", "m130"])
+@pytest.mark.parametrize("var", VARIANTS, ids=["gated", "scan_only"])
+def test_wavescan_layer_shapes_every_row(name, var):
+    cfg = synth.shrink(synth.CONFIGS[name], final_state=True)
+    say("case wavescan full size", name, var)
+    inp = synth.scan_inputs(cfg, DEV)
+    y, hf = parity.gpu_scan(inp, plan=WAVE, **var)
+    torch.cuda.synchronize()
+    yr, hr = parity.oracle_full(inp, **var)
+    ey, eh = parity.rowwise_err(y, yr), parity.rowwise_err(hf, hr)
+    say(f"  {name} {var}: every row: y {ey:.3e} h_final {eh:.3e}")
+    assert ey <= parity.TOL[cfg.io] and eh <= parity.TOL[cfg.io]
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_wavescan_million_tokens_sampled_rows(reverse):
+    cfg = synth.CONFIGS["long"]
+    say("case wavescan long", "reverse" if reverse else "causal")
+    inp = synth.scan_inputs(cfg, DEV)
+    y, hf = parity.gpu_scan(inp, plan=WAVE, reverse=reverse)
+    torch.cuda.synchronize()
+    rb, rd = parity.sample_rows(cfg.batch, cfg.dim, 24, seed=cfg.seed + 3)
+    if reverse:
+        yr, hr = parity.oracle_reverse_rows(inp, rb, rd)
+    else:
+        yr, hr = parity.oracle_rows(inp, rb, rd)
+    sel = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
+    ey, eh = parity.rowwise_err(y[sel], yr), parity.rowwise_err(hf[sel], hr)
+    say(f"  long: rows {len(rb)} y {ey:.3e} h {eh:.3e}")
+    assert ey <= parity.TOL[cfg.io] and eh <= parity.TOL[cfg.io]
+
+
+EXACT = [(1, 1, 3, "bf16"), (1, 7, 20, "f32"), (1, 9, 20, "bf16"), (1, 511, 17, "f32"),
+         (1, 512, 17, "bf16"), (1, 513, 17, "bf16"), (2, 1025, 33, "f32"),
+         (1, 5000, 16, "bf16")]
+
+
+@pytest.mark.parametrize("case", EXACT, ids=lambda c: "b{}_L{}_d{}_{}".format(*c))
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_wavescan_lane_and_segment_edges_bit_exact(case, reverse):
+    """A = 0, Delta = 1: integer states, exact in any association order, so the wave
+    scan's lane folds, DPP levels, exclusive shift and segment carries must reproduce the
+    oracle bit for bit; impulses sit on every lane (8) and segment (512) edge."""
+    batch, L, dim, io = case
+    say("case wavescan exact", case, reverse)
+    edges = set()
+    for m in range(0, L // 8 + 2):
+        edges.update((8 * m - 1, 8 * m))
+    for m in range(0, L // SEG + 2):
+        edges.update((SEG * m - 1, SEG * m, SEG * m + 1))
+    edges = [e for e in edges if 0 <= e < L] + [L - 1]
+    inp = _integer_problem(batch, L, dim, io, seed=L + (7 if reverse else 0), impulses=edges)
+    gen = torch.Generator(device="cpu").manual_seed(L)
+    h0 = torch.randint(-3, 4, (batch, dim, 16), generator=gen).float().to(DEV)
+    y, hf = parity.gpu_scan(inp, use_z=False, h0=h0, plan=WAVE, softplus=False, bias=False,
+                            reverse=reverse)
+    torch.cuda.synchronize()
+    run = oracle.Oracle().scan_reverse if reverse else oracle.Oracle().scan
+    yr, hr = run(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                 delta_softplus=False, h0=h0, nthreads=parity.threads())
+    assert np.array_equal(oracle.f64(y), yr)
+    assert np.array_equal(oracle.f64(hf), hr)
+
+
+def test_wavescan_bidirectional_sum():
+    cfg = synth.ScanConfig("wave_bidir", 2, 1300, 90, io="f32", seed=77)
+    inp = synth.scan_inputs(cfg, DEV)
+    from selective_state_space_53_amd import binding
+    kw = dict(D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], plan=WAVE)
+    y = binding.ssm_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], **kw)
+    binding.ssm_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], y=y,
+                         reverse=True, accumulate=True, **kw)
+    torch.cuda.synchronize()
+    y1, _ = parity.oracle_full(inp)
+    y2, _ = _oracle(inp, True)
+    assert parity.rowwise_err(y, y1 + y2) <= 1e-5
+
+
+def test_wavescan_deterministic_causal_in_place():
+    cfg = synth.ScanConfig("wave_det", 2, 1500, 130, io="bf16", seed=12)
+    inp = synth.scan_inputs(cfg, DEV)
+    y1, h1 = parity.gpu_scan(inp, plan=WAVE)
+    y2, h2 = parity.gpu_scan(inp, plan=WAVE)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    t0 = 700
+    inp2 = dict(inp)
+    inp2["x"] = inp["x"].clone()
+    inp2["x"][:, :, t0] += 1.0
+    y3, _ = parity.gpu_scan(inp2, plan=WAVE)
+    torch.cuda.synchronize()
+    assert torch.equal(y3[:, :, :t0], y1[:, :, :t0])
+    assert not torch.equal(y3[:, :, t0], y1[:, :, t0])
+    # in place: h_final == h0
+    from selective_state_space_53_amd import binding
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    h0 = torch.randn((2, 130, 16), generator=gen).to(DEV)
+    keep = h0.clone()
+    y4, hf = binding.ssm_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                  D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], h0=h0,
+                                  h_final=h0, return_final_state=True, plan=WAVE)
+    torch.cuda.synchronize()
+    yr, hr = parity.oracle_full(inp, h0=keep)
+    assert hf.data_ptr() == h0.data_ptr()
+    assert parity.rowwise_err(y4, yr) <= 2e-2 and parity.rowwise_err(h0, hr) <= 2e-2
