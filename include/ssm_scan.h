@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 5
+#define SSM_SCAN_ABI_VERSION 6
 
 typedef enum {
     SSM_OK = 0,
@@ -117,6 +117,16 @@ typedef struct {
                            and reverse, and the backward skips its own forward pass; nothing
                            checks that they match (stale contents give wrong gradients).
                            0 = the backward recomputes them.                              */
+    int32_t structured_a; /* ssm_scan_fwd / ssm_scan_varlen_fwd with plan = 3 (the wave scan):
+                           1 = for every channel d whose A row satisfies A[d,n] ==
+                           (n+1)*A[d,0] exactly (fp32; checked on the device, per channel),
+                           take the decays as powers exp(Delta*A[d,0])^(n+1) -- one exp per
+                           (token, channel) and a multiply per state instead of one exp per
+                           (token, channel, state); other channels take the general path.
+                           The results differ from the general path by rounding only (the
+                           powers accumulate up to 16 roundings and multiply the exp's own
+                           relative error by n+1). 0 = general path everywhere. Any other
+                           plan with structured_a = 1 returns SSM_ERR_UNSUPPORTED.       */
 } ssm_scan_options;
 
 /*

@@ -35,7 +35,8 @@ class ScanOptions(ctypes.Structure):
                 ("timing_end", ctypes.c_void_p), ("reverse", ctypes.c_int32),
                 ("accumulate", ctypes.c_int32), ("bwd_group_channels", ctypes.c_int32),
                 ("bwd_chunk_len", ctypes.c_int64), ("save_workspace", ctypes.c_void_p),
-                ("save_workspace_bytes", ctypes.c_size_t), ("saved", ctypes.c_int32)]
+                ("save_workspace_bytes", ctypes.c_size_t), ("saved", ctypes.c_int32),
+                ("structured_a", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -94,7 +95,7 @@ lib.ssm_abi_version.argtypes = []
 # SSM_SCAN_ABI_VERSION this binding's argument lists and ScanOptions follow; a library
 # built from other sources (a stale .so) is refused rather than called with the wrong
 # layout.
-ABI_VERSION = 5
+ABI_VERSION = 6
 if lib.ssm_abi_version() != ABI_VERSION:
     raise ImportError(f"{_LIB_PATH} has ABI version {lib.ssm_abi_version()}, this binding "
                       f"expects {ABI_VERSION}: rebuild the library")
@@ -151,16 +152,16 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 def _options(plan: int, chunk_len: int, events=None, group_channels: int = 0,
              reverse=False, accumulate=False, bwd_group_channels: int = 0, bwd_chunk_len: int = 0,
-             save=None, saved=False):
+             save=None, saved=False, structured_a=False):
     if (plan == 0 and chunk_len == 0 and events is None and group_channels == 0
             and not reverse and not accumulate and bwd_group_channels == 0
-            and bwd_chunk_len == 0 and save is None and not saved):
+            and bwd_chunk_len == 0 and save is None and not saved and not structured_a):
         return None
     ev0, ev1 = (None, None) if events is None else events
     return ctypes.byref(ScanOptions(chunk_len, plan, group_channels, ev0, ev1, int(bool(reverse)),
                                     int(bool(accumulate)), bwd_group_channels, bwd_chunk_len,
                                     _ptr(save), 0 if save is None else save.numel(),
-                                    int(bool(saved))))
+                                    int(bool(saved)), int(bool(structured_a))))
 
 
 def ssm_scan_workspace_bytes(batch, seqlen, dim, dstate, io_dtype, plan=0, chunk_len=0,
@@ -187,7 +188,7 @@ def ssm_scan_varlen_workspace_bytes(total, dim, dstate, io_dtype, plan=0, chunk_
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                  h0=None, return_final_state=False, y=None, h_final=None, workspace=None,
                  plan=0, chunk_len=0, stream=None, timing_events=None, group_channels=0,
-                 reverse=False, accumulate=False, save_for_backward=None):
+                 reverse=False, accumulate=False, save_for_backward=None, structured_a=False):
     """x, delta, z: [batch][dim][seqlen]; B, C: [batch][seqlen][16]; A: [dim][16];
     D, delta_bias: [dim]; h0: [batch][dim][16]. Returns y (and h_final).
     reverse: anti-causal scan; accumulate: add into the given y instead of writing it.
@@ -220,7 +221,7 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     _dev(h_final, "h_final", torch.float32, (batch, dim, N))
     _dev(save_for_backward, "save_for_backward", torch.uint8)
     opts = _options(plan, chunk_len, timing_events, group_channels, reverse, accumulate,
-                    save=save_for_backward)
+                    save=save_for_backward, structured_a=structured_a)
     ws_bytes = lib.ssm_scan_workspace_bytes(batch, seqlen, dim, N, code, opts)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

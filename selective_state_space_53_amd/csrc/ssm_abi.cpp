@@ -178,6 +178,12 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
         if (opts->accumulate != 0 && opts->accumulate != 1)
             return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.accumulate=%d not 0 or 1",
                         (int)opts->accumulate);
+        if (opts->structured_a != 0 && opts->structured_a != 1)
+            return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.structured_a=%d not 0 or 1",
+                        (int)opts->structured_a);
+        if (opts->structured_a && opts->plan != 3)
+            return fail(SSM_ERR_UNSUPPORTED,
+                        "ssm_scan_options.structured_a needs plan = 3 (the wave scan)");
         req_plan = opts->plan;
         req_chunk = opts->chunk_len;
     }
@@ -430,6 +436,7 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
     prm.aligned = ((seqlen * elem) % 16) == 0;
     prm.reverse = opts ? opts->reverse : 0;
     prm.accumulate = opts ? opts->accumulate : 0;
+    prm.structured_a = opts ? opts->structured_a : 0;
     if (save) {
         prm.ckpt = static_cast<float*>(save);
         prm.nckpt = (seqlen + kBwdTile - 1) / kBwdTile;

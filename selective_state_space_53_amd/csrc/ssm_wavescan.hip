@@ -16,14 +16,15 @@
 //    the K consecutive tokens l K .. l K + K - 1 of the segment (in scan order).
 //  * Per segment, once per token: Delta = softplus(delta + bias), u = Delta x (each token
 //    by the one lane that owns it, no sharing). Then for each of the 16 states:
-//      1. the lane's K pairs (a_j, b_j) folded in order, keeping the in-lane prefixes;
+//      1. the composite of the lane's K pairs (a_j, b_j): the decays' product taken as
+//         one exp of the lane's summed Delta, the inputs folded in order;
 //      2. an inclusive scan of the lanes' folds across the 64 lanes (six DPP levels:
 //         row_shr 1, 2, 4, 8, then row_bcast 15 and 31), shifted by one lane
 //         (wave_shr 1) to the exclusive prefix;
 //      3. the state entering the lane = that prefix applied to the state entering the
 //         segment (a wave-uniform value, carried in a scalar register);
-//      4. every token's state from the lane's carry-in and its in-lane prefix, and the
-//         readout y += C_t[n] h_t;
+//      4. the lane's K tokens re-run in order from that state, and the readout
+//         y += C_t[n] h_t;
 //      5. the state after the segment (lane 63's last token) carried to the next.
 //  * Then D x, the SiLU gate, the io-dtype store, and after the last segment h_final.
 //
@@ -179,7 +180,7 @@ __device__ __forceinline__ void wave_scan2(float& a0, float& b0, float& a1, floa
 // already free of conflicts and the flip keeps it so).
 __device__ __forceinline__ int swz(int q) { return q ^ ((((q >> 5) ^ (q >> 6)) & 1) << 2); }
 
-template <typename IO, bool REV, int K, int W>
+template <typename IO, bool REV, bool STRUCT, int K, int W>
 __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                                                          const IO* __restrict__ Bg,
                                                          const IO* __restrict__ Cg) {
@@ -210,6 +211,15 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
     for (int n = 0; n < kDState; ++n) {
         A2[n] = p.A[(valid ? d : 0) * kDState + n] * kLog2e;
         hc[n] = (p.h0 && valid) ? p.h0[row * kDState + n] : 0.0f;
+    }
+    // structured A (opt-in): this row's A[n] == (n+1) A[0] exactly, so exp(Delta A[n]) =
+    // r^(n+1) with r = exp(Delta A[0]) (wave-uniform; rows that fail take the general path)
+    bool row_struct = STRUCT;
+    {
+        const float a0 = p.A[(valid ? d : 0) * kDState];
+#pragma unroll
+        for (int n = 1; n < kDState; ++n)
+            row_struct = row_struct && (p.A[(valid ? d : 0) * kDState + n] == (float)(n + 1) * a0);
     }
     const float bias = (p.bias && valid) ? p.bias[d] : 0.0f;
     const float Dd = (p.D && valid) ? p.D[d] : 0.0f;
@@ -271,6 +281,7 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
     };
 
     // ---- this lane's x, delta, z of a segment (raw, one segment ahead)
+    constexpr bool kPrefetchRows = sizeof(IO) == 2;
     RawK<IO, K> rx, rd, rz;
     auto row_load = [&](int s) {
         const int64_t m0 = lane_base(s, lane);
@@ -293,9 +304,13 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
         const int nmem = (int)((L - m0 < K) ? (L - m0 < 0 ? 0 : L - m0) : K);  // valid tokens
         const bool vec = p.aligned && nmem == K;
         if (it + 1 < nseg) stage_load(seg_of(it + 1));
-        if (valid) {
+        if (!kPrefetchRows && valid && it > 0) row_load(s);
+        // the segment's compute for this wave's row, on the general or the structured path
+        auto segment = [&](auto path) {
+            constexpr bool S = decltype(path)::value;
             // per token, in scan order j (memory element e = j, or K-1-j for REV)
             float dl[K], u[K];
+            float dsum = 0.0f;   // the lane's sum of Delta: its total decay is exp(A dsum)
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 const int e = REV ? K - 1 - j : j;
@@ -304,20 +319,33 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                 delta = (e < nmem) ? delta : 0.0f;   // padding tokens: (1, 0), the identity
                 dl[j] = delta;
                 u[j] = delta * rx.get(e);
+                dsum += delta;
             }
-            // the raw x and z of this segment stay for the epilogue; the next segment's
-            // rows are loaded into the other set
+            // the raw x and z of this segment stay for the epilogue; with bf16 rows the next
+            // segment's rows are loaded now into the other set (with fp32 rows, twice the
+            // registers, they are loaded at the top of the next segment instead)
             RawK<IO, K> cx = rx, cz = rz;
-            if (it + 1 < nseg) row_load(seg_of(it + 1));
+            if (kPrefetchRows && it + 1 < nseg) row_load(seg_of(it + 1));
             float y[K];
 #pragma unroll
             for (int j = 0; j < K; ++j) y[j] = 0.0f;
+            // structured rows: per token r = exp(Delta A[0]), per lane R = exp(dsum A[0]);
+            // pw / fpw hold the current powers (r^(n+1), R^(n+1)) from state to state
+            float rt[K], pw[K], Rt = 0.0f, fpw = 0.0f;
+            if constexpr (S) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    rt[j] = fast_exp2(dl[j] * A2[0]);
+                    pw[j] = 0.0f;
+                }
+                Rt = fast_exp2(dsum * A2[0]);
+            }
             const int lq = lane * K;
             const int m = ((lane >> 2) ^ (lane >> 3)) & 1;   // swz(lq + 4g) = (lq + 4g) ^ (m << 2)
             // two states at a time: their folds, scans and fix-ups interleave
 #pragma unroll
             for (int n = 0; n < kDState; n += 2) {
-                float a[2][K], bb[2][K];
+                float a[2][K], bb[2][K], fa[2], fb[2];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const float* Bn = &sBC[buf][0][n + r][0];
@@ -327,28 +355,38 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                         const float4 bq = *reinterpret_cast<const float4*>(Bn + ((lq + 4 * g) ^ (m << 2)));
                         Bv[4 * g] = bq.x; Bv[4 * g + 1] = bq.y; Bv[4 * g + 2] = bq.z; Bv[4 * g + 3] = bq.w;
                     }
-                    // 1. the lane's pairs and their in-lane prefixes
+                    // 1. the lane's pairs, and their composite: the decay product as one
+                    // exp of the summed Delta, the input folded in order. Structured rows:
+                    // the decays and their product are the next powers of r and of R.
 #pragma unroll
                     for (int j = 0; j < K; ++j) {
-                        a[r][j] = fast_exp2(dl[j] * A2[n + r]);
+                        if constexpr (S) {
+                            a[r][j] = (n + r == 0) ? rt[j] : pw[j] * rt[j];
+                            pw[j] = a[r][j];
+                        } else {
+                            a[r][j] = fast_exp2(dl[j] * A2[n + r]);
+                        }
                         bb[r][j] = u[j] * Bv[j];
                     }
+                    float f = bb[r][0];
 #pragma unroll
-                    for (int j = 1; j < K; ++j) {
-                        bb[r][j] = __builtin_fmaf(a[r][j], bb[r][j - 1], bb[r][j]);
-                        a[r][j] = a[r][j] * a[r][j - 1];
+                    for (int j = 1; j < K; ++j) f = __builtin_fmaf(a[r][j], f, bb[r][j]);
+                    fb[r] = f;
+                    if constexpr (S) {
+                        fa[r] = (n + r == 0) ? Rt : fpw * Rt;
+                        fpw = fa[r];
+                    } else {
+                        fa[r] = fast_exp2(dsum * A2[n + r]);
                     }
                 }
-                // 2. the exclusive prefix of the lanes' folds
-                float sa0 = a[0][K - 1], sb0 = bb[0][K - 1], sa1 = a[1][K - 1], sb1 = bb[1][K - 1];
+                // 2. the exclusive prefix of the lanes' composites
                 float ea0, eb0, ea1, eb1;
-                wave_scan2(sa0, sb0, sa1, sb1, ea0, eb0, ea1, eb1);
-                // 3. the state entering this lane's tokens; 4. every token's state and the
-                // readout; 5. the state after the segment (lane 63's last token)
+                wave_scan2(fa[0], fb[0], fa[1], fb[1], ea0, eb0, ea1, eb1);
+                // 3. the state entering this lane's tokens; 4. every token's state, in order,
+                // and the readout; 5. the state after the segment (lane 63's last token)
                 const float ea[2] = {ea0, ea1}, eb[2] = {eb0, eb1};
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const float hin = __builtin_fmaf(ea[r], hc[n + r], eb[r]);
                     const float* Cn = &sBC[buf][1][n + r][0];
                     float Cv[K];
 #pragma unroll
@@ -356,15 +394,14 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                         const float4 cq = *reinterpret_cast<const float4*>(Cn + ((lq + 4 * g) ^ (m << 2)));
                         Cv[4 * g] = cq.x; Cv[4 * g + 1] = cq.y; Cv[4 * g + 2] = cq.z; Cv[4 * g + 3] = cq.w;
                     }
-                    float hl = 0.0f;
+                    float h = __builtin_fmaf(ea[r], hc[n + r], eb[r]);
 #pragma unroll
                     for (int j = 0; j < K; ++j) {
-                        const float h = __builtin_fmaf(a[r][j], hin, bb[r][j]);
+                        h = __builtin_fmaf(a[r][j], h, bb[r][j]);
                         y[j] = __builtin_fmaf(Cv[j], h, y[j]);
-                        hl = h;
                     }
                     hc[n + r] = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hl), 63));
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, h), 63));
                 }
                 // the readout sums are materialized here: otherwise the compiler may sink
                 // every state's readout into the epilogue and keep all 16 x K states alive
@@ -390,6 +427,14 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                 for (int e = 0; e < K; ++e) o[e] += old.get(e);
             }
             if (nmem > 0) StoreK<IO, K>::store(yr + m0, vec, nmem, o);
+                };
+        if (valid) {
+            if constexpr (STRUCT) {
+                if (row_struct) segment(std::true_type{});
+                else segment(std::false_type{});
+            } else {
+                segment(std::false_type{});
+            }
         }
         if (it + 1 < nseg) stage_store(buf ^ 1);
         __syncthreads();
@@ -409,8 +454,12 @@ hipError_t launch_wavescan_t(const ScanParams& prm, const void* B, const void* C
     ScanParams p = prm;
     p.groups_per_batch = (int32_t)((p.dim + W - 1) / W);
     const dim3 grid((unsigned)(p.batch * p.groups_per_batch));
-    hipLaunchKernelGGL((wavescan_kernel<IO, REV, K, W>), grid, dim3(W * 64), 0, stream, p,
-                       static_cast<const IO*>(B), static_cast<const IO*>(C));
+    if (p.structured_a)
+        hipLaunchKernelGGL((wavescan_kernel<IO, REV, true, K, W>), grid, dim3(W * 64), 0, stream,
+                           p, static_cast<const IO*>(B), static_cast<const IO*>(C));
+    else
+        hipLaunchKernelGGL((wavescan_kernel<IO, REV, false, K, W>), grid, dim3(W * 64), 0, stream,
+                           p, static_cast<const IO*>(B), static_cast<const IO*>(C));
     return hipGetLastError();
 }
 

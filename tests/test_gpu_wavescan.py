@@ -186,3 +186,99 @@ def test_wavescan_deterministic_causal_in_place():
     yr, hr = parity.oracle_full(inp, h0=keep)
     assert hf.data_ptr() == h0.data_ptr()
     assert parity.rowwise_err(y4, yr) <= 2e-2 and parity.rowwise_err(h0, hr) <= 2e-2
+
+
+# ---------------------------------------------------------------- structured A (opt-in)
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "b{}_L{}_d{}_{}".format(*s))
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_structured_a_ragged_all_rows(shape, reverse):
+    """structured_a = 1 on the configurations' A = -(n+1) (every row structured: decays as
+    powers of exp(Delta A[0])), against the fp64 oracle at the io tolerance, every row."""
+    batch, L, dim, io = shape
+    cfg = synth.ScanConfig("wave_struct", batch, L, dim, io=io, seed=900 + L)
+    say("case structured A ragged", shape, "reverse" if reverse else "causal")
+    inp = synth.scan_inputs(cfg, DEV)
+    gen = torch.Generator(device="cpu").manual_seed(L + 1)
+    h0 = torch.randn((batch, dim, 16), generator=gen).to(DEV)
+    for var in VARIANTS:
+        y, hf = parity.gpu_scan(inp, h0=h0, plan=WAVE, reverse=reverse, structured_a=True, **var)
+        torch.cuda.synchronize()
+        yr, hr = _oracle(inp, reverse, h0=h0, **var)
+        ey, eh = parity.rowwise_err(y, yr), parity.rowwise_err(hf, hr)
+        say(f"  {var}: y {ey:.3e} h {eh:.3e}")
+        assert ey <= parity.TOL[io] and eh <= parity.TOL[io]
+
+
+@pytest.mark.parametrize("name", ["m2p8", "m130"])
+def test_structured_a_layer_shapes_every_row(name):
+    cfg = synth.shrink(synth.CONFIGS[name], final_state=True)
+    say("case structured A full size", name)
+    inp = synth.scan_inputs(cfg, DEV)
+    for var in VARIANTS:
+        y, hf = parity.gpu_scan(inp, plan=WAVE, structured_a=True, **var)
+        torch.cuda.synchronize()
+        yr, hr = parity.oracle_full(inp, **var)
+        ey, eh = parity.rowwise_err(y, yr), parity.rowwise_err(hf, hr)
+        say(f"  {name} {var}: every row: y {ey:.3e} h_final {eh:.3e}")
+        assert ey <= parity.TOL[cfg.io] and eh <= parity.TOL[cfg.io]
+
+
+def test_structured_a_million_tokens_sampled_rows():
+    cfg = synth.CONFIGS["long"]
+    say("case structured A long")
+    inp = synth.scan_inputs(cfg, DEV)
+    y, hf = parity.gpu_scan(inp, plan=WAVE, structured_a=True)
+    torch.cuda.synchronize()
+    rb, rd = parity.sample_rows(cfg.batch, cfg.dim, 24, seed=cfg.seed + 5)
+    yr, hr = parity.oracle_rows(inp, rb, rd)
+    sel = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
+    ey, eh = parity.rowwise_err(y[sel], yr), parity.rowwise_err(hf[sel], hr)
+    say(f"  long structured: y {ey:.3e} h {eh:.3e}")
+    assert ey <= parity.TOL[cfg.io] and eh <= parity.TOL[cfg.io]
+
+
+def test_structured_a_falls_back_on_unstructured_rows():
+    """Rows whose A breaks A[n] == (n+1) A[0] (a perturbed entry, random values, a row off
+    by one ulp) take the general path; every row must still match the oracle, and the rows
+    that did take the structured path match it too. fp32 io at the 1e-5 bar."""
+    cfg = synth.ScanConfig("wave_mixed", 2, 1300, 48, io="f32", seed=31)
+    inp = synth.scan_inputs(cfg, DEV)
+    A = inp["A"].clone()
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    A[5] = -torch.rand(16, generator=gen).to(DEV) * 3.0 - 0.1           # random row
+    A[9, 7] *= 1.5                                                       # one entry off
+    A[17, 15] = torch.nextafter(A[17, 15], torch.tensor(0.0, device=DEV))  # one ulp off
+    A[30] = -0.37 * torch.arange(1, 17, device=DEV, dtype=torch.float32)  # structured, A0 != -1
+    inp = dict(inp, A=A)
+    y, hf = parity.gpu_scan(inp, plan=WAVE, structured_a=True)
+    torch.cuda.synchronize()
+    yr, hr = parity.oracle_full(inp)
+    ey, eh = parity.rowwise_err(y, yr), parity.rowwise_err(hf, hr)
+    say(f"  mixed rows: y {ey:.3e} h {eh:.3e}")
+    assert ey <= 1e-5 and eh <= 1e-5
+    # the general path gives bit-identical results on the unstructured rows
+    y0, h0 = parity.gpu_scan(inp, plan=WAVE)
+    torch.cuda.synchronize()
+    for d in (5, 9, 17):
+        assert torch.equal(y[:, d], y0[:, d]) and torch.equal(hf[:, d], h0[:, d]), d
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_structured_a_edges_bit_exact(reverse):
+    """A = 0 satisfies A[n] == (n+1) A[0]: the structured path with integer inputs must
+    reproduce the oracle bit for bit at lane and segment edges."""
+    batch, L, dim, io = 2, 1537, 24, "bf16"
+    edges = sorted({e for m in range(L // 8 + 2) for e in (8 * m - 1, 8 * m)} |
+                   {e for m in range(L // SEG + 2) for e in (SEG * m - 1, SEG * m, SEG * m + 1)})
+    edges = [e for e in edges if 0 <= e < L]
+    inp = _integer_problem(batch, L, dim, io, seed=5 + reverse, impulses=edges)
+    gen = torch.Generator(device="cpu").manual_seed(2)
+    h0 = torch.randint(-3, 4, (batch, dim, 16), generator=gen).float().to(DEV)
+    y, hf = parity.gpu_scan(inp, use_z=False, h0=h0, plan=WAVE, softplus=False, bias=False,
+                            reverse=reverse, structured_a=True)
+    torch.cuda.synchronize()
+    run = oracle.Oracle().scan_reverse if reverse else oracle.Oracle().scan
+    yr, hr = run(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                 delta_softplus=False, h0=h0, nthreads=parity.threads())
+    assert np.array_equal(oracle.f64(y), yr)
+    assert np.array_equal(oracle.f64(hf), hr)
