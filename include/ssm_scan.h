@@ -74,8 +74,9 @@ typedef struct {
                            pass over chunks, then the chunks again with their carried-in
                            state), 3 = wave scan (the lanes of a wave split the sequence
                            and are joined by a prefix combine of (decay, input) pairs;
-                           one sweep per (batch, channel) row, no workspace; batch rows
-                           of ssm_scan_fwd without save_workspace only).                 */
+                           one sweep per (batch, channel) row; the workspace holds B and C
+                           widened to fp32 in its own layout, batch*ceil(seqlen/512)*64 KB;
+                           batch rows of ssm_scan_fwd without save_workspace only).      */
     int32_t group_channels; /* channels per workgroup: 0 = library choice, else one of
                            32, 48, 64, 80, 96 (all 16 states of a channel stay in one
                            workgroup; 2 states per lane, group_channels/8 waves)        */

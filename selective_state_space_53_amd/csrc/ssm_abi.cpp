@@ -190,11 +190,18 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     if (batch * ((dim + 31) / 32) >= (int64_t(1) << 30))
         return fail(SSM_ERR_INVALID_ARGUMENT, "batch*dim too large");
     if (req_plan == 3) {
-        // the wave-scan plan: one launch over every (batch, channel) row, no workspace
+        // the wave-scan plan: B/C widened into the workspace in its staged layout (64 KB
+        // per batch row and 512-token segment), then one launch over every row
         *plan = ssm::ScanPlan{};
         plan->wavescan = 1;
         plan->nchunks = 1;
         plan->chunk_len = seqlen;
+        const int64_t nseg = (seqlen + ssm::kWaveSegTokens - 1) / ssm::kWaveSegTokens;
+        int64_t bytes;
+        if (!bytes4(batch, nseg, 2 * ssm::kDState * ssm::kWaveSegTokens, 4, &bytes))
+            return fail(SSM_ERR_INVALID_ARGUMENT, "workspace size overflows");
+        plan->ws_bcq = 0;
+        plan->ws_total = align_up((size_t)bytes, 256);
         return SSM_OK;
     }
     const int64_t lpad = (seqlen + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;

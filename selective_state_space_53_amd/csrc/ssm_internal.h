@@ -9,6 +9,7 @@ namespace ssm {
 
 constexpr int kDState = 16;        // states per channel supported by the kernels
 constexpr int kTokenTile = 32;     // tokens per scan tile (chunk lengths are multiples)
+constexpr int kWaveSegTokens = 512;   // tokens per segment of the wave scan (64 lanes x 8)
 // Bytes of the static device scratch behind ssm_scan_fwd_noalloc (one copy per GPU).
 constexpr size_t kScratchBytes = size_t(32) << 20;
 

@@ -28,11 +28,13 @@
 //      5. the state after the segment (lane 63's last token) carried to the next.
 //  * Then D x, the SiLU gate, the io-dtype store, and after the last segment h_final.
 //
-// B_t and C_t are shared by all channels of a batch row: each workgroup (W rows of one
-// batch row) stages them per segment into LDS as fp32 [state][token], one segment ahead
-// (double buffered), with an XOR swizzle of the token index that keeps the lanes' 16-byte
-// reads free of bank conflicts. No other data goes through LDS and the only barrier is
-// the one per segment that hands over the staged B/C.
+// B_t and C_t are shared by all channels of a batch row: a first small kernel widens them
+// once to fp32 in the workspace, laid out per segment as [B or C][state][token] with an
+// XOR swizzle of the token index that keeps the lanes' 16-byte LDS reads free of bank
+// conflicts; each workgroup (W rows of one batch row) then copies a segment's 64 KB
+// straight into LDS (global_load_lds), one segment ahead into a second buffer. No other
+// data goes through LDS and the only barrier is the one per segment that hands over the
+// staged B/C.
 //
 // REV = the anti-causal scan: segments are taken from the last to the first and tokens
 // inside a segment from the last to the first; the staged B/C and the lanes' registers
@@ -181,15 +183,11 @@ __device__ __forceinline__ void wave_scan2(float& a0, float& b0, float& a1, floa
 __device__ __forceinline__ int swz(int q) { return q ^ ((((q >> 5) ^ (q >> 6)) & 1) << 2); }
 
 template <typename IO, bool REV, bool STRUCT, int K, int W>
-__global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
-                                                         const IO* __restrict__ Bg,
-                                                         const IO* __restrict__ Cg) {
+__global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p) {
     constexpr int T = 64 * K;                 // tokens per segment
-    constexpr int NTH = W * 64;
-    constexpr int TASKS = 2 * T;              // staging: one (token, B or C) per task
-    static_assert(TASKS % NTH == 0, "staging tasks per thread");
-    constexpr int NT = TASKS / NTH;
-    constexpr int VPT = 16 * sizeof(IO) / 16;   // 16-byte loads per token of B or C
+    constexpr int SEG_BYTES = 2 * kDState * T * 4;   // the staged B/C of one segment
+    constexpr int CHUNKS = SEG_BYTES / 1024;         // 1 KB per wave-wide 16-byte load
+    static_assert(CHUNKS % W == 0, "staging chunks per wave");
     __shared__ float sBC[2][2][kDState][T];
 
     const int tid = threadIdx.x;
@@ -202,8 +200,8 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
     const int64_t row = b * p.dim + (valid ? d : 0);
     const int64_t L = p.seqlen;
     const int nseg = (int)((L + T - 1) / T);
-    const IO* Bb = Bg + b * L * kDState;
-    const IO* Cb = Cg + b * L * kDState;
+    // this batch row's B/C segments, widened to fp32 in the staged layout (wave_bc_kernel)
+    const char* bcw = reinterpret_cast<const char*>(p.bcq) + (int64_t)b * nseg * SEG_BYTES;
 
     // per-row constants (uniform: scalar loads)
     float A2[kDState], hc[kDState];
@@ -236,47 +234,19 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
         return (int64_t)s * T + (REV ? T - (ln + 1) * K : ln * K);
     };
 
-    // ---- B/C staging: task i = (B or C, scan index q) of one segment
-    typedef typename std::conditional<sizeof(IO) == 2, uint4, float4>::type Vec;
-    Vec stage[NT][VPT];
-    auto stage_load = [&](int s) {
+    // ---- B/C staging: one segment's 64 KB copied straight from the widened workspace into
+    // an LDS buffer by the workgroup's waves (global_load_lds_dwordx4: 1 KB per wave-wide
+    // load, no registers); complete once every wave has waited for its vector memory
+    // accesses and passed the barrier that follows
+    auto stage = [&](int s, int buf) {
+        const char* src = bcw + (int64_t)s * SEG_BYTES;
+        char* dst = reinterpret_cast<char*>(&sBC[buf][0][0][0]);
 #pragma unroll
-        for (int k = 0; k < NT; ++k) {
-            const int i = tid + k * NTH;
-            const int q = i % T;
-            const IO* src = (i < T) ? Bb : Cb;
-            const int64_t t = (int64_t)s * T + (REV ? T - 1 - q : q);
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                if (t < L)
-                    stage[k][v] = *reinterpret_cast<const Vec*>(src + t * kDState + v * (16 / sizeof(IO)));
-                else
-                    stage[k][v] = zero_vec<Vec>();
-            }
-        }
-    };
-    auto stage_store = [&](int buf) {
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-            const int i = tid + k * NTH;
-            const int q = i % T;
-            const int bc = i / T;
-            float* dst = &sBC[buf][bc][0][swz(q)];
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                constexpr int EPV = 16 / sizeof(IO);     // elements per 16-byte load
-                float e[EPV];
-                if constexpr (sizeof(IO) == 2) {
-                    const uint4 r = stage[k][v];
-                    e[0] = bf16_lo(r.x); e[1] = bf16_hi(r.x); e[2] = bf16_lo(r.y); e[3] = bf16_hi(r.y);
-                    e[4] = bf16_lo(r.z); e[5] = bf16_hi(r.z); e[6] = bf16_lo(r.w); e[7] = bf16_hi(r.w);
-                } else {
-                    const float4 r = stage[k][v];
-                    e[0] = r.x; e[1] = r.y; e[2] = r.z; e[3] = r.w;
-                }
-#pragma unroll
-                for (int m = 0; m < EPV; ++m) dst[(v * EPV + m) * T] = e[m];
-            }
+        for (int k = 0; k < CHUNKS / W; ++k) {
+            const int c = k * W + w;
+            __builtin_amdgcn_global_load_lds(
+                src + c * 1024 + lane * 16,
+                (__attribute__((address_space(3))) void*)(dst + c * 1024), 16, 0, 0);
         }
     };
 
@@ -292,9 +262,9 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
         if (zr) rz.load(zr + m0, vec, n);
     };
 
-    stage_load(seg_of(0));
-    stage_store(0);
+    stage(seg_of(0), 0);
     if (valid) row_load(seg_of(0));
+    wait_vmem();
     __syncthreads();
 
     for (int it = 0; it < nseg; ++it) {
@@ -303,7 +273,7 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
         const int64_t m0 = lane_base(s, lane);
         const int nmem = (int)((L - m0 < K) ? (L - m0 < 0 ? 0 : L - m0) : K);  // valid tokens
         const bool vec = p.aligned && nmem == K;
-        if (it + 1 < nseg) stage_load(seg_of(it + 1));
+        if (it + 1 < nseg) stage(seg_of(it + 1), buf ^ 1);
         if (!kPrefetchRows && valid && it > 0) row_load(s);
         // the segment's compute for this wave's row, on the general or the structured path
         auto segment = [&](auto path) {
@@ -379,6 +349,18 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                         fa[r] = fast_exp2(dsum * A2[n + r]);
                     }
                 }
+                // C of the pair, read now so that the scan hides the LDS latency
+                float Cv[2][K];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const float* Cn = &sBC[buf][1][n + r][0];
+#pragma unroll
+                    for (int g = 0; g < K / 4; ++g) {
+                        const float4 cq = *reinterpret_cast<const float4*>(Cn + ((lq + 4 * g) ^ (m << 2)));
+                        Cv[r][4 * g] = cq.x; Cv[r][4 * g + 1] = cq.y;
+                        Cv[r][4 * g + 2] = cq.z; Cv[r][4 * g + 3] = cq.w;
+                    }
+                }
                 // 2. the exclusive prefix of the lanes' composites
                 float ea0, eb0, ea1, eb1;
                 wave_scan2(fa[0], fb[0], fa[1], fb[1], ea0, eb0, ea1, eb1);
@@ -387,18 +369,11 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                 const float ea[2] = {ea0, ea1}, eb[2] = {eb0, eb1};
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    const float* Cn = &sBC[buf][1][n + r][0];
-                    float Cv[K];
-#pragma unroll
-                    for (int g = 0; g < K / 4; ++g) {
-                        const float4 cq = *reinterpret_cast<const float4*>(Cn + ((lq + 4 * g) ^ (m << 2)));
-                        Cv[4 * g] = cq.x; Cv[4 * g + 1] = cq.y; Cv[4 * g + 2] = cq.z; Cv[4 * g + 3] = cq.w;
-                    }
                     float h = __builtin_fmaf(ea[r], hc[n + r], eb[r]);
 #pragma unroll
                     for (int j = 0; j < K; ++j) {
                         h = __builtin_fmaf(a[r][j], h, bb[r][j]);
-                        y[j] = __builtin_fmaf(Cv[j], h, y[j]);
+                        y[j] = __builtin_fmaf(Cv[r][j], h, y[j]);
                     }
                     hc[n + r] = __builtin_bit_cast(
                         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, h), 63));
@@ -427,7 +402,7 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                 for (int e = 0; e < K; ++e) o[e] += old.get(e);
             }
             if (nmem > 0) StoreK<IO, K>::store(yr + m0, vec, nmem, o);
-                };
+        };
         if (valid) {
             if constexpr (STRUCT) {
                 if (row_struct) segment(std::true_type{});
@@ -436,7 +411,7 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
                 segment(std::false_type{});
             }
         }
-        if (it + 1 < nseg) stage_store(buf ^ 1);
+        wait_vmem();   // this wave's part of the next segment's B/C is in LDS
         __syncthreads();
     }
     if (valid && p.h_final && lane == 0) {
@@ -447,36 +422,72 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p,
     }
 }
 
+// B and C widened to fp32 into the wave scan's staged layout: per (batch row b, segment s
+// of T tokens), [B or C][state n][swz(q)] for the scan-order index q of each token of the
+// segment (zeros for the padding tokens past the end), so that staging a segment is one
+// contiguous copy. One thread per (b, s, q).
+template <typename IO, bool REV, int T>
+__global__ __launch_bounds__(256) void wave_bc_kernel(const IO* __restrict__ B,
+                                                      const IO* __restrict__ C,
+                                                      float* __restrict__ out, int64_t batch,
+                                                      int64_t seqlen, int64_t nseg) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= batch * nseg * T) return;
+    const int q = (int)(i % T);
+    const int64_t bs = i / T;                  // b * nseg + s
+    const int64_t s = bs % nseg;
+    const int64_t b = bs / nseg;
+    const int64_t t = s * T + (REV ? T - 1 - q : q);
+    float* o = out + bs * (2 * kDState * T) + swz(q);
+    if (t < seqlen) {
+        const IO* pb = B + (b * seqlen + t) * kDState;
+        const IO* pc = C + (b * seqlen + t) * kDState;
+#pragma unroll
+        for (int n = 0; n < kDState; ++n) {
+            o[n * T] = to_f32(pb[n]);
+            o[(kDState + n) * T] = to_f32(pc[n]);
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < 2 * kDState; ++n) o[n * T] = 0.0f;
+    }
+}
+
 template <typename IO, bool REV>
 hipError_t launch_wavescan_t(const ScanParams& prm, const void* B, const void* C,
-                             hipStream_t stream) {
-    constexpr int K = 8, W = 16;
+                             hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    constexpr int K = 8, W = 16, T = 64 * K;
+    static_assert(T == kWaveSegTokens, "segment length of the workspace layout");
     ScanParams p = prm;
     p.groups_per_batch = (int32_t)((p.dim + W - 1) / W);
+    const int64_t nseg = (p.seqlen + T - 1) / T;
+    const int64_t n = p.batch * nseg * T;
+    hipLaunchKernelGGL((wave_bc_kernel<IO, REV, T>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                       0, stream, static_cast<const IO*>(B), static_cast<const IO*>(C), p.bcq,
+                       p.batch, p.seqlen, nseg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(p.batch * p.groups_per_batch));
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return hipGetLastError();
     if (p.structured_a)
-        hipLaunchKernelGGL((wavescan_kernel<IO, REV, true, K, W>), grid, dim3(W * 64), 0, stream,
-                           p, static_cast<const IO*>(B), static_cast<const IO*>(C));
+        hipLaunchKernelGGL((wavescan_kernel<IO, REV, true, K, W>), grid, dim3(W * 64), 0, stream, p);
     else
-        hipLaunchKernelGGL((wavescan_kernel<IO, REV, false, K, W>), grid, dim3(W * 64), 0, stream,
-                           p, static_cast<const IO*>(B), static_cast<const IO*>(C));
-    return hipGetLastError();
+        hipLaunchKernelGGL((wavescan_kernel<IO, REV, false, K, W>), grid, dim3(W * 64), 0, stream, p);
+    e = hipGetLastError();
+    if (e == hipSuccess && ev1) e = hipEventRecord(ev1, stream);
+    return e;
 }
 
 }  // namespace
 
 hipError_t launch_wavescan(const ScanParams& prm, const void* B, const void* C, bool bf16,
                            hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipGetLastError();
-    hipError_t e;
     if (bf16)
-        e = prm.reverse ? launch_wavescan_t<uint16_t, true>(prm, B, C, stream)
-                        : launch_wavescan_t<uint16_t, false>(prm, B, C, stream);
-    else
-        e = prm.reverse ? launch_wavescan_t<float, true>(prm, B, C, stream)
-                        : launch_wavescan_t<float, false>(prm, B, C, stream);
-    if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, stream);
-    return e;
+        return prm.reverse
+                   ? launch_wavescan_t<uint16_t, true>(prm, B, C, stream, ev_begin, ev_end)
+                   : launch_wavescan_t<uint16_t, false>(prm, B, C, stream, ev_begin, ev_end);
+    return prm.reverse ? launch_wavescan_t<float, true>(prm, B, C, stream, ev_begin, ev_end)
+                       : launch_wavescan_t<float, false>(prm, B, C, stream, ev_begin, ev_end);
 }
 
 }  // namespace ssm
