@@ -21,6 +21,36 @@ __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 
+// 2^y with round-to-nearest arithmetic only, for the decays of the fp32-io kernels:
+// y = n + f with n = rint(y) and |f| <= 1/2; 2^f from its Taylor series (f ln 2)^k / k!
+// up to k = 7 (truncation below 6e-9 relative on |f| <= 1/2), Horner with fused
+// multiply-adds; then the exact scaling by 2^n. Error within ~1.2 ulp and without a
+// systematic sign (mean relative error ~1e-10 over y in [-10, 0]). The hardware
+// v_exp_f32 is as close per call but not unbiased, and a state with a long memory
+// multiplies hundreds of decays: on the Mamba-2.8B layer shape in fp32 its bias alone
+// takes the worst row's final state to ~1.5e-5 relative, this exp keeps it near 4e-6.
+__device__ __forceinline__ float exp2_unbiased(float y) {
+    y = (y < -160.0f) ? -160.0f : ((y > 128.0f) ? 128.0f : y);
+    const float n = __builtin_rintf(y);
+    const float f = y - n;   // exact
+    float p = 1.5252733804059841e-05f;
+    p = __builtin_fmaf(p, f, 1.5403530393381609e-04f);
+    p = __builtin_fmaf(p, f, 1.3333558146428443e-03f);
+    p = __builtin_fmaf(p, f, 9.6181291076284772e-03f);
+    p = __builtin_fmaf(p, f, 5.5504108664821580e-02f);
+    p = __builtin_fmaf(p, f, 2.4022650695910071e-01f);
+    p = __builtin_fmaf(p, f, 6.9314718055994531e-01f);
+    p = __builtin_fmaf(p, f, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+// The decay exp(Delta A) = 2^y of a kernel with io type IO: the unbiased form for fp32
+// io (whose results are held to 1e-5), the hardware exp for bf16 io.
+template <typename IO> __device__ __forceinline__ float decay_exp2(float y) {
+    if constexpr (sizeof(IO) == 4) return exp2_unbiased(y);
+    else return fast_exp2(y);
+}
+
 // softplus(v) = max(v, 0) + log1p(e^-|v|). log1p(e) is taken as log(w) + (e - (w - 1))
 // with w = 1 + e rounded: the second term restores what the rounding of 1 + e lost
 // (w - 1 is exact for w in [1, 2]), so small e keeps full relative accuracy.

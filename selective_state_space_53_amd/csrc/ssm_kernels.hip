@@ -370,8 +370,8 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         float* const pout = sP + (pr * CG + cc) * kLdsRow;
 #define SSM_TOKEN(OUT, DS, US, Q)                                                     \
     {                                                                                 \
-        const float e0 = fast_exp2(DS * a2[0]);                                       \
-        const float e1 = fast_exp2(DS * a2[1]);                                       \
+        const float e0 = decay_exp2<IO>(DS * a2[0]);                                  \
+        const float e1 = decay_exp2<IO>(DS * a2[1]);                                  \
         h[0] = __builtin_fmaf(e0, h[0], Q.x * US);                                    \
         h[1] = __builtin_fmaf(e1, h[1], Q.y * US);                                    \
         if (kOut) OUT = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                        \
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(const DecodeParams p)
         float acc = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            hh[k] = __builtin_fmaf(fast_exp2(delta * aa[k] * kLog2e), hh[k], u * Bv[r][k]);
+            hh[k] = __builtin_fmaf(decay_exp2<IO>(delta * aa[k] * kLog2e), hh[k], u * Bv[r][k]);
             acc = __builtin_fmaf(Cv[r][k], hh[k], acc);
         }
         if (ok[r]) store_stream4(p.state + grow[r] * kDState + 4 * j, hh[0], hh[1], hh[2], hh[3]);

@@ -305,10 +305,10 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p) {
             if constexpr (S) {
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
-                    rt[j] = fast_exp2(dl[j] * A2[0]);
+                    rt[j] = decay_exp2<IO>(dl[j] * A2[0]);
                     pw[j] = 0.0f;
                 }
-                Rt = fast_exp2(dsum * A2[0]);
+                Rt = decay_exp2<IO>(dsum * A2[0]);
             }
             const int lq = lane * K;
             const int m = ((lane >> 2) ^ (lane >> 3)) & 1;   // swz(lq + 4g) = (lq + 4g) ^ (m << 2)
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p) {
                             a[r][j] = (n + r == 0) ? rt[j] : pw[j] * rt[j];
                             pw[j] = a[r][j];
                         } else {
-                            a[r][j] = fast_exp2(dl[j] * A2[n + r]);
+                            a[r][j] = decay_exp2<IO>(dl[j] * A2[n + r]);
                         }
                         bb[r][j] = u[j] * Bv[j];
                     }
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(W * 64) void wavescan_kernel(const ScanParams p) {
                         fa[r] = (n + r == 0) ? Rt : fpw * Rt;
                         fpw = fa[r];
                     } else {
-                        fa[r] = fast_exp2(dsum * A2[n + r]);
+                        fa[r] = decay_exp2<IO>(dsum * A2[n + r]);
                     }
                 }
                 // C of the pair, read now so that the scan hides the LDS latency

@@ -44,6 +44,39 @@ def rowwise_err(got, ref) -> float:
     return float(np.max(diff[~zero] / scale[~zero]))
 
 
+def per_token_err(got, ref, floor_frac=0.1) -> float:
+    """Per-token error of a [batch][L][N] gradient that is a sum over channels (dB, dC):
+    for each (b, t) the max-norm error over the N states divided by the max-norm of the
+    reference at that token -- or, where that sum cancelled, by a floor of floor_frac
+    times the median per-token max-norm of its batch row."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape and g.ndim == 3, (g.shape, r.shape)
+    scale = np.max(np.abs(r), axis=2)                               # [b][L]
+    floor = floor_frac * np.median(scale, axis=1, keepdims=True)    # [b][1]
+    den = np.maximum(scale, floor)
+    if np.all(den == 0):
+        return float(np.max(np.abs(g - r)))
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.max(np.abs(g - r), axis=2) / den))
+
+
+def boundary_rows(batch, dim, cg, nspread, seed=0):
+    """(b, d) rows on both sides of every boundary between groups of cg channels (the
+    last channel of a group and the first of the next, plus channel 0 and the last
+    channel), in every batch row, plus nspread random rows."""
+    ch = {0, dim - 1}
+    for k in range(1, (dim + cg - 1) // cg):
+        ch.update((k * cg - 1, k * cg))
+    picks = {(b, d) for b in range(batch) for d in ch if d < dim}
+    rng = np.random.default_rng(seed)
+    target = len(picks) + nspread
+    while len(picks) < min(target, batch * dim):
+        picks.add((int(rng.integers(batch)), int(rng.integers(dim))))
+    rows = sorted(picks)
+    return np.array([r[0] for r in rows]), np.array([r[1] for r in rows])
+
+
 def gpu_scan(inp: dict, use_z=True, use_D=True, h0=None, final=True, plan=0, chunk_len=0,
              softplus=True, bias=True, group_channels=0, reverse=False, structured_a=False):
     from selective_state_space_53_amd import binding
@@ -64,8 +97,9 @@ def oracle_full(inp: dict, use_z=True, use_D=True, h0=None, softplus=True, bias=
 
 
 def sample_rows(batch, dim, n, seed=0):
-    """Deterministic (b, d) sample: the corners of every channel group boundary
-    that exists plus random rows."""
+    """Deterministic (b, d) sample of about n rows: the first and last row, channels 63 and
+    64 (the 64-channel boundary), and random rows. (Tests that must cover the channel
+    groups of a plan use boundary_rows.)"""
     rng = np.random.default_rng(seed)
     picks = {(0, 0), (batch - 1, dim - 1), (0, min(63, dim - 1)), (batch - 1, min(64, dim - 1))}
     while len(picks) < min(n, batch * dim):

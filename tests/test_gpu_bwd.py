@@ -55,6 +55,8 @@ def _compare(g, ref, io, tol=None):
         elif k in ("dA", "dD", "ddelta_bias"):
             got, r = got.reshape(1, -1), r.reshape(1, -1)
         errs[k] = parity.rowwise_err(got, r)
+        if k in ("dB", "dC"):
+            errs[k + "/token"] = parity.per_token_err(oracle.f64(g[k]), np.asarray(ref[OKEY.get(k, k)]))
     say("   " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad

@@ -67,14 +67,21 @@ def test_reverse_all_rows(shape, plan, chunk):
         assert ey <= parity.TOL[io] and eh <= parity.TOL[io]
 
 
-@pytest.mark.parametrize("name,nrows", [("m2p8", 64), ("long", 4)])
-def test_reverse_full_size_sampled_rows(name, nrows):
+@pytest.mark.parametrize("name,nrows", [("m2p8", 0), ("long", 16)])
+def test_reverse_full_size_rows(name, nrows):
+    """Anti-causal scan at full size in the library's plan: every row of the 2.8B layer;
+    the million-token row on both sides of every 32-channel group boundary plus spread
+    rows."""
     cfg = synth.CONFIGS[name]
     say("case reverse full size", name)
     inp = synth.scan_inputs(cfg, DEV)
     y, hf = parity.gpu_scan(inp, reverse=True)
     torch.cuda.synchronize()
-    rb, rd = parity.sample_rows(cfg.batch, cfg.dim, nrows, seed=cfg.seed + 1)
+    if nrows == 0:
+        rb = np.repeat(np.arange(cfg.batch), cfg.dim)
+        rd = np.tile(np.arange(cfg.dim), cfg.batch)
+    else:
+        rb, rd = parity.boundary_rows(cfg.batch, cfg.dim, 32, nrows, seed=cfg.seed + 1)
     yr, hr = parity.oracle_reverse_rows(inp, rb, rd)
     sel = (torch.as_tensor(rb, device=DEV), torch.as_tensor(rd, device=DEV))
     ey, eh = parity.rowwise_err(y[sel], yr), parity.rowwise_err(hf[sel], hr)
