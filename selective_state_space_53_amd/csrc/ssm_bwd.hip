@@ -220,15 +220,15 @@ __device__ __forceinline__ void bwd_event_tile(
             hp1 = v.y;
         }
         const float o1 = __builtin_fmaf(G1, q.y, G0 * q.x);          // G.B
-        const float w0 = G0 * hp0 * e0;
-        const float w1 = G1 * hp1 * e1;
+        Gc[0] = e0 * G0;                                              // a G
+        Gc[1] = e1 * G1;
+        const float w0 = Gc[0] * hp0;
+        const float w1 = Gc[1] * hp1;
         const float o2 = __builtin_fmaf(w1, Ar[1], w0 * Ar[0]);      // G.h.a.A
         dA[0] = __builtin_fmaf(w0, Dk, dA[0]);
         dA[1] = __builtin_fmaf(w1, Dk, dA[1]);
         const float sr = row_sum4(G0 * Uk, G1 * Uk, Qk * hs[k][0], Qk * hs[k][1], lane16);
         red[k * kLaneRows * 4] = sr;
-        Gc[0] = e0 * G0;
-        Gc[1] = e1 * G1;
         if (first && p.dh0 && valid)
             *reinterpret_cast<float2*>(p.dh0 + ((int64_t)s * p.dim + d) * kDState + 2 * pr) =
                 make_float2(Gc[0], Gc[1]);
@@ -328,7 +328,11 @@ void scan_bwd_kernel(const BwdParams p) {
     const uint32_t lrow = (uint32_t)((int64_t)cq * L * (int64_t)sizeof(IO));
     // byte offset of this thread's 2 tokens starting at token t
     auto at = [&](int64_t t) { return lrow + (uint32_t)((t + 2 * jq) * (int64_t)sizeof(IO)); };
-    const float* ck = p.ckpt + row * p.nckpt * kDState + 2 * pr;
+    // checkpoints [batch][L/16][dim][16]: a tile's are one 2 KB run per workgroup, read
+    // once, so they are loaded non-temporally and do not push the input rows, which the
+    // next tiles read again, out of the L2
+    const float* ck = p.ckpt + (b * p.nckpt * p.dim + d) * kDState + 2 * pr;
+    const int64_t ckstride = p.dim * kDState;
     float* const pbc = p.part_bc + ((b * p.groups_per_batch + grp) * L) * 32;
     // B/C staging: threads 0..127 move one 16-byte (pair, token) entry per tile
     const bool bc_mover = tid < 128;
@@ -370,7 +374,11 @@ void scan_bwd_kernel(const BwdParams p) {
             rg.load(reinterpret_cast<const IO*>(gw + at(t0)), vec, nq);
         }
         if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
-        if (valid) rck = *reinterpret_cast<const float2*>(ck + (t0 / kT) * kDState);
+        if (valid) {
+            const f32x2_t v = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x2_t*>(ck + (t0 / kT) * ckstride));
+            rck = make_float2(v.x, v.y);
+        }
         if (PACKED && tid == 0) rev = p.tile_ev[t0 / kT];
     };
     rx.zero();
@@ -514,8 +522,22 @@ void scan_bwd_kernel(const BwdParams p) {
                 const float hp1 = REV ? (k < kLast ? hs[k < kLast ? k + 1 : kLast][1] : hs1)
                                       : (k > 0 ? hs[k > 0 ? k - 1 : 0][1] : hs1);
                 o1[j] = __builtin_fmaf(G1, q.y, G0 * q.x);          // G.B
-                const float w0 = G0 * hp0 * e0;
-                const float w1 = G1 * hp1 * e1;
+                // a G: the gradient carried to the token before, and with h_{t-1} the
+                // decay terms G h a (2 multiplies fewer per token than G h a on its own;
+                // with fp32 inputs, whose prefetched rows take twice the registers, the
+                // longer-lived products spill, and the separate form stays)
+                float ag0, ag1, w0, w1;
+                if constexpr (sizeof(IO) == 2) {
+                    ag0 = e0 * G0;
+                    ag1 = e1 * G1;
+                    w0 = ag0 * hp0;
+                    w1 = ag1 * hp1;
+                } else {
+                    w0 = G0 * hp0 * e0;
+                    w1 = G1 * hp1 * e1;
+                    ag0 = e0 * G0;
+                    ag1 = e1 * G1;
+                }
                 o2[j] = __builtin_fmaf(w1, Ar[1], w0 * Ar[0]);      // G.h.a.A
                 dA[0] = __builtin_fmaf(w0, Ds[j], dA[0]);
                 dA[1] = __builtin_fmaf(w1, Ds[j], dA[1]);
@@ -525,8 +547,8 @@ void scan_bwd_kernel(const BwdParams p) {
                 // the 4 lanes of a quad hold the same bits, so all of them write: no
                 // branch, and the adjoint stays one scheduling region per 4 tokens
                 red[k * kLaneRows * 4] = sr;
-                Gc[0] = e0 * G0;
-                Gc[1] = e1 * G1;
+                Gc[0] = ag0;
+                Gc[1] = ag1;
             }
             *reinterpret_cast<float4*>(p1 + slot) = make_float4(o1[0], o1[1], o1[2], o1[3]);
             *reinterpret_cast<float4*>(p2 + slot) = make_float4(o2[0], o2[1], o2[2], o2[3]);
@@ -576,7 +598,7 @@ void scan_bwd_kernel(const BwdParams p) {
         }
         // 16 tokens x 32 values (dB then dC): value i < 512 (i = tid, tid + CG*8) is the
         // sum over the CG/16 rows of value i & 31 of token i >> 5; a wave writes 64
-        // contiguous floats
+        // contiguous floats, non-temporally (only the reduction kernel reads them)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int i = tid + m * CG * 8;
@@ -587,7 +609,7 @@ void scan_bwd_kernel(const BwdParams p) {
 #pragma unroll
             for (int j = 0; j < kRowsPerPair; ++j)
                 sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 4 + which * 2 + (n & 1)];
-            if (k < nvalid) pbc[(t0 + k) * 32 + v] = sum;
+            if (k < nvalid) __builtin_nontemporal_store(sum, &pbc[(t0 + k) * 32 + v]);
         }
     }
 

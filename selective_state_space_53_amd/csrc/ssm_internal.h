@@ -42,7 +42,7 @@ struct ScanParams {
     float* chunk_sum;    // [batch*dim][nchunks]
     int32_t* chunk_flag; // [nchunks]: 1 = a sequence begins inside the chunk (packed input)
     const int32_t* cu;   // packed sequences: [nseq+1] token offsets, or null (batch rows)
-    float* ckpt;         // checkpoint pass: [batch*dim][nckpt][16], the state before every
+    float* ckpt;         // checkpoint pass: [batch][nckpt][dim][16], the state before every
                          // 16th token; null otherwise
     void* q;             // checkpoint pass: [batch][dim][L] io, the output before the gate
                          // (y still gets the gated output), or null
@@ -89,7 +89,7 @@ struct BwdParams {
     const float* D;
     const float* bias;
     const float* dh_final;   // [batch*dim][16] or null (packed: see below)
-    const float* ckpt;       // [batch*dim][nckpt][16]: the state before every 16th token
+    const float* ckpt;       // [batch][nckpt][dim][16]: the state before every 16th token
     const void* q;           // [batch][dim][seqlen] io: the forward output before the gate
     const float* bcq;        // B and C widened, as for the forward
     void* dx;

@@ -12,25 +12,30 @@
 //
 // How the work maps onto CDNA4 (the pages' SRAM-tiled CUDA scan, in "The
 // convolution trick is gone" of the creativeworksofknowledge Mamba lesson, is prior
-// art; what carries over is "keep the state on chip, stream the sequence once,
-// write back only boundary states"):
+// art; what carries over is keeping the state on chip, streaming the sequence once
+// and writing back only boundary states):
 //
-//  * A workgroup owns 64 channels of one batch row and all 16 states: four waves,
-//    wave w holding states 4w..4w+3 of all 64 channels, one channel per lane. Each
-//    lane keeps its 4 states in VGPRs for the whole sequence (or chunk). B_t and C_t
-//    do not depend on the channel, so for a wave they are uniform: they arrive by
-//    scalar loads and enter the VALU ops as SGPR operands.
-//  * The sequence is streamed in tiles of 32 tokens. Per tile: (pre) each wave
-//    computes softplus(Delta), Delta*x and the gate for 8 of the 32 tokens of all
-//    64 channels and shares Delta and Delta*x through LDS; (core) each wave runs the
-//    recurrence over the 32 tokens for its 4 states and writes the partial readout
-//    sum_{its 4 n} C*h to LDS; (post) each wave adds the four partials of its 8
-//    tokens, applies D*x and the gate, and stores y. Every (t, d) element-wise
-//    step is done once, every (t, d, n) step once.
+//  * A workgroup owns CG channels of one batch row and all 16 states (CG a multiple of
+//    16, chosen by the planner: 80 on the 2.8B layer, i.e. 640 threads and one
+//    workgroup per CU). Each lane keeps one state pair (2 states) of one channel in
+//    VGPRs for the whole sequence (or chunk); a 16-lane row holds one pair of 16
+//    consecutive channels.
+//  * B_t and C_t do not depend on the channel. A small pass widens them once into
+//    fp32 per state pair ([batch][pair][token][B0 B1 C0 C1]); the scan stages each
+//    tile's slice through LDS, and a row reads its pair's four values with one
+//    row-uniform 16-byte LDS read per token.
+//  * The sequence is streamed in tiles of 32 tokens. Per tile: (pre) thread (channel,
+//    token quad) computes softplus(Delta), Delta*x, D*x and the gate, and shares Delta
+//    and Delta*x through LDS; (core) each lane runs the recurrence over the 32 tokens
+//    for its pair and writes the partial readout C*h of the pair to LDS; (post) the
+//    8 pairs' partials are summed, D*x added, the gate applied and y stored. Every
+//    (t, d) element-wise step is done once, every (t, d, n) step once.
 //  * Long sequences with few channel groups are cut into chunks (the tiles-with-
 //    final-state idea of the pages' kernel): pass 1 runs each chunk from a zero state
 //    and writes only its end state and sum of Delta, a carry pass composes them in
 //    chunk order, and pass 2 reruns every chunk from its carried-in state.
+//  * The other mapping, lanes over time joined by a wave-wide prefix combine, is in
+//    ssm_wavescan.hip.
 // No MFMA: there is no dense contraction here; the bound is the VALU (one exp per
 // (t, d, n)) with HBM traffic of ~8 bytes per (t, d) in bf16.
 
@@ -231,8 +236,11 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     const IO* dr = static_cast<const IO*>(p.delta) + rowq * p.seqlen;
     const IO* zr = (kOut && p.z) ? static_cast<const IO*>(p.z) + rowq * p.seqlen : nullptr;
     IO* yr = kOut ? static_cast<IO*>(p.y) + rowq * p.seqlen : nullptr;
-    // CKPT: the state before every 16th token, [row][t/16][16]
-    float* const ck = CKPT ? p.ckpt + row * p.nckpt * kDState + 2 * pr : nullptr;
+    // CKPT: the state before every 16th token, [batch][t/16][dim][16] (a 16-token block's
+    // checkpoints of a workgroup's channels are one contiguous run, which the backward
+    // reads whole)
+    float* const ck = CKPT ? p.ckpt + (b * p.nckpt * p.dim + d) * kDState + 2 * pr : nullptr;
+    const int64_t ckstride = p.dim * kDState;
     // B/C staging: the first 256 threads each move 16 bytes (one token of one pair)
     const bool bc_mover = tid < 256;
     const float* bcsrc = p.bcq + ((b * 8 + (tid >> 5)) * p.lpad + (tid & 31)) * 4;
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             // (a block past the end of the row has none)
             auto checkpoint = [&](int64_t blk) {
                 if (CKPT && valid && blk * 16 < p.seqlen)
-                    *reinterpret_cast<float2*>(ck + blk * kDState) = make_float2(h[0], h[1]);
+                    *reinterpret_cast<float2*>(ck + blk * ckstride) = make_float2(h[0], h[1]);
             };
             checkpoint(REV ? t0 / 16 + 1 : t0 / 16);
             // the LDS operands of 4 tokens, read one group ahead of their use
@@ -433,7 +441,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                 // any reset there (the backward applies the resets itself)
                 if (CKPT && valid &&
                     (REV ? ((k == kTile - 1 && nvalid > 16) || k == 15) : (k == 0 || (k == 16 && real))))
-                    *reinterpret_cast<float2*>(ck + (t / 16) * kDState) = make_float2(h[0], h[1]);
+                    *reinterpret_cast<float2*>(ck + (t / 16) * ckstride) = make_float2(h[0], h[1]);
                 if (real && t == (REV ? hi - 1 : lo)) {     // first token of sequence s
                     float2 hv = make_float2(0.f, 0.f);
                     if (p.h0 && valid)
