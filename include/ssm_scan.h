@@ -78,8 +78,8 @@ typedef struct {
                            widened to fp32 in its own layout, batch*ceil(seqlen/512)*64 KB;
                            batch rows of ssm_scan_fwd without save_workspace only).      */
     int32_t group_channels; /* channels per workgroup: 0 = library choice, else one of
-                           32, 48, 64, 80, 96 (all 16 states of a channel stay in one
-                           workgroup; 2 states per lane, group_channels/8 waves)        */
+                           16, 32, 48, 64, 80, 96 (all 16 states of a channel stay in
+                           one workgroup; 2 states per lane, group_channels/8 waves)    */
     void* timing_begin; /* hipEvent_t or NULL: recorded on `stream` right before the
                            launch of the scan kernel that writes y                     */
     void* timing_end;   /* hipEvent_t or NULL: recorded right after that launch        */

@@ -85,20 +85,24 @@ constexpr int64_t kLdsPerCU = 160 * 1024;
 constexpr int64_t kMaxWavesFull = 4, kMaxWavesLocal = 5;
 
 // Relative time of one pass: `groups` workgroups of cg channels, `tiles` tiles each.
-// A workgroup's cg/8 waves are counted as dealt to the CU's four SIMDs from the first,
-// ceil(cg/32) on the busiest (as for the backward, where a second 6-wave workgroup was
-// measured not to join the first; here, with CG = 48 on the 2.8B layer, 349 us against
-// 249 us at CG = 80).
+// A workgroup of more than 4 waves is counted as dealt to the CU's four SIMDs from the
+// first, ceil(cg/32) on the busiest (as for the backward, where a second 6-wave
+// workgroup was measured not to join the first; here, with CG = 48 on the 2.8B layer,
+// 349 us against 249 us at CG = 80). The waves of workgroups of up to 4 waves spread
+// over the SIMDs: k of them put ceil(k * waves / 4) on the busiest.
 double pass_cost(int64_t groups, int64_t tiles, int cg, bool local) {
-    const int64_t per_simd = (cg / 8 + 3) / 4;
+    const int64_t waves = cg / 8;
+    const bool spread = waves <= 4;
+    const int64_t per_simd = (waves + 3) / 4;
+    const int64_t max_w = local ? kMaxWavesLocal : kMaxWavesFull;
     int64_t k = kLdsPerCU / scan_lds_bytes(cg, local);                  // by LDS
-    const int64_t kw = (local ? kMaxWavesLocal : kMaxWavesFull) / per_simd;  // by registers
+    const int64_t kw = spread ? max_w * 4 / waves : max_w / per_simd;    // by registers
     if (kw < k) k = kw;
     const int64_t per_cu = (groups + kCUs - 1) / kCUs;
     if (k > per_cu) k = per_cu;
     if (k < 1) k = 1;
     const int64_t rounds = (groups + kCUs * k - 1) / (kCUs * k);
-    const int64_t w = k * per_simd;                                      // busiest SIMD
+    const int64_t w = spread ? (k * waves + 3) / 4 : k * per_simd;      // busiest SIMD
     // pass 1 skips the readout and the output stage; a workgroup's set-up costs about
     // one tile
     return (double)rounds * (double)(tiles + 1) * (double)w * wave_cost(w) * (local ? 0.85 : 1.0);
@@ -161,9 +165,9 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     int64_t req_chunk = 0;
     if (opts) {
         req_cg = opts->group_channels;
-        if (req_cg != 0 && !(req_cg >= 32 && req_cg <= 96 && req_cg % 16 == 0))
+        if (req_cg != 0 && !(req_cg >= 16 && req_cg <= 96 && req_cg % 16 == 0))
             return fail(SSM_ERR_INVALID_ARGUMENT,
-                        "ssm_scan_options.group_channels=%d not in {0, 32, 48, 64, 80, 96}",
+                        "ssm_scan_options.group_channels=%d not in {0, 16, 32, 48, 64, 80, 96}",
                         (int)req_cg);
         if (opts->plan < 0 || opts->plan > 3)
             return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.plan=%d not in {0,1,2,3}",
@@ -207,13 +211,16 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     const int64_t lpad = (seqlen + ssm::kTokenTile - 1) / ssm::kTokenTile * ssm::kTokenTile;
 
     // Channels per workgroup and chunking: the choice with the lowest modelled time
-    // (pass_cost above) among group sizes 32..96 and chunk counts 1 (single pass), 2,
+    // (pass_cost above) among group sizes 16..96 and chunk counts 1 (single pass), 2,
     // 3, 4, 6, 8, 12, ... A requested group size, plan or chunk length restricts the
-    // search. Ties go to fewer chunks, then to larger groups -- except that 32 channels
-    // come before 48: several 4-wave workgroups per CU, out of phase and with the core at
-    // raised priority, beat one 6-wave workgroup whose SIMDs hold 2, 2, 1, 1 waves (the
-    // 130M layer: 167 us at 32 against 181 us at 48, which the model ties).
-    static const int kCands[] = {96, 80, 64, 32, 48};
+    // search. Ties go to fewer chunks, then to the candidate order: 16 channels first --
+    // several 2-wave workgroups per CU run out of phase, their core at raised priority,
+    // and none waits at a barrier for a busier SIMD (the 2.8B layer: 215 us at 16
+    // against 241 us at 80, the 130M layer 160 against 163 us at 32, both ties in the
+    // model) -- then larger groups, except that 32 channels come before 48: several
+    // 4-wave workgroups per CU beat one 6-wave workgroup whose SIMDs hold 2, 2, 1, 1
+    // waves (the 130M layer: 167 us at 32 against 181 us at 48, which the model ties).
+    static const int kCands[] = {16, 96, 80, 64, 32, 48};
     PlanChoice best{0, 0, 0, 1e300, 0};
     for (int c : kCands) {
         if (req_cg && c != req_cg) continue;

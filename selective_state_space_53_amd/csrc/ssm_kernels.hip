@@ -241,10 +241,15 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     // reads whole)
     float* const ck = CKPT ? p.ckpt + (b * p.nckpt * p.dim + d) * kDState + 2 * pr : nullptr;
     const int64_t ckstride = p.dim * kDState;
-    // B/C staging: the first 256 threads each move 16 bytes (one token of one pair)
-    const bool bc_mover = tid < 256;
+    // B/C staging: a tile's 256 (pair, token) entries of 16 bytes; the first 256 threads
+    // move one each (a 16-channel workgroup has 128 threads: two each)
+    constexpr int kMovers = CG * 8 < 256 ? CG * 8 : 256;
+    constexpr int kMoves = 256 / kMovers;
+    const bool bc_mover = tid < kMovers;
     const float* bcsrc = p.bcq + ((b * 8 + (tid >> 5)) * p.lpad + (tid & 31)) * 4;
     float* const bcdst = sBC + tid * 4;
+    // entry tid + m * kMovers: pair (tid >> 5) + m * kMovers / 32, the same token
+    constexpr int64_t kMoveSrc = kMovers / 32;   // pairs per move
     float dsum = 0.0f;
 
     // ---- packed sequences: s is the sequence of the next token to be scanned, [lo, hi)
@@ -312,7 +317,9 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     const float* const coreU = sU + cc * kLdsRow;
 
     Raw4<IO> rx, rdl, rz;
-    float4 rbc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 rbc[kMoves];
+#pragma unroll
+    for (int m = 0; m < kMoves; ++m) rbc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
     auto tile_of = [&](int it) { return REV ? tbase + nt - 1 - it : tbase + it; };
     auto load_tile = [&](int ti) {
         const int64_t t0 = t_beg + (int64_t)ti * kTile;
@@ -324,13 +331,21 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             rdl.load(dr + t0 + 4 * jq, vec, nq);
             if (zr) rz.load(zr + t0 + 4 * jq, vec, nq);
         }
-        if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
+        if (bc_mover) {
+#pragma unroll
+            for (int m = 0; m < kMoves; ++m)
+                rbc[m] = *reinterpret_cast<const float4*>(bcsrc + (m * kMoveSrc * p.lpad + t0) * 4);
+        }
     };
     rx.zero();
     rdl.zero();
     rz.zero();
     load_tile(tile_of(0));
-    if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
+    if (bc_mover) {
+#pragma unroll
+        for (int m = 0; m < kMoves; ++m)
+            *reinterpret_cast<float4*>(bcdst + m * kMovers * 4) = rbc[m];
+    }
     wait_vmem();   // nothing in flight at the loop's entry: no wait at its top
 
     for (int it = 0; it < nt; ++it) {
@@ -369,7 +384,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // raised wave priority so that the others' load and store phases do not take its
         // issue slots (million-token forward 13.02 -> 12.76 ms, packed 339 -> 335 us in a
         // same-box A/B; with one workgroup per CU, as at 80 channels, it gains nothing)
-        if (CG == 32) __builtin_amdgcn_s_setprio(1);
+        if (CG <= 32) __builtin_amdgcn_s_setprio(1);
         // ---- core: the recurrence over the 32 tokens for (channel cc, states 2pr, 2pr+1).
         // Every lane of a row reads the same (B0, B1, C0, C1) of a token from LDS, so B
         // and C arrive in VGPRs and every op below is a plain VOP2 with VGPR operands
@@ -469,15 +484,19 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // at once (~160 VGPRs); an empty asm that claims to update the state keeps the
         // recurrence above it
         if (LOCAL) asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(dsum));
-        if (CG == 32) __builtin_amdgcn_s_setprio(0);
+        if (CG <= 32) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         // the next tile's B/C into the other LDS buffer (its last readers finished before
         // the barrier above; its next readers come after the next barrier). The loads were
         // issued before the core, so the wait is short; taken here, before this tile's
         // stores, it does not wait for them.
         wait_vmem();
-        if (bc_mover && it + 1 < nt)
-            *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile) = rbc;
+        if (bc_mover && it + 1 < nt) {
+#pragma unroll
+            for (int m = 0; m < kMoves; ++m)
+                *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile + m * kMovers * 4) =
+                    rbc[m];
+        }
 
         // ---- post: this thread's 4 tokens: sum the 8 pairs' partials, skip, gate, store
         if (kOut) {
@@ -639,6 +658,7 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
         hipLaunchKernelGGL((scan_kernel<IO, LOCAL, REV, PACKED, CKPT, N>), grid, dim3(N * 8), \
                            0, stream, prm);                                              \
         break;
+        SSM_CASE(16)
         SSM_CASE(32)
         SSM_CASE(48)
         SSM_CASE(64)

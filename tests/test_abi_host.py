@@ -235,6 +235,14 @@ def test_binding_wraps_every_export(b):
         assert callable(getattr(b, n)), n
 
 
+def test_forward_group_channels(b):
+    # channels per workgroup: multiples of 16 from 16 to 96, else refused
+    for cg in (16, 32, 48, 64, 80, 96):
+        assert b.ssm_scan_workspace_bytes(2, 100, 64, 16, 1, group_channels=cg) > 0, cg
+    for cg in (8, 24, 112, -16):
+        assert b.ssm_scan_workspace_bytes(2, 100, 64, 16, 1, group_channels=cg) == 0, cg
+
+
 def test_bwd_workspace_and_rejects(b):
     ws = b.ssm_scan_bwd_workspace_bytes(2, 100, 64, 16, 1)
     assert ws > b.ssm_scan_workspace_bytes(2, 100, 64, 16, 1)

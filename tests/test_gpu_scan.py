@@ -132,7 +132,7 @@ def test_ragged_all_rows(shape, plan, chunk):
         assert ey <= parity.TOL[io] and eh <= parity.TOL[io]
 
 
-@pytest.mark.parametrize("cg", [32, 48, 64, 80, 96])
+@pytest.mark.parametrize("cg", [16, 32, 48, 64, 80, 96])
 @pytest.mark.parametrize("plan,chunk", [(1, 0), (2, 64)], ids=["single", "c64"])
 def test_every_group_size_all_rows(cg, plan, chunk):
     """Every channels-per-workgroup variant of the kernel, on a shape where the last
