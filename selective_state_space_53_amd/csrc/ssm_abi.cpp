@@ -64,9 +64,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // LDS bytes of one scan workgroup of cg channels (must match the kernel's arrays):
 // Delta, Delta*x and (not in pass 1) the 8 partial readouts, [cg][36] floats each,
-// plus two tiles of widened B/C.
+// plus two tiles of widened B/C, 8 x (32 x 4 + 4) floats each.
 int64_t scan_lds_bytes(int cg, bool local) {
-    return (int64_t)((local ? 2 : 10) * cg * 36 + (local ? 4 : 0) + 2 * 1024) * 4;
+    return (int64_t)((local ? 2 : 10) * cg * 36 + (local ? 4 : 0) + 2 * 8 * 132) * 4;
 }
 
 // ---- launch cost model -------------------------------------------------------------
@@ -480,9 +480,9 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
 // ---- backward ---------------------------------------------------------------------
 
 // LDS bytes of one backward workgroup of cg channels (must match scan_bwd_kernel):
-// Delta, u, dq [cg][20]; two [8][cg][16] partial arrays; two B/C tiles; row sums
-// [16][cg/2][4].
-int64_t bwd_lds_bytes(int cg) { return (int64_t)(348 * cg + 1024) * 4; }
+// Delta, u, dq [cg][20]; two [8][cg][16] partial arrays; two B/C tiles of 8 x (16 x 4 + 4)
+// floats; row sums [16][cg/2][4].
+int64_t bwd_lds_bytes(int cg) { return (int64_t)(348 * cg + 1088) * 4; }
 
 // Relative time of one backward pass: `groups` workgroups of cg channels over `tiles`
 // 16-token tiles (as pass_cost, with the backward's LDS and its <= 168 VGPRs: 3 waves

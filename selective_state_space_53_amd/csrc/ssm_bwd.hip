@@ -53,7 +53,11 @@ constexpr int kRowP = kT;         // row of the per-pair partial arrays: unpadde
                                   // size decides whether two workgroups fit in a CU); the
                                   // 4-token slots of channel c are XOR-swizzled instead
                                   // (swz below)
-constexpr int kBcT = 8 * kT * 4;  // floats of widened B/C per tile
+// widened B/C of a tile: [pair][token][B0 B1 C0 C1], each pair's 16 tokens padded by 16
+// bytes, so that the rows of a wave reading two pairs' entries of one token hit different
+// banks (unpadded the pairs are 256 bytes apart: the same banks)
+constexpr int kBcPairT = kT * 4 + 4;
+constexpr int kBcT = 8 * kBcPairT;  // floats of widened B/C per tile
 
 // The swizzle of channel c's 4-token slots in its 64-byte partial row: rows of consecutive
 // channels alternate between the two halves of a 128-byte bank line, and bits 1 and 2 of c
@@ -337,7 +341,7 @@ void scan_bwd_kernel(const BwdParams p) {
     // B/C staging: threads 0..127 move one 16-byte (pair, token) entry per tile
     const bool bc_mover = tid < 128;
     const float* bcsrc = p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + (tid & 15)) * 4;
-    float* const bcdst = sBC + tid * 4;
+    float* const bcdst = sBC + (tid >> 4) * kBcPairT + (tid & 15) * 4;
 
     float* const myD = sD + cq * kRowF + 2 * jq;
     float* const myU = sU + cq * kRowF + 2 * jq;
@@ -435,7 +439,7 @@ void scan_bwd_kernel(const BwdParams p) {
         // same for the whole workgroup, so every branch on them is uniform
         const uint32_t ev = PACKED ? sEv : 0u;
         const uint32_t smask = ev & 0xffffu, emask = ev >> 16;
-        const float* bct = sBC + (it & 1) * kBcT + pr * (kT * 4);
+        const float* bct = sBC + (it & 1) * kBcT + pr * kBcPairT;
         // the recomputation and the adjoint (VALU-bound) run at raised wave priority, so
         // that a CU's other workgroups, in their load and store phases, do not take the
         // issue slots from them: 707 -> 674 us on the 2.8B layer, 372 -> 348 us on the

@@ -149,7 +149,13 @@ __global__ __launch_bounds__(256) void bc_widen_kernel(const IO* __restrict__ B,
 // --------------------------------------------------------------------- the scan
 constexpr int kTile = 32;                 // tokens per tile
 constexpr int kLdsRow = kTile + 4;        // padded [channel][token] LDS row (floats)
-constexpr int kBcTile = 8 * kTile * 4;    // floats of widened B/C per tile (8 state pairs)
+// Widened B/C of a tile in LDS: [pair][token][B0 B1 C0 C1], each pair's 32 tokens padded
+// by 16 bytes. A row reads one 16-byte entry per token, the same for its 16 lanes, and a
+// wave's four rows read up to four pairs at once (with 16 channels per workgroup always
+// four different ones); unpadded, the pairs are 512 bytes apart and the four reads hit
+// the same four banks, padded they fall on four different bank quads.
+constexpr int kBcPair = kTile * 4 + 4;    // floats per pair
+constexpr int kBcTile = 8 * kBcPair;      // floats of widened B/C per tile (8 state pairs)
 
 // One workgroup = CG channels (a multiple of 16) of one batch row x all 16 states,
 // CG*8 threads = CG/8 waves.
@@ -185,7 +191,8 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
     __shared__ float sD[CG * kLdsRow];
     __shared__ float sU[CG * kLdsRow];
-    __shared__ float sP[kOut ? 8 * CG * kLdsRow : 4];
+    constexpr int kPStride = CG * kLdsRow;   // floats per pair of partial readouts
+    __shared__ float sP[kOut ? 8 * kPStride : 4];
     __shared__ float sBC[2 * kBcTile];
 
     const int tid = threadIdx.x;
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     constexpr int kMoves = 256 / kMovers;
     const bool bc_mover = tid < kMovers;
     const float* bcsrc = p.bcq + ((b * 8 + (tid >> 5)) * p.lpad + (tid & 31)) * 4;
-    float* const bcdst = sBC + tid * 4;
+    float* const bcdst = sBC + (tid >> 5) * kBcPair + (tid & 31) * 4;
     // entry tid + m * kMovers: pair (tid >> 5) + m * kMovers / 32, the same token
     constexpr int64_t kMoveSrc = kMovers / 32;   // pairs per move
     float dsum = 0.0f;
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     if (bc_mover) {
 #pragma unroll
         for (int m = 0; m < kMoves; ++m)
-            *reinterpret_cast<float4*>(bcdst + m * kMovers * 4) = rbc[m];
+            *reinterpret_cast<float4*>(bcdst + m * kMoveSrc * kBcPair) = rbc[m];
     }
     wait_vmem();   // nothing in flight at the loop's entry: no wait at its top
 
@@ -389,8 +396,8 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // Every lane of a row reads the same (B0, B1, C0, C1) of a token from LDS, so B
         // and C arrive in VGPRs and every op below is a plain VOP2 with VGPR operands
         // (the fast FP32 issue path; SGPR or DPP operands halve it).
-        const float* bct = sBC + (it & 1) * kBcTile + pr * (kTile * 4);
-        float* const pout = sP + (pr * CG + cc) * kLdsRow;
+        const float* bct = sBC + (it & 1) * kBcTile + pr * kBcPair;
+        float* const pout = sP + pr * kPStride + cc * kLdsRow;
 #define SSM_TOKEN(OUT, DS, US, Q)                                                     \
     {                                                                                 \
         const float e0 = decay_exp2<IO>(DS * a2[0]);                                  \
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         if (bc_mover && it + 1 < nt) {
 #pragma unroll
             for (int m = 0; m < kMoves; ++m)
-                *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile + m * kMovers * 4) =
+                *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile + m * kMoveSrc * kBcPair) =
                     rbc[m];
         }
 
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             float yv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const float4 a = *reinterpret_cast<const float4*>(sP + (q * CG + cq) * kLdsRow + 4 * jq);
+                const float4 a = *reinterpret_cast<const float4*>(sP + q * kPStride + cq * kLdsRow + 4 * jq);
                 yv[0] += a.x; yv[1] += a.y; yv[2] += a.z; yv[3] += a.w;
             }
 #pragma unroll
