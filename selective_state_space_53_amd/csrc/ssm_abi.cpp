@@ -515,7 +515,7 @@ struct BwdPlan {
         ws_seq, ws_total;
 };
 
-// Where the checkpoints ([batch*dim][ceil(L/16)][16] fp32, offset 0) and q ([batch][dim][L]
+// Where the checkpoints ([batch][ceil(L/16)][dim][16] fp32, offset 0) and q ([batch][dim][L]
 // io) start a backward workspace, and the bytes they take. False on overflow.
 bool saved_layout(int64_t batch, int64_t seqlen, int64_t dim, ssm_dtype io_dtype, size_t* ws_q,
                   size_t* total) {
