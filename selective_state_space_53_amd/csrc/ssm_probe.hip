@@ -47,7 +47,12 @@ enum Kind {
     kExpFmac4 = 7,  // 1 v_exp_f32 then 4 independent v_fmac_f32 (VGPR), repeated
     kCoreStruct = 8,// the core with structured decays (no exp): per token 2 x v_mul for
                     // the decays, 2 x (v_mul, v_fmac) update, v_mul + v_fmac readout
-    kNumKinds = 9
+    kPermSwap16 = 9,// v_permlane16_swap_b32 a, b (gfx950: odd 16-lane rows of a <-> even
+                    // rows of b), on 8 independent register pairs
+    kCndmask = 10,  // v_cndmask_b32 acc, acc, vb, vcc
+    kCndmaskS = 11, // v_cndmask_b32_e64 acc, acc, vb, s[pair]   (VOP3, SGPR-pair condition)
+    kBfi = 12,      // v_bfi_b32 acc, vmask, vb, acc             (VOP3, VGPR operands)
+    kNumKinds = 13
 };
 
 // instructions per loop iteration, by kind
@@ -87,6 +92,27 @@ __global__ __launch_bounds__(256) void valu_kernel(int iters, uint64_t* __restri
 #undef OP
         } else if constexpr (KIND == kExp) {
 #define OP(i) asm volatile("v_exp_f32 %0, %1" : "+v"(a##i) : "v"(vb));
+            P16(OP) P16(OP) P16(OP) P16(OP)
+#undef OP
+        } else if constexpr (KIND == kPermSwap16) {
+            // pairs (a0,a1) .. (a14,a15): each pair is written again 8 instructions later
+#define OP2(i, j) asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(a##i), "+v"(a##j));
+#define PS OP2(0, 1) OP2(2, 3) OP2(4, 5) OP2(6, 7) OP2(8, 9) OP2(10, 11) OP2(12, 13) OP2(14, 15)
+            PS PS PS PS PS PS PS PS
+#undef PS
+#undef OP2
+        } else if constexpr (KIND == kCndmask) {
+#define OP(i) asm volatile("v_cndmask_b32 %0, %0, %1, vcc" : "+v"(a##i) : "v"(vb));
+            P16(OP) P16(OP) P16(OP) P16(OP)
+#undef OP
+        } else if constexpr (KIND == kCndmaskS) {
+            const uint64_t cond = (uint64_t)(uint32_t)sb * 0x100000001ull;
+#define OP(i) asm volatile("v_cndmask_b32_e64 %0, %0, %1, %2" : "+v"(a##i) : "v"(vb), "s"(cond));
+            P16(OP) P16(OP) P16(OP) P16(OP)
+#undef OP
+        } else if constexpr (KIND == kBfi) {
+            const uint32_t vm = (lane & 8) ? 0xffffffffu : 0u;
+#define OP(i) asm volatile("v_bfi_b32 %0, %1, %2, %0" : "+v"(a##i) : "v"(vm), "v"(vb));
             P16(OP) P16(OP) P16(OP) P16(OP)
 #undef OP
         } else if constexpr (KIND == kAddDpp) {
@@ -199,7 +225,7 @@ int ssmprobe_valu(int kind, int nblocks, int iters, uint64_t* rec, float* sink, 
     const dim3 g((unsigned)nblocks), b(256);
     switch (kind) {
 #define K(N) case N: hipLaunchKernelGGL(valu_kernel<N>, g, b, 0, s, iters, rec, sink, 1.0f, 0x3f7fbe77); break;
-        K(0) K(1) K(2) K(3) K(4) K(5) K(6) K(7) K(8)
+        K(0) K(1) K(2) K(3) K(4) K(5) K(6) K(7) K(8) K(9) K(10) K(11) K(12)
 #undef K
         default:
             return -1;
