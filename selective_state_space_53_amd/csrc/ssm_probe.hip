@@ -52,7 +52,9 @@ enum Kind {
     kCndmask = 10,  // v_cndmask_b32 acc, acc, vb, vcc
     kCndmaskS = 11, // v_cndmask_b32_e64 acc, acc, vb, s[pair]   (VOP3, SGPR-pair condition)
     kBfi = 12,      // v_bfi_b32 acc, vmask, vb, acc             (VOP3, VGPR operands)
-    kNumKinds = 13
+    kCmpCnd = 13,   // v_cmp_lt_i32 vcc, vlane, vk then v_cndmask_b32 acc, 0, acc, vcc:
+                    // the compare-and-select pair the compiler emits for a per-lane test
+    kNumKinds = 14
 };
 
 // instructions per loop iteration, by kind
@@ -114,6 +116,11 @@ __global__ __launch_bounds__(256) void valu_kernel(int iters, uint64_t* __restri
             const uint32_t vm = (lane & 8) ? 0xffffffffu : 0u;
 #define OP(i) asm volatile("v_bfi_b32 %0, %1, %2, %0" : "+v"(a##i) : "v"(vm), "v"(vb));
             P16(OP) P16(OP) P16(OP) P16(OP)
+#undef OP
+        } else if constexpr (KIND == kCmpCnd) {
+            const int vl = lane & 7;
+#define OP(i) asm volatile("v_cmp_lt_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, 0, %0, vcc" : "+v"(a##i) : "v"(vl), "v"(i & 3) : "vcc");
+            P16(OP) P16(OP)
 #undef OP
         } else if constexpr (KIND == kAddDpp) {
 #define OP(i) asm volatile("v_add_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf" : "+v"(a##i));
@@ -225,7 +232,7 @@ int ssmprobe_valu(int kind, int nblocks, int iters, uint64_t* rec, float* sink, 
     const dim3 g((unsigned)nblocks), b(256);
     switch (kind) {
 #define K(N) case N: hipLaunchKernelGGL(valu_kernel<N>, g, b, 0, s, iters, rec, sink, 1.0f, 0x3f7fbe77); break;
-        K(0) K(1) K(2) K(3) K(4) K(5) K(6) K(7) K(8) K(9) K(10) K(11) K(12)
+        K(0) K(1) K(2) K(3) K(4) K(5) K(6) K(7) K(8) K(9) K(10) K(11) K(12) K(13)
 #undef K
         default:
             return -1;
