@@ -118,7 +118,7 @@ typedef struct {
                            and reverse, and the backward skips its own forward pass; nothing
                            checks that they match (stale contents give wrong gradients).
                            0 = the backward recomputes them.                              */
-    int32_t structured_a; /* ssm_scan_fwd / ssm_scan_varlen_fwd with plan = 3 (the wave scan):
+    int32_t structured_a; /* ssm_scan_fwd with plan = 3 (the wave scan, batch rows only):
                            1 = for every channel d whose A row satisfies A[d,n] ==
                            (n+1)*A[d,0] exactly (fp32; checked on the device, per channel),
                            take the decays as powers exp(Delta*A[d,0])^(n+1) -- one exp per
