@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -247,10 +249,14 @@ __device__ __forceinline__ void bwd_event_tile(
 
 // (3 waves per SIMD: the register budget of 168 that lets two workgroups of 48 channels,
 // or three of 32, share a CU; 64 channels fill a CU's LDS with one workgroup of 8 waves)
-template <typename IO, int CG, bool PACKED, bool REV>
+// LEAN: the launch guarantees whole aligned tiles, every channel of every group in range,
+// softplus on and a gate: no per-token selects and no branches around the loads and
+// stores of the tile loop.
+template <typename IO, int CG, bool PACKED, bool REV, bool LEAN = false>
 __global__ __launch_bounds__(CG * 8) __attribute__((amdgpu_waves_per_eu(CG == 64 ? 2 : 3)))
 void scan_bwd_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
+    static_assert(!LEAN || (!PACKED && !REV), "lean tiles: causal batch rows");
     // causal: the recomputation leaves each token's decays exp(Delta A) in the tile's
     // partial rows, where the adjoint reads them back (and then overwrites them with its
     // partials) instead of evaluating the exp a second time. The anti-causal order needs
@@ -368,17 +374,36 @@ void scan_bwd_kernel(const BwdParams p) {
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
-        if (validq) {
-            rx.load(reinterpret_cast<const IO*>(xw + at(t0)), vec, nq);
-            rd.load(reinterpret_cast<const IO*>(dw + at(t0)), vec, nq);
-            if (zr) {
-                rz.load(reinterpret_cast<const IO*>(zw + at(t0)), vec, nq);
-                rq.load(reinterpret_cast<const IO*>(qw + at(t0)), vec, nq);
+        // one uniform branch for the tile rather than one per load
+        if (LEAN) {
+            const uint32_t o = at(t0);
+            rx.load(reinterpret_cast<const IO*>(xw + o), true, 2);
+            rd.load(reinterpret_cast<const IO*>(dw + o), true, 2);
+            rz.load(reinterpret_cast<const IO*>(zw + o), true, 2);
+            rq.load(reinterpret_cast<const IO*>(qw + o), true, 2);
+            rg.load(reinterpret_cast<const IO*>(gw + o), true, 2);
+        } else if (vec) {
+            if (validq) {
+                const uint32_t o = at(t0);
+                rx.load(reinterpret_cast<const IO*>(xw + o), true, 2);
+                rd.load(reinterpret_cast<const IO*>(dw + o), true, 2);
+                if (zr) {
+                    rz.load(reinterpret_cast<const IO*>(zw + o), true, 2);
+                    rq.load(reinterpret_cast<const IO*>(qw + o), true, 2);
+                }
+                rg.load(reinterpret_cast<const IO*>(gw + o), true, 2);
             }
-            rg.load(reinterpret_cast<const IO*>(gw + at(t0)), vec, nq);
+        } else if (validq) {
+            rx.load(reinterpret_cast<const IO*>(xw + at(t0)), false, nq);
+            rd.load(reinterpret_cast<const IO*>(dw + at(t0)), false, nq);
+            if (zr) {
+                rz.load(reinterpret_cast<const IO*>(zw + at(t0)), false, nq);
+                rq.load(reinterpret_cast<const IO*>(qw + at(t0)), false, nq);
+            }
+            rg.load(reinterpret_cast<const IO*>(gw + at(t0)), false, nq);
         }
         if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
-        if (valid) {
+        if (LEAN || valid) {
             const f32x2_t v = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x2_t*>(ck + (t0 / kT) * ckstride));
             rck = make_float2(v.x, v.y);
@@ -416,23 +441,37 @@ void scan_bwd_kernel(const BwdParams p) {
         if (PACKED && tid == 0) sEv = rev;
         if (it + 1 < ntiles) load_tile(REV ? ti + 1 : ti - 1);
         float dl[2], sg[2], dqv[2], uu[2], dzv[2];
+        // the usual case (a whole tile, softplus on, a gate) in straight-line code, the
+        // general one with its selects for padding tokens and options (bf16 only: with
+        // fp32 rows, which take twice the registers, the second copy of the code spills)
+        const bool fast = LEAN || (sizeof(IO) == 2 && vec && p.softplus && zr);
+        auto pre = [&](auto fast_c) {
+            constexpr bool kFast = decltype(fast_c)::value;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const float v = dv[k] + bias;
-            float delta = p.softplus ? softplus_f(v) : v;
-            delta = k < nq ? delta : 0.0f;       // padding tokens: no decay, no input
-            dl[k] = delta;
-            sg[k] = p.softplus ? sigmoid_f(v) : 1.0f;
-            uu[k] = delta * xv[k];
-            const float gz = zr ? silu_f(zv[k]) : 1.0f;
-            dqv[k] = gv[k] * gz;
-            dzv[k] = zr ? gv[k] * qv[k] * dsilu_f(zv[k]) : 0.0f;
-        }
+            for (int k = 0; k < 2; ++k) {
+                const float v = dv[k] + bias;
+                float delta = (kFast || p.softplus) ? softplus_f(v) : v;
+                if (!kFast) delta = k < nq ? delta : 0.0f;   // padding: no decay, no input
+                dl[k] = delta;
+                sg[k] = (kFast || p.softplus) ? sigmoid_f(v) : 1.0f;
+                uu[k] = delta * xv[k];
+                const float gz = (kFast || zr) ? silu_f(zv[k]) : 1.0f;
+                dqv[k] = gv[k] * gz;
+                dzv[k] = (kFast || zr) ? gv[k] * qv[k] * dsilu_f(zv[k]) : 0.0f;
+            }
+        };
+        if (fast) pre(std::true_type{});
+        else pre(std::false_type{});
         *reinterpret_cast<float2*>(myD) = make_float2(dl[0], dl[1]);
         *reinterpret_cast<float2*>(myU) = make_float2(uu[0], uu[1]);
         *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
-        if (zr && validq && nq > 0)
+        if (LEAN) {
+            store2(reinterpret_cast<IO*>(dzw + at(t0)), true, 2, dzv[0], dzv[1]);
+        } else if (fast) {
+            if (validq) store2(reinterpret_cast<IO*>(dzw + at(t0)), true, 2, dzv[0], dzv[1]);
+        } else if (zr && validq && nq > 0) {
             store2(reinterpret_cast<IO*>(dzw + at(t0)), vec, nq, dzv[0], dzv[1]);
+        }
         __syncthreads();
 
         // packed: the tile's tokens that start (smask) or end (emask) a sequence; the
@@ -590,14 +629,20 @@ void scan_bwd_kernel(const BwdParams p) {
                 dxo[k] = __builtin_fmaf(dqv[k], Dd, dus[k] * dl[k]);
                 const float dD = __builtin_fmaf(dus[k], xv[k], das[k]);
                 ddo[k] = dD * sg[k];
-                if (k < nq) {
+                if (LEAN || vec || k < nq) {
                     dDacc = __builtin_fmaf(dqv[k], xv[k], dDacc);
                     dbacc += ddo[k];
                 }
             }
-            if (validq && nq > 0) {
-                store2(reinterpret_cast<IO*>(dxw + at(t0)), vec, nq, dxo[0], dxo[1]);
-                store2(reinterpret_cast<IO*>(ddw + at(t0)), vec, nq, ddo[0], ddo[1]);
+            if (LEAN || vec) {
+                if (LEAN || validq) {
+                    const uint32_t o = at(t0);
+                    store2(reinterpret_cast<IO*>(dxw + o), true, 2, dxo[0], dxo[1]);
+                    store2(reinterpret_cast<IO*>(ddw + o), true, 2, ddo[0], ddo[1]);
+                }
+            } else if (validq && nq > 0) {
+                store2(reinterpret_cast<IO*>(dxw + at(t0)), false, nq, dxo[0], dxo[1]);
+                store2(reinterpret_cast<IO*>(ddw + at(t0)), false, nq, ddo[0], ddo[1]);
             }
         }
         // 16 tokens x 32 values (dB then dC): value i < 512 (i = tid, tid + CG*8) is the
@@ -613,7 +658,7 @@ void scan_bwd_kernel(const BwdParams p) {
 #pragma unroll
             for (int j = 0; j < kRowsPerPair; ++j)
                 sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 4 + which * 2 + (n & 1)];
-            if (k < nvalid) __builtin_nontemporal_store(sum, &pbc[(t0 + k) * 32 + v]);
+            if (LEAN || k < nvalid) __builtin_nontemporal_store(sum, &pbc[(t0 + k) * 32 + v]);
         }
     }
 
@@ -947,7 +992,26 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         BwdParams p2 = prm;
         p2.chunk_offset = 0;
         const dim3 g2((unsigned)(ngroups * prm.nchunks));
-        SSM_BWD_ALL(scan_bwd_kernel, g2, p2)
+        // the lean instantiation (bf16 causal batch rows): see scan_bwd_kernel
+        const bool lean = bf16 && !prm.cu && !prm.reverse && prm.aligned && prm.softplus &&
+                          prm.z && prm.seqlen % kT == 0 && prm.chunk_len % kT == 0 &&
+                          prm.dim % cg == 0;
+        if (lean) {
+            switch (cg) {
+#define SSM_LEAN(N)                                                                        \
+    case N:                                                                                \
+        hipLaunchKernelGGL((scan_bwd_kernel<uint16_t, N, false, false, true>), g2, dim3(N * 8), \
+                           0, stream, p2);                                                 \
+        break;
+                SSM_LEAN(32)
+                SSM_LEAN(48)
+                SSM_LEAN(64)
+#undef SSM_LEAN
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            SSM_BWD_ALL(scan_bwd_kernel, g2, p2)
+        }
     }
 #undef SSM_BWD_ALL
 #undef SSM_BWD
