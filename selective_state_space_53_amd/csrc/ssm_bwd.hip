@@ -348,6 +348,26 @@ void scan_bwd_kernel(const BwdParams p) {
     const bool bc_mover = tid < 128;
     const float* bcsrc = p.bcq + ((b * 8 + (tid >> 4)) * p.lpad + (tid & 15)) * 4;
     float* const bcdst = sBC + (tid >> 4) * kBcPairT + (tid & 15) * 4;
+    // LEAN: buffer resources over the workgroup's rows of the eight streams and its batch
+    // row's widened B/C; per lane a byte offset into each, per tile a uniform one
+    struct {
+        __amdgpu_buffer_rsrc_t x, d, z, g, q, dx, dd, dz, bc;
+        uint32_t vo, vbc;
+    } lio;
+    if constexpr (LEAN) {
+        const uint32_t ext = (uint32_t)(CG * L * (int64_t)sizeof(IO));
+        lio.x = make_rsrc(xw, ext);
+        lio.d = make_rsrc(dw, ext);
+        lio.z = make_rsrc(zw, ext);
+        lio.g = make_rsrc(gw, ext);
+        lio.q = make_rsrc(qw, ext);
+        lio.dx = make_rsrc(dxw, ext);
+        lio.dd = make_rsrc(ddw, ext);
+        lio.dz = make_rsrc(dzw, ext);
+        lio.bc = make_rsrc(p.bcq + b * 8 * p.lpad * 4, (uint32_t)(8 * p.lpad * 16));
+        lio.vo = at(0);
+        lio.vbc = (uint32_t)((((tid >> 4) & 7) * p.lpad + (tid & 15)) * 16);
+    }
 
     float* const myD = sD + cq * kRowF + 2 * jq;
     float* const myU = sU + cq * kRowF + 2 * jq;
@@ -375,13 +395,13 @@ void scan_bwd_kernel(const BwdParams p) {
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
         // one uniform branch for the tile rather than one per load
-        if (LEAN) {
-            const uint32_t o = at(t0);
-            rx.load(reinterpret_cast<const IO*>(xw + o), true, 2);
-            rd.load(reinterpret_cast<const IO*>(dw + o), true, 2);
-            rz.load(reinterpret_cast<const IO*>(zw + o), true, 2);
-            rq.load(reinterpret_cast<const IO*>(qw + o), true, 2);
-            rg.load(reinterpret_cast<const IO*>(gw + o), true, 2);
+        if constexpr (LEAN) {
+            const int so = (int)(t0 * (int64_t)sizeof(IO));
+            rx.w = __builtin_amdgcn_raw_buffer_load_b32(lio.x, (int)lio.vo, so, 0);
+            rd.w = __builtin_amdgcn_raw_buffer_load_b32(lio.d, (int)lio.vo, so, 0);
+            rz.w = __builtin_amdgcn_raw_buffer_load_b32(lio.z, (int)lio.vo, so, 0);
+            rq.w = __builtin_amdgcn_raw_buffer_load_b32(lio.q, (int)lio.vo, so, 0);
+            rg.w = __builtin_amdgcn_raw_buffer_load_b32(lio.g, (int)lio.vo, so, 0);
         } else if (vec) {
             if (validq) {
                 const uint32_t o = at(t0);
@@ -402,7 +422,11 @@ void scan_bwd_kernel(const BwdParams p) {
             }
             rg.load(reinterpret_cast<const IO*>(gw + at(t0)), false, nq);
         }
-        if (bc_mover) rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
+        if (LEAN && bc_mover)
+            rbc = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 lio.bc, (int)lio.vbc, (int)(t0 * 16), 0));
+        else if (bc_mover)
+            rbc = *reinterpret_cast<const float4*>(bcsrc + t0 * 4);
         if (LEAN || valid) {
             const f32x2_t v = __builtin_nontemporal_load(
                 reinterpret_cast<const f32x2_t*>(ck + (t0 / kT) * ckstride));
@@ -465,8 +489,9 @@ void scan_bwd_kernel(const BwdParams p) {
         *reinterpret_cast<float2*>(myD) = make_float2(dl[0], dl[1]);
         *reinterpret_cast<float2*>(myU) = make_float2(uu[0], uu[1]);
         *reinterpret_cast<float2*>(myQ) = make_float2(dqv[0], dqv[1]);
-        if (LEAN) {
-            store2(reinterpret_cast<IO*>(dzw + at(t0)), true, 2, dzv[0], dzv[1]);
+        if constexpr (LEAN) {
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(dzv[0], dzv[1]), lio.dz,
+                                                  (int)lio.vo, (int)(t0 * (int64_t)sizeof(IO)), 0);
         } else if (fast) {
             if (validq) store2(reinterpret_cast<IO*>(dzw + at(t0)), true, 2, dzv[0], dzv[1]);
         } else if (zr && validq && nq > 0) {
@@ -634,8 +659,14 @@ void scan_bwd_kernel(const BwdParams p) {
                     dbacc += ddo[k];
                 }
             }
-            if (LEAN || vec) {
-                if (LEAN || validq) {
+            if constexpr (LEAN) {
+                const int so = (int)(t0 * (int64_t)sizeof(IO));
+                __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(dxo[0], dxo[1]), lio.dx,
+                                                      (int)lio.vo, so, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(ddo[0], ddo[1]), lio.dd,
+                                                      (int)lio.vo, so, 0);
+            } else if (vec) {
+                if (validq) {
                     const uint32_t o = at(t0);
                     store2(reinterpret_cast<IO*>(dxw + o), true, 2, dxo[0], dxo[1]);
                     store2(reinterpret_cast<IO*>(ddw + o), true, 2, ddo[0], ddo[1]);
@@ -993,9 +1024,11 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         p2.chunk_offset = 0;
         const dim3 g2((unsigned)(ngroups * prm.nchunks));
         // the lean instantiation (bf16 causal batch rows): see scan_bwd_kernel
+        // (and a batch row of B/C below 2 GiB, for its buffer offsets; a workgroup's rows
+        // are below 4 GiB for every plan)
         const bool lean = bf16 && !prm.cu && !prm.reverse && prm.aligned && prm.softplus &&
                           prm.z && prm.seqlen % kT == 0 && prm.chunk_len % kT == 0 &&
-                          prm.dim % cg == 0;
+                          prm.dim % cg == 0 && prm.lpad * 128 < (int64_t(1) << 31);
         if (lean) {
             switch (cg) {
 #define SSM_LEAN(N)                                                                        \

@@ -88,6 +88,17 @@ __device__ __forceinline__ void store_stream4(float* p, float a, float b, float 
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
 }
 
+// Raw buffer accesses: a 128-bit resource held in scalar registers (base address, byte
+// extent, and the format word of a raw buffer on this GPU family), a 32-bit per-lane byte
+// offset and a uniform one, so that an access needs no 64-bit address arithmetic per lane.
+// An access past the extent reads zero and writes nothing.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 __device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_one(uint16_t* p, float v) {
     *p = __builtin_bit_cast(uint16_t, (__bf16)v);

@@ -262,6 +262,26 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     const bool bc_mover = tid < kMovers;
     const float* bcsrc = p.bcq + ((b * 8 + (tid >> 5)) * p.lpad + (tid & 31)) * 4;
     float* const bcdst = sBC + (tid >> 5) * kBcPair + (tid & 31) * 4;
+    // LEAN: buffer resources over the workgroup's rows of x, Delta, z, y and q (CG rows of
+    // seqlen tokens from row d0) and over its batch row's widened B/C; per lane one byte
+    // offset into each (its row and 4 tokens, its B/C entry), per tile one uniform offset
+    struct {
+        __amdgpu_buffer_rsrc_t x, d, z, y, q, bc;
+        uint32_t vo, vbc;
+    } lio;
+    if constexpr (LEAN) {
+        const int64_t wb = (b * p.dim + d0) * p.seqlen;
+        const uint32_t ext = (uint32_t)(CG * p.seqlen * (int64_t)sizeof(IO));
+        lio.x = make_rsrc(static_cast<const IO*>(p.x) + wb, ext);
+        lio.d = make_rsrc(static_cast<const IO*>(p.delta) + wb, ext);
+        lio.z = make_rsrc(kOut ? static_cast<const IO*>(p.z) + wb : nullptr, kOut ? ext : 0u);
+        lio.y = make_rsrc(kOut ? static_cast<const IO*>(p.y) + wb : nullptr, kOut ? ext : 0u);
+        lio.q = make_rsrc(CKPT && p.q ? static_cast<const IO*>(p.q) + wb : nullptr,
+                          CKPT && p.q ? ext : 0u);
+        lio.bc = make_rsrc(p.bcq + b * 8 * p.lpad * 4, (uint32_t)(8 * p.lpad * 16));
+        lio.vo = (uint32_t)((cq * p.seqlen + 4 * jq) * (int64_t)sizeof(IO));
+        lio.vbc = (uint32_t)((((tid >> 5) & 7) * p.lpad + (tid & 31)) * 16);
+    }
     // entry tid + m * kMovers: pair (tid >> 5) + m * kMovers / 32, the same token
     constexpr int64_t kMoveSrc = kMovers / 32;   // pairs per move
     float dsum = 0.0f;
@@ -342,10 +362,19 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         const bool vec = p.aligned && nvalid == kTile;
         // (one uniform branch for the whole tile rather than one per load: the per-load
         // form costs a branch and an exec-mask change per row)
-        if (LEAN) {
-            rx.load(xr + t0 + 4 * jq, true, 4);
-            rdl.load(dr + t0 + 4 * jq, true, 4);
-            if (kOut) rz.load(zr + t0 + 4 * jq, true, 4);
+        if constexpr (LEAN) {
+            const int so = (int)(t0 * (int64_t)sizeof(IO));
+            u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(lio.x, (int)lio.vo, so, 0);
+            rx.w[0] = v.x;
+            rx.w[1] = v.y;
+            v = __builtin_amdgcn_raw_buffer_load_b64(lio.d, (int)lio.vo, so, 0);
+            rdl.w[0] = v.x;
+            rdl.w[1] = v.y;
+            if (kOut) {
+                v = __builtin_amdgcn_raw_buffer_load_b64(lio.z, (int)lio.vo, so, 0);
+                rz.w[0] = v.x;
+                rz.w[1] = v.y;
+            }
         } else if (vec) {
             if (validq) {
                 rx.load(xr + t0 + 4 * jq, true, 4);
@@ -357,7 +386,13 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             rdl.load(dr + t0 + 4 * jq, false, nq);
             if (zr) rz.load(zr + t0 + 4 * jq, false, nq);
         }
-        if (bc_mover) {
+        if (LEAN && bc_mover) {
+#pragma unroll
+            for (int m = 0; m < kMoves; ++m)
+                rbc[m] = __builtin_bit_cast(
+                    float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                lio.bc, (int)lio.vbc, (int)((m * kMoveSrc * p.lpad + t0) * 16), 0));
+        } else if (bc_mover) {
 #pragma unroll
             for (int m = 0; m < kMoves; ++m)
                 rbc[m] = *reinterpret_cast<const float4*>(bcsrc + (m * kMoveSrc * p.lpad + t0) * 4);
@@ -544,13 +579,21 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) yv[k] += post_a[k];
             // training forward: q, the output before the gate, for the backward
-            if (CKPT && p.q && (LEAN || (validq && nq > 0)))
-                Store4<IO>::store(static_cast<IO*>(p.q) + rowq * p.seqlen + t0 + 4 * jq,
-                                  LEAN || vec, nq, yv);
+            if constexpr (LEAN) {
+                if (CKPT && p.q)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, lio.q,
+                        (int)lio.vo, (int)(t0 * (int64_t)sizeof(IO)), 0);
+            } else if (CKPT && p.q && validq && nq > 0) {
+                Store4<IO>::store(static_cast<IO*>(p.q) + rowq * p.seqlen + t0 + 4 * jq, vec, nq,
+                                  yv);
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) yv[k] *= post_g[k];
-            if (LEAN) {
-                Store4<IO>::store(yr + t0 + 4 * jq, true, 4, yv);
+            if constexpr (LEAN) {
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, lio.y,
+                    (int)lio.vo, (int)(t0 * (int64_t)sizeof(IO)), 0);
             } else if (vec ? validq : (validq && nq > 0)) {
                 if (p.accumulate) {
                     Raw4<IO> old;
@@ -714,8 +757,10 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
     // the lean instantiation (bf16 causal batch rows): see scan_kernel
     if constexpr (sizeof(IO) == 2 && !REV && !PACKED) {
         const int64_t tile = kTile;
+        // (and 32-bit buffer offsets: a workgroup's rows and a batch row of B/C below 2 GiB)
         if (prm.aligned && prm.softplus && !prm.accumulate && (LOCAL || prm.z) &&
-            prm.seqlen % tile == 0 && prm.chunk_len % tile == 0 && prm.dim % cg == 0)
+            prm.seqlen % tile == 0 && prm.chunk_len % tile == 0 && prm.dim % cg == 0 &&
+            (int64_t)cg * prm.seqlen * 2 < (int64_t(1) << 31) && prm.lpad * 128 < (int64_t(1) << 31))
             return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, true>(cg, grid, stream, prm);
     }
     return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, false>(cg, grid, stream, prm);
