@@ -185,17 +185,19 @@ constexpr int kBcTile = 8 * kBcPair;      // floats of widened B/C per tile (8 s
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
 // without an event take the same unrolled path as unpacked input.
-// LEAN: the launch guarantees whole aligned tiles (seqlen and chunk_len multiples of the
-// tile), every channel of every group in range, softplus on, a gate when this pass
-// applies one and no accumulation: the tile loop then has no per-token selects and no
+// LEAN (1: with the gate z, 2: without): the launch guarantees whole aligned tiles
+// (seqlen and chunk_len multiples of the tile), every channel of every group in range,
+// softplus on and no accumulation: the tile loop then has no per-token selects and no
 // branches around its loads and stores (4% of the kernel on the Mamba-2.8B layer shape).
-template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG, bool LEAN>
+template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG, int LEAN>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
     static_assert(!CKPT || !LOCAL, "checkpoints: final pass");
-    static_assert(!LEAN || (!PACKED && !REV), "lean tiles: causal batch rows");
+    constexpr bool kLean = LEAN != 0;
+    static_assert(!kLean || (!PACKED && !REV), "lean tiles: causal batch rows");
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
+    constexpr bool kLeanGate = kOut && LEAN == 1;
     __shared__ float sD[CG * kLdsRow];
     __shared__ float sU[CG * kLdsRow];
     constexpr int kPStride = CG * kLdsRow;   // floats per pair of partial readouts
@@ -269,12 +271,13 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         __amdgpu_buffer_rsrc_t x, d, z, y, q, bc;
         uint32_t vo, vbc;
     } lio;
-    if constexpr (LEAN) {
+    if constexpr (kLean) {
         const int64_t wb = (b * p.dim + d0) * p.seqlen;
         const uint32_t ext = (uint32_t)(CG * p.seqlen * (int64_t)sizeof(IO));
         lio.x = make_rsrc(static_cast<const IO*>(p.x) + wb, ext);
         lio.d = make_rsrc(static_cast<const IO*>(p.delta) + wb, ext);
-        lio.z = make_rsrc(kOut ? static_cast<const IO*>(p.z) + wb : nullptr, kOut ? ext : 0u);
+        lio.z = make_rsrc(kLeanGate ? static_cast<const IO*>(p.z) + wb : nullptr,
+                          kLeanGate ? ext : 0u);
         lio.y = make_rsrc(kOut ? static_cast<const IO*>(p.y) + wb : nullptr, kOut ? ext : 0u);
         lio.q = make_rsrc(CKPT && p.q ? static_cast<const IO*>(p.q) + wb : nullptr,
                           CKPT && p.q ? ext : 0u);
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         const bool vec = p.aligned && nvalid == kTile;
         // (one uniform branch for the whole tile rather than one per load: the per-load
         // form costs a branch and an exec-mask change per row)
-        if constexpr (LEAN) {
+        if constexpr (kLean) {
             const int so = (int)(t0 * (int64_t)sizeof(IO));
             u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(lio.x, (int)lio.vo, so, 0);
             rx.w[0] = v.x;
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             v = __builtin_amdgcn_raw_buffer_load_b64(lio.d, (int)lio.vo, so, 0);
             rdl.w[0] = v.x;
             rdl.w[1] = v.y;
-            if (kOut) {
+            if (kLeanGate) {
                 v = __builtin_amdgcn_raw_buffer_load_b64(lio.z, (int)lio.vo, so, 0);
                 rz.w[0] = v.x;
                 rz.w[1] = v.y;
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             rdl.load(dr + t0 + 4 * jq, false, nq);
             if (zr) rz.load(zr + t0 + 4 * jq, false, nq);
         }
-        if (LEAN && bc_mover) {
+        if (kLean && bc_mover) {
 #pragma unroll
             for (int m = 0; m < kMoves; ++m)
                 rbc[m] = __builtin_bit_cast(
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // The usual case -- a whole tile, softplus on, a gate if this pass applies one --
         // takes straight-line code; the selects of the general form (padding tokens,
         // options) cost ~5% of the kernel on the Mamba-2.8B layer shape.
-        const bool fast = LEAN || (vec && p.softplus && (!kOut || zr));
+        const bool fast = kLean || (vec && p.softplus && (!kOut || zr));
         auto pre = [&](auto fast_c) {
             constexpr bool kFast = decltype(fast_c)::value;
 #pragma unroll
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             if (kOut) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    post_g[k] = (kFast || zr) ? silu_f(zv[k]) : 1.0f;
+                    post_g[k] = LEAN == 2 ? 1.0f : (kFast || zr) ? silu_f(zv[k]) : 1.0f;
                     post_a[k] = Dd * xv[k];
                 }
             }
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) yv[k] += post_a[k];
             // training forward: q, the output before the gate, for the backward
-            if constexpr (LEAN) {
+            if constexpr (kLean) {
                 if (CKPT && p.q)
                     __builtin_amdgcn_raw_buffer_store_b64(
                         u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, lio.q,
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k) yv[k] *= post_g[k];
-            if constexpr (LEAN) {
+            if constexpr (kLean) {
                 __builtin_amdgcn_raw_buffer_store_b64(
                     u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, lio.y,
                     (int)lio.vo, (int)(t0 * (int64_t)sizeof(IO)), 0);
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(const DecodeParams p)
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, bool LEAN>
+template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int LEAN>
 hipError_t launch_scan_cg(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
     switch (cg) {
 #define SSM_CASE(N)                                                                        \
@@ -758,12 +761,16 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
     if constexpr (sizeof(IO) == 2 && !REV && !PACKED) {
         const int64_t tile = kTile;
         // (and 32-bit buffer offsets: a workgroup's rows and a batch row of B/C below 2 GiB)
-        if (prm.aligned && prm.softplus && !prm.accumulate && (LOCAL || prm.z) &&
-            prm.seqlen % tile == 0 && prm.chunk_len % tile == 0 && prm.dim % cg == 0 &&
-            (int64_t)cg * prm.seqlen * 2 < (int64_t(1) << 31) && prm.lpad * 128 < (int64_t(1) << 31))
-            return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, true>(cg, grid, stream, prm);
+        if (prm.aligned && prm.softplus && !prm.accumulate && prm.seqlen % tile == 0 &&
+            prm.chunk_len % tile == 0 && prm.dim % cg == 0 &&
+            (int64_t)cg * prm.seqlen * 2 < (int64_t(1) << 31) && prm.lpad * 128 < (int64_t(1) << 31)) {
+            if (LOCAL || prm.z)
+                return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 1>(cg, grid, stream, prm);
+            if constexpr (!LOCAL)
+                return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 2>(cg, grid, stream, prm);
+        }
     }
-    return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, false>(cg, grid, stream, prm);
+    return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 0>(cg, grid, stream, prm);
 }
 
 template <typename IO, bool LOCAL>
