@@ -1,0 +1,102 @@
+"""The lean and the general form of the scan kernels give the same bits.
+
+A bf16 causal launch on whole aligned tiles with every channel group in range, softplus
+on and no accumulation runs the kernels' lean form (straight-line tile loops, buffer
+accesses); any other launch runs the general form. The two do the same arithmetic in the
+same order, so a shape run once with a channel grouping that qualifies and once with one
+that does not (the last group ragged) must agree bit for bit wherever the grouping does not
+change a summation order: y and h_final of the forward; dx, ddelta, dz, dA, dD,
+ddelta_bias and dh0 of the backward (dB and dC are sums over channels, grouped
+differently, and are checked against the oracle instead). Both are also checked against
+the fp64 oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_53_amd import binding  # noqa: F401  (fails loudly if unbuilt)
+
+
+def _same(a, b, what):
+    a, b = a.cpu(), b.cpu()
+    diff = (a.float() - b.float()).abs().max().item() if a.numel() else 0.0
+    assert torch.equal(a, b), f"{what}: lean and general forms differ (max {diff:.3e})"
+
+
+@pytest.mark.parametrize("use_z", [True, False], ids=["gated", "scan_only"])
+@pytest.mark.parametrize("plan,chunk", [(1, 0), (2, 64)], ids=["single", "c64"])
+def test_forward_lean_equals_general(use_z, plan, chunk):
+    # 96 channels: groups of 16 (every group whole: lean) or 64 (a ragged last group:
+    # general); 256 tokens = 8 whole tiles
+    cfg = synth.ScanConfig("lean", 2, 256, 96, io="bf16", seed=901)
+    say("case lean forward", use_z, plan, chunk)
+    inp = synth.scan_inputs(cfg, DEV)
+    gen = torch.Generator(device="cpu").manual_seed(902)
+    h0 = torch.randn((2, 96, 16), generator=gen).to(DEV)
+    yl, hl = parity.gpu_scan(inp, use_z=use_z, h0=h0, plan=plan, chunk_len=chunk,
+                             group_channels=16)
+    yg, hg = parity.gpu_scan(inp, use_z=use_z, h0=h0, plan=plan, chunk_len=chunk,
+                             group_channels=64)
+    torch.cuda.synchronize()
+    _same(yl, yg, "y")
+    _same(hl, hg, "h_final")
+    yr, hr = parity.oracle_full(inp, use_z=use_z, h0=h0)
+    ey, eh = parity.rowwise_err(yl, yr), parity.rowwise_err(hl, hr)
+    say(f"  y err {ey:.3e}  h_final err {eh:.3e}")
+    assert ey <= parity.TOL["bf16"] and eh <= parity.TOL["bf16"]
+
+
+def test_backward_lean_equals_general():
+    # 64 channels: backward groups of 32 (lean) or 48 (a ragged last group: general); the
+    # forward checkpoint pass likewise in groups of 16 (lean) or 48 (general)
+    from selective_state_space_53_amd import binding
+    batch, L, dim = 2, 256, 64
+    cfg = synth.ScanConfig("leanb", batch, L, dim, io="bf16", seed=911)
+    say("case lean backward")
+    inp = synth.scan_inputs(cfg, DEV)
+    dy = synth.scan_inputs(cfg, DEV, seed=912)["z"]
+    gen = torch.Generator(device="cpu").manual_seed(913)
+    h0 = torch.randn((batch, dim, 16), generator=gen).to(DEV)
+    dhf = torch.randn((batch, dim, 16), generator=gen).to(DEV)
+
+    def run(fwd_cg, bwd_cg):
+        g = binding.ssm_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                                 D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], h0=h0,
+                                 dh_final=dhf, want_dh0=True, group_channels=fwd_cg,
+                                 bwd_group_channels=bwd_cg)
+        torch.cuda.synchronize()
+        return g
+
+    gl, gg = run(16, 32), run(48, 48)
+    for k in ("dx", "ddelta", "dz", "dA", "dD", "ddelta_bias", "dh0"):
+        _same(gl[k], gg[k], k)
+    ref = oracle.Oracle().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                                   D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                   h0=h0, dh_final=dhf, nthreads=parity.threads())
+    for g in (gl, gg):
+        for k in ("dB", "dC"):
+            got = oracle.f64(g[k]).reshape(batch, -1)
+            r = np.asarray(ref[k]).reshape(batch, -1)
+            e = parity.rowwise_err(got, r)
+            say(f"  {k} err {e:.3e}")
+            assert e <= parity.TOL["bf16"]
