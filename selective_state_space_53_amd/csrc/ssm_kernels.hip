@@ -185,16 +185,16 @@ constexpr int kBcTile = 8 * kBcPair;      // floats of widened B/C per tile (8 s
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
 // without an event take the same unrolled path as unpacked input.
-// LEAN (1: with the gate z, 2: without): the launch guarantees whole aligned tiles
-// (seqlen and chunk_len multiples of the tile), every channel of every group in range,
-// softplus on and no accumulation: the tile loop then has no per-token selects and no
-// branches around its loads and stores (4% of the kernel on the Mamba-2.8B layer shape).
+// LEAN (1: with the gate z, 2: without): the launch guarantees batch rows of whole aligned
+// tiles (seqlen and chunk_len multiples of the tile), every channel of every group in range
+// and softplus on: the tile loop then has no per-token selects and no branches around its
+// loads and stores (4% of the kernel on the Mamba-2.8B layer shape).
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG, int LEAN>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
     static_assert(!CKPT || !LOCAL, "checkpoints: final pass");
     constexpr bool kLean = LEAN != 0;
-    static_assert(!kLean || (!PACKED && !REV), "lean tiles: causal batch rows");
+    static_assert(!kLean || !PACKED, "lean tiles: batch rows");
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
     constexpr bool kLeanGate = kOut && LEAN == 1;
@@ -594,9 +594,17 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) yv[k] *= post_g[k];
             if constexpr (kLean) {
+                const int so = (int)(t0 * (int64_t)sizeof(IO));
+                if (p.accumulate) {   // (uniform) the second direction of a bidirectional scan
+                    const u32x2_t o = __builtin_amdgcn_raw_buffer_load_b64(lio.y, (int)lio.vo, so, 0);
+                    yv[0] += bf16_lo(o.x);
+                    yv[1] += bf16_hi(o.x);
+                    yv[2] += bf16_lo(o.y);
+                    yv[3] += bf16_hi(o.y);
+                }
                 __builtin_amdgcn_raw_buffer_store_b64(
                     u32x2_t{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, lio.y,
-                    (int)lio.vo, (int)(t0 * (int64_t)sizeof(IO)), 0);
+                    (int)lio.vo, so, 0);
             } else if (vec ? validq : (validq && nq > 0)) {
                 if (p.accumulate) {
                     Raw4<IO> old;
@@ -757,11 +765,11 @@ hipError_t launch_scan_cg(int cg, dim3 grid, hipStream_t stream, const ScanParam
 
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT>
 hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
-    // the lean instantiation (bf16 causal batch rows): see scan_kernel
-    if constexpr (sizeof(IO) == 2 && !REV && !PACKED) {
+    // the lean instantiation (bf16 batch rows): see scan_kernel
+    if constexpr (sizeof(IO) == 2 && !PACKED) {
         const int64_t tile = kTile;
         // (and 32-bit buffer offsets: a workgroup's rows and a batch row of B/C below 2 GiB)
-        if (prm.aligned && prm.softplus && !prm.accumulate && prm.seqlen % tile == 0 &&
+        if (prm.aligned && prm.softplus && prm.seqlen % tile == 0 &&
             prm.chunk_len % tile == 0 && prm.dim % cg == 0 &&
             (int64_t)cg * prm.seqlen * 2 < (int64_t(1) << 31) && prm.lpad * 128 < (int64_t(1) << 31)) {
             if (LOCAL || prm.z)

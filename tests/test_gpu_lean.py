@@ -1,8 +1,8 @@
 """The lean and the general form of the scan kernels give the same bits.
 
-A bf16 causal launch on whole aligned tiles with every channel group in range, softplus
-on and no accumulation runs the kernels' lean form (straight-line tile loops, buffer
-accesses); any other launch runs the general form. The two do the same arithmetic in the
+A bf16 launch of batch rows (either direction) on whole aligned tiles with every channel
+group in range and softplus on runs the kernels' lean form (straight-line tile loops,
+buffer accesses); any other launch runs the general form. The two do the same arithmetic in the
 same order, so a shape run once with a channel grouping that qualifies and once with one
 that does not (the last group ragged) must agree bit for bit wherever the grouping does not
 change a summation order: y and h_final of the forward; dx, ddelta, dz, dA, dD,
@@ -43,36 +43,63 @@ def _same(a, b, what):
     assert torch.equal(a, b), f"{what}: lean and general forms differ (max {diff:.3e})"
 
 
+@pytest.mark.parametrize("reverse", [False, True], ids=["causal", "anticausal"])
 @pytest.mark.parametrize("use_z", [True, False], ids=["gated", "scan_only"])
 @pytest.mark.parametrize("plan,chunk", [(1, 0), (2, 64)], ids=["single", "c64"])
-def test_forward_lean_equals_general(use_z, plan, chunk):
+def test_forward_lean_equals_general(use_z, plan, chunk, reverse):
     # 96 channels: groups of 16 (every group whole: lean) or 64 (a ragged last group:
     # general); 256 tokens = 8 whole tiles
     cfg = synth.ScanConfig("lean", 2, 256, 96, io="bf16", seed=901)
-    say("case lean forward", use_z, plan, chunk)
+    say("case lean forward", use_z, plan, chunk, reverse)
     inp = synth.scan_inputs(cfg, DEV)
     gen = torch.Generator(device="cpu").manual_seed(902)
     h0 = torch.randn((2, 96, 16), generator=gen).to(DEV)
     yl, hl = parity.gpu_scan(inp, use_z=use_z, h0=h0, plan=plan, chunk_len=chunk,
-                             group_channels=16)
+                             group_channels=16, reverse=reverse)
     yg, hg = parity.gpu_scan(inp, use_z=use_z, h0=h0, plan=plan, chunk_len=chunk,
-                             group_channels=64)
+                             group_channels=64, reverse=reverse)
     torch.cuda.synchronize()
     _same(yl, yg, "y")
     _same(hl, hg, "h_final")
-    yr, hr = parity.oracle_full(inp, use_z=use_z, h0=h0)
+    if reverse:
+        # the oracle of the anti-causal scan: the causal one on time-reversed inputs
+        flip = {k: (v.flip(-1) if k in ("x", "delta", "z") else v.flip(1) if k in ("B", "C") else v)
+                for k, v in inp.items()}
+        yr, hr = parity.oracle_full(flip, use_z=use_z, h0=h0)
+        yr = np.ascontiguousarray(np.asarray(yr)[..., ::-1])
+    else:
+        yr, hr = parity.oracle_full(inp, use_z=use_z, h0=h0)
     ey, eh = parity.rowwise_err(yl, yr), parity.rowwise_err(hl, hr)
     say(f"  y err {ey:.3e}  h_final err {eh:.3e}")
     assert ey <= parity.TOL["bf16"] and eh <= parity.TOL["bf16"]
 
 
-def test_backward_lean_equals_general():
+def test_bidirectional_accumulate_lean_equals_general():
+    """The causal scan, then the anti-causal one accumulated into the same y."""
+    from selective_state_space_53_amd import binding
+    cfg = synth.ScanConfig("leanacc", 2, 256, 96, io="bf16", seed=921)
+    say("case lean accumulate")
+    inp = synth.scan_inputs(cfg, DEV)
+    outs = []
+    for cg in (16, 64):
+        y = parity.gpu_scan(inp, final=False, group_channels=cg)
+        y = y[0] if isinstance(y, tuple) else y
+        binding.ssm_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                             z=inp["z"], delta_bias=inp["delta_bias"], y=y, reverse=True,
+                             accumulate=True, group_channels=cg)
+        torch.cuda.synchronize()
+        outs.append(y.clone())
+    _same(outs[0], outs[1], "y (both directions)")
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["causal", "anticausal"])
+def test_backward_lean_equals_general(reverse):
     # 64 channels: backward groups of 32 (lean) or 48 (a ragged last group: general); the
     # forward checkpoint pass likewise in groups of 16 (lean) or 48 (general)
     from selective_state_space_53_amd import binding
     batch, L, dim = 2, 256, 64
     cfg = synth.ScanConfig("leanb", batch, L, dim, io="bf16", seed=911)
-    say("case lean backward")
+    say("case lean backward", reverse)
     inp = synth.scan_inputs(cfg, DEV)
     dy = synth.scan_inputs(cfg, DEV, seed=912)["z"]
     gen = torch.Generator(device="cpu").manual_seed(913)
@@ -83,20 +110,28 @@ def test_backward_lean_equals_general():
         g = binding.ssm_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
                                  D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], h0=h0,
                                  dh_final=dhf, want_dh0=True, group_channels=fwd_cg,
-                                 bwd_group_channels=bwd_cg)
+                                 bwd_group_channels=bwd_cg, reverse=reverse)
         torch.cuda.synchronize()
         return g
 
     gl, gg = run(16, 32), run(48, 48)
     for k in ("dx", "ddelta", "dz", "dA", "dD", "ddelta_bias", "dh0"):
         _same(gl[k], gg[k], k)
-    ref = oracle.Oracle().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
-                                   D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
-                                   h0=h0, dh_final=dhf, nthreads=parity.threads())
+    if reverse:   # time-reversed inputs through the causal oracle, gradients reversed back
+        fl = lambda t: t.flip(-1)
+        ref = oracle.Oracle().scan_bwd(fl(inp["x"]), fl(inp["delta"]), inp["A"], inp["B"].flip(1),
+                                       inp["C"].flip(1), fl(dy), D=inp["D"], z=fl(inp["z"]),
+                                       delta_bias=inp["delta_bias"], h0=h0, dh_final=dhf,
+                                       nthreads=parity.threads())
+        ref = {k: (np.asarray(v)[:, ::-1] if k in ("dB", "dC") else v) for k, v in ref.items()}
+    else:
+        ref = oracle.Oracle().scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
+                                       D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"],
+                                       h0=h0, dh_final=dhf, nthreads=parity.threads())
     for g in (gl, gg):
         for k in ("dB", "dC"):
             got = oracle.f64(g[k]).reshape(batch, -1)
-            r = np.asarray(ref[k]).reshape(batch, -1)
+            r = np.ascontiguousarray(np.asarray(ref[k])).reshape(batch, -1)
             e = parity.rowwise_err(got, r)
             say(f"  {k} err {e:.3e}")
             assert e <= parity.TOL["bf16"]
