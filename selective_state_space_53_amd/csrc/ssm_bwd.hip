@@ -249,14 +249,13 @@ __device__ __forceinline__ void bwd_event_tile(
 
 // (3 waves per SIMD: the register budget of 168 that lets two workgroups of 48 channels,
 // or three of 32, share a CU; 64 channels fill a CU's LDS with one workgroup of 8 waves)
-// LEAN: the launch guarantees batch rows of whole aligned tiles, every channel of every
-// group in range, softplus on and a gate: no per-token selects and no branches around the
+// LEAN: the launch guarantees rows of whole aligned tiles, every channel of every group
+// in range, softplus on and a gate: no per-token selects and no branches around the
 // loads and stores of the tile loop.
 template <typename IO, int CG, bool PACKED, bool REV, bool LEAN = false>
 __global__ __launch_bounds__(CG * 8) __attribute__((amdgpu_waves_per_eu(CG == 64 ? 2 : 3)))
 void scan_bwd_kernel(const BwdParams p) {
     static_assert(CG % 16 == 0 && CG >= 32 && CG <= 64, "channel group");
-    static_assert(!LEAN || !PACKED, "lean tiles: batch rows");
     // The adjoint evaluates each token's decays exp(Delta A) again rather than reading back
     // what the recomputation produced: kept in the tile's partial rows in LDS they saved
     // the VALU two exps and two multiplies per token, but since the tile loop lost its
@@ -1005,17 +1004,23 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         BwdParams p2 = prm;
         p2.chunk_offset = 0;
         const dim3 g2((unsigned)(ngroups * prm.nchunks));
-        // the lean instantiation (bf16 batch rows): see scan_bwd_kernel
+        // the lean instantiation (bf16): see scan_bwd_kernel
         // (and a batch row of B/C below 2 GiB, for its buffer offsets; a workgroup's rows
         // are below 4 GiB for every plan)
-        const bool lean = bf16 && !prm.cu && prm.aligned && prm.softplus && prm.z &&
+        const bool lean = bf16 && prm.aligned && prm.softplus && prm.z &&
                           prm.seqlen % kT == 0 && prm.chunk_len % kT == 0 &&
                           prm.dim % cg == 0 && prm.lpad * 128 < (int64_t(1) << 31);
         if (lean) {
             switch (cg) {
 #define SSM_LEAN(N)                                                                        \
     case N:                                                                                \
-        if (prm.reverse)                                                                   \
+        if (prm.cu && prm.reverse)                                                         \
+            hipLaunchKernelGGL((scan_bwd_kernel<uint16_t, N, true, true, true>), g2,          \
+                               dim3(N * 8), 0, stream, p2);                                \
+        else if (prm.cu)                                                                   \
+            hipLaunchKernelGGL((scan_bwd_kernel<uint16_t, N, true, false, true>), g2,         \
+                               dim3(N * 8), 0, stream, p2);                                \
+        else if (prm.reverse)                                                              \
             hipLaunchKernelGGL((scan_bwd_kernel<uint16_t, N, false, true, true>), g2,         \
                                dim3(N * 8), 0, stream, p2);                                \
         else                                                                               \

@@ -185,16 +185,15 @@ constexpr int kBcTile = 8 * kBcPair;      // floats of widened B/C per tile (8 s
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
 // without an event take the same unrolled path as unpacked input.
-// LEAN (1: with the gate z, 2: without): the launch guarantees batch rows of whole aligned
-// tiles (seqlen and chunk_len multiples of the tile), every channel of every group in range
-// and softplus on: the tile loop then has no per-token selects and no branches around its
+// LEAN (1: with the gate z, 2: without): the launch guarantees rows of whole aligned tiles
+// (seqlen and chunk_len multiples of the tile), every channel of every group in range and
+// softplus on: the tile loop then has no per-token selects and no branches around its
 // loads and stores (4% of the kernel on the Mamba-2.8B layer shape).
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG, int LEAN>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
     static_assert(!CKPT || !LOCAL, "checkpoints: final pass");
     constexpr bool kLean = LEAN != 0;
-    static_assert(!kLean || !PACKED, "lean tiles: batch rows");
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
     constexpr bool kLeanGate = kOut && LEAN == 1;
@@ -765,8 +764,8 @@ hipError_t launch_scan_cg(int cg, dim3 grid, hipStream_t stream, const ScanParam
 
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT>
 hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
-    // the lean instantiation (bf16 batch rows): see scan_kernel
-    if constexpr (sizeof(IO) == 2 && !PACKED) {
+    // the lean instantiation (bf16): see scan_kernel
+    if constexpr (sizeof(IO) == 2) {
         const int64_t tile = kTile;
         // (and 32-bit buffer offsets: a workgroup's rows and a batch row of B/C below 2 GiB)
         if (prm.aligned && prm.softplus && prm.seqlen % tile == 0 &&
