@@ -185,7 +185,8 @@ constexpr int kBcTile = 8 * kBcPair;      // floats of widened B/C per tile (8 s
 // before its first token (in the direction of the scan) and saved after its last.
 // Those events depend on the token only, so every branch on them is uniform; tiles
 // without an event take the same unrolled path as unpacked input.
-// LEAN (1: with the gate z, 2: without): the launch guarantees rows of whole aligned tiles
+// LEAN (1: with the gate z, 2: without, 3: with the gate, adding into y -- the second
+// direction of a bidirectional scan): the launch guarantees rows of whole aligned tiles
 // (seqlen and chunk_len multiples of the tile), every channel of every group in range and
 // softplus on: the tile loop then has no per-token selects and no branches around its
 // loads and stores (4% of the kernel on the Mamba-2.8B layer shape).
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     constexpr bool kLean = LEAN != 0;
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
-    constexpr bool kLeanGate = kOut && LEAN == 1;
+    constexpr bool kLeanGate = kOut && (LEAN == 1 || LEAN == 3);
     __shared__ float sD[CG * kLdsRow];
     __shared__ float sU[CG * kLdsRow];
     constexpr int kPStride = CG * kLdsRow;   // floats per pair of partial readouts
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             for (int k = 0; k < 4; ++k) yv[k] *= post_g[k];
             if constexpr (kLean) {
                 const int so = (int)(t0 * (int64_t)sizeof(IO));
-                if (p.accumulate) {   // (uniform) the second direction of a bidirectional scan
+                if constexpr (LEAN == 3) {
                     const u32x2_t o = __builtin_amdgcn_raw_buffer_load_b64(lio.y, (int)lio.vo, so, 0);
                     yv[0] += bf16_lo(o.x);
                     yv[1] += bf16_hi(o.x);
@@ -771,10 +772,18 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
         if (prm.aligned && prm.softplus && prm.seqlen % tile == 0 &&
             prm.chunk_len % tile == 0 && prm.dim % cg == 0 &&
             (int64_t)cg * prm.seqlen * 2 < (int64_t(1) << 31) && prm.lpad * 128 < (int64_t(1) << 31)) {
-            if (LOCAL || prm.z)
+            // Pass 1 of the chunked plan writes no y (the gate and accumulation do not apply);
+            // accumulating takes the lean form with the gate and without checkpoints only
+            // (the bidirectional use), the general form otherwise.
+            if (LOCAL || (!prm.accumulate && prm.z))
                 return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 1>(cg, grid, stream, prm);
-            if constexpr (!LOCAL)
-                return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 2>(cg, grid, stream, prm);
+            if constexpr (!LOCAL) {
+                if (!prm.accumulate)
+                    return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 2>(cg, grid, stream, prm);
+                if constexpr (!CKPT)
+                    if (prm.z)
+                        return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 3>(cg, grid, stream, prm);
+            }
         }
     }
     return launch_scan_cg<IO, LOCAL, REV, PACKED, CKPT, 0>(cg, grid, stream, prm);
