@@ -1005,11 +1005,12 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         p2.chunk_offset = 0;
         const dim3 g2((unsigned)(ngroups * prm.nchunks));
         // the lean instantiation (bf16): see scan_bwd_kernel
-        // (and a batch row of B/C below 2 GiB, for its buffer offsets; a workgroup's rows
-        // are below 4 GiB for every plan)
+        // (and a workgroup's rows and a batch row of B/C below 2 GiB, so that every buffer
+        // offset is a non-negative 32-bit integer)
         const bool lean = bf16 && prm.aligned && prm.softplus && prm.z &&
                           prm.seqlen % kT == 0 && prm.chunk_len % kT == 0 &&
-                          prm.dim % cg == 0 && prm.lpad * 128 < (int64_t(1) << 31);
+                          prm.dim % cg == 0 && (int64_t)cg * prm.seqlen * 2 < (int64_t(1) << 31) &&
+                          prm.lpad * 128 < (int64_t(1) << 31);
         if (lean) {
             switch (cg) {
 #define SSM_LEAN(N)                                                                        \

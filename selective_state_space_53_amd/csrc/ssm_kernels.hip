@@ -189,7 +189,8 @@ constexpr int kBcTile = 8 * kBcPair;      // floats of widened B/C per tile (8 s
 // direction of a bidirectional scan): the launch guarantees rows of whole aligned tiles
 // (seqlen and chunk_len multiples of the tile), every channel of every group in range and
 // softplus on: the tile loop then has no per-token selects and no branches around its
-// loads and stores (4% of the kernel on the Mamba-2.8B layer shape).
+// loads and stores, which go through buffer resources (with the per-tile branch below, 8%
+// of the kernel's time on the Mamba-2.8B layer shape).
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG, int LEAN>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         float dl[4], uu[4], post_a[4], post_g[4];
         // The usual case -- a whole tile, softplus on, a gate if this pass applies one --
         // takes straight-line code; the selects of the general form (padding tokens,
-        // options) cost ~5% of the kernel on the Mamba-2.8B layer shape.
+        // options) cost ~2% of the kernel on the Mamba-2.8B layer shape.
         const bool fast = kLean || (vec && p.softplus && (!kOut || zr));
         auto pre = [&](auto fast_c) {
             constexpr bool kFast = decltype(fast_c)::value;
