@@ -876,15 +876,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
     const int64_t stride = L * 32;
     float s = 0.0f;
     int g = 0;
-    for (; g + 4 <= groups; g += 4) {   // four loads in flight, added in group order
-        const float a0 = src[(int64_t)g * stride], a1 = src[(int64_t)(g + 1) * stride];
-        const float a2 = src[(int64_t)(g + 2) * stride], a3 = src[(int64_t)(g + 3) * stride];
-        s += a0;
-        s += a1;
-        s += a2;
-        s += a3;
+    // eight loads in flight, added in group order; streaming loads, since every partial is
+    // read once (with four plain loads in flight: 38.1 -> 26.8 us on the 2.8B layer's 168 MB)
+    for (; g + 8 <= groups; g += 8) {
+        float a[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = __builtin_nontemporal_load(src + (int64_t)(g + j) * stride);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += a[j];
     }
-    for (; g < groups; ++g) s += src[(int64_t)g * stride];
+    for (; g < groups; ++g) s += __builtin_nontemporal_load(src + (int64_t)g * stride);
     const int64_t t = rem / 32;
     const int n32 = (int)(rem % 32);
     float* out = n32 < 16 ? dB : dC;
@@ -896,19 +897,27 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     const float* __restrict__ part_A, const float* __restrict__ part_D,
     const float* __restrict__ part_bias, float* __restrict__ dA, float* __restrict__ dD,
     float* __restrict__ dbias, int64_t batch, int64_t dim) {
-    // batch = the number of partial rows (batch rows x chunks)
+    // batch = the number of partial rows (batch rows x chunks). Eight streaming loads in
+    // flight per sum, added in row order: the chunked plans have hundreds of partial rows
+    // and few outputs, so the sums are bound by load latency (million-token backward:
+    // one thread per (d, n) over 316 chunk rows).
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < dim * kDState) {
+    auto sum_rows = [&](const float* part, int64_t stride) {
         float s = 0.0f;
-        for (int64_t b = 0; b < batch; ++b) s += part_A[b * dim * kDState + i];
-        dA[i] = s;
-    }
-    if (i < dim) {
-        float sd = 0.0f, sb = 0.0f;
-        for (int64_t b = 0; b < batch; ++b) {
-            sd += part_D[b * dim + i];
-            sb += part_bias[b * dim + i];
+        int64_t b = 0;
+        for (; b + 8 <= batch; b += 8) {
+            float a[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = __builtin_nontemporal_load(part + (b + j) * stride + i);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += a[j];
         }
+        for (; b < batch; ++b) s += __builtin_nontemporal_load(part + b * stride + i);
+        return s;
+    };
+    if (i < dim * kDState) dA[i] = sum_rows(part_A, dim * kDState);
+    if (i < dim) {
+        const float sd = sum_rows(part_D, dim), sb = sum_rows(part_bias, dim);
         if (dD) dD[i] = sd;
         if (dbias) dbias[i] = sb;
     }
@@ -1051,8 +1060,9 @@ hipError_t launch_scan_bwd(int cg, const BwdParams& prm, bool bf16, hipStream_t 
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)cdiv(prm.dim * kDState, 256)),
-                       dim3(256), 0, stream, prm.part_A, prm.part_D, prm.part_bias, prm.dA,
+    // (64-thread workgroups: a layer's dim x 16 sums spread over every CU)
+    hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)cdiv(prm.dim * kDState, 64)),
+                       dim3(64), 0, stream, prm.part_A, prm.part_D, prm.part_bias, prm.dA,
                        prm.dD, prm.dbias, prm.batch * prm.nchunks, prm.dim);
     e = hipGetLastError();
     if (e != hipSuccess || !prm.cu || !prm.dh0) return e;
