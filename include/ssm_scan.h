@@ -118,16 +118,21 @@ typedef struct {
                            and reverse, and the backward skips its own forward pass; nothing
                            checks that they match (stale contents give wrong gradients).
                            0 = the backward recomputes them.                              */
-    int32_t structured_a; /* ssm_scan_fwd with plan = 3 (the wave scan, batch rows only):
-                           1 = for every channel d whose A row satisfies A[d,n] ==
-                           (n+1)*A[d,0] exactly (fp32; checked on the device, per channel),
-                           take the decays as powers exp(Delta*A[d,0])^(n+1) -- one exp per
-                           (token, channel) and a multiply per state instead of one exp per
-                           (token, channel, state); other channels take the general path.
-                           The results differ from the general path by rounding only (the
-                           powers accumulate up to 16 roundings and multiply the exp's own
-                           relative error by n+1). 0 = general path everywhere. Any other
-                           plan with structured_a = 1 returns SSM_ERR_UNSUPPORTED.       */
+    int32_t structured_a; /* ssm_scan_fwd: 1 = channels whose A row satisfies A[d,n] ==
+                           (n+1)*A[d,0] exactly (fp32; checked on the device) may take their
+                           decays from fewer exps; the results differ from the general path
+                           by rounding only. The wave scan (plan 3, batch rows) takes, per
+                           such channel, the powers exp(Delta*A[d,0])^(n+1) -- one exp per
+                           (token, channel) and a multiply per state; the powers accumulate up
+                           to 16 roundings and multiply the exp's own relative error by n+1.
+                           The single-pass and chunked plans (the chunked plan's final pass)
+                           take, for bf16 batch rows of whole 32-token tiles with softplus on,
+                           not accumulating and without save_workspace, in groups of 16 or 32
+                           channels whose A rows all satisfy it, each odd state's decay as the
+                           even state's times exp(Delta*A[d,0]) -- one exp per (token,
+                           channel, state pair) and one per (token, channel). Every other
+                           channel and launch takes the general decays, bit for bit as with
+                           0. 0 = general decays everywhere.                              */
 } ssm_scan_options;
 
 /*

@@ -196,7 +196,8 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     the library records around the launch of the scan kernel that writes y.
     save_for_backward: a uint8 device tensor of ssm_scan_bwd_workspace_bytes(...) bytes
     into which the call also saves the checkpoints and q; pass it to ssm_scan_bwd as its
-    workspace with saved=True."""
+    workspace with saved=True. structured_a: channels with A[d,n] == (n+1)*A[d,0] may take
+    their decays from fewer exps (ssm_scan_options.structured_a)."""
     _dev(x, "x")
     io = x.dtype
     batch, dim, seqlen = x.shape

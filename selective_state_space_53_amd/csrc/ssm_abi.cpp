@@ -185,9 +185,6 @@ ssm_status make_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
         if (opts->structured_a != 0 && opts->structured_a != 1)
             return fail(SSM_ERR_INVALID_ARGUMENT, "ssm_scan_options.structured_a=%d not 0 or 1",
                         (int)opts->structured_a);
-        if (opts->structured_a && opts->plan != 3)
-            return fail(SSM_ERR_UNSUPPORTED,
-                        "ssm_scan_options.structured_a needs plan = 3 (the wave scan)");
         req_plan = opts->plan;
         req_chunk = opts->chunk_len;
     }

@@ -51,7 +51,8 @@ struct ScanParams {
     int32_t nchunks, ngroups, groups_per_batch, chunk_offset;
     int32_t nseq;
     int32_t softplus, aligned, reverse, accumulate;
-    int32_t structured_a;   // wave scan: powers of exp(Delta*A[d,0]) for structured rows
+    int32_t structured_a;   // structured A allowed: the wave scan's powers of exp(Delta*A[d,0]),
+                            // the sequential lean form's paired decays
 };
 
 struct DecodeParams {

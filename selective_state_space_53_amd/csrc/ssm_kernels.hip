@@ -191,19 +191,33 @@ constexpr int kBcTile = 8 * kBcPair;      // floats of widened B/C per tile (8 s
 // softplus on: the tile loop then has no per-token selects and no branches around its
 // loads and stores, which go through buffer resources (with the per-tile branch below, 8%
 // of the kernel's time on the Mamba-2.8B layer shape).
+// LEAN 4 (with the gate) and 5 (without), batch rows of a final pass without checkpoints:
+// the lean form with structured A. A workgroup whose A rows all satisfy A[d,n] ==
+// (n+1) A[d,0] (checked here) takes the odd state's decay of each pair from the even
+// one's, exp(Delta A[d,2p+1]) = exp(Delta A[d,2p]) exp(Delta A[d,0]), the second factor
+// evaluated once per (token, channel) in the pre stage: one exp per (token, channel,
+// pair) instead of two. Other workgroups take the general decays.
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT, int CG, int LEAN>
 __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     static_assert(CG % 16 == 0 && CG >= 16 && CG <= 96, "channel group");
     static_assert(!CKPT || !LOCAL, "checkpoints: final pass");
     constexpr bool kLean = LEAN != 0;
+    constexpr bool kStructA = LEAN >= 4;
+    static_assert(!kStructA || (!LOCAL && !PACKED && !CKPT), "structured A: batch rows, final pass");
     constexpr int kRowsPerPair = CG / 16;
     constexpr bool kOut = !LOCAL;   // this pass writes y (CKPT: also the checkpoints)
-    constexpr bool kLeanGate = kOut && (LEAN == 1 || LEAN == 3);
+    constexpr bool kLeanGate = kOut && (LEAN == 1 || LEAN == 3 || LEAN == 4);
     __shared__ float sD[CG * kLdsRow];
     __shared__ float sU[CG * kLdsRow];
     constexpr int kPStride = CG * kLdsRow;   // floats per pair of partial readouts
     __shared__ float sP[kOut ? 8 * kPStride : 4];
-    __shared__ float sBC[2 * kBcTile];
+    // One B/C buffer is enough where the next tile's B/C is written after the barrier that
+    // ends this tile's core (below); the structured form, whose exp(Delta A[d,0]) row takes
+    // the LDS of the second buffer, has one (five 16-channel workgroups per CU still fit).
+    constexpr int kBcBufs = kStructA ? 1 : 2;
+    __shared__ float sBC[kBcBufs * kBcTile];
+    __shared__ float sR[kStructA ? CG * kLdsRow : 1];
+    __shared__ int sFlag[1];
 
     const int tid = threadIdx.x;
     const int g = blockIdx.x % p.ngroups;
@@ -230,6 +244,8 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     const int64_t rowq = b * p.dim + dq;
 
     float a2[2], h[2];
+    bool sall = false;    // structured form: every A row of the workgroup is structured
+    float a0q = 0.0f;     // structured form: A[dq,0] log2(e) for the pre stage's channel
     {
         float2 av = make_float2(0.f, 0.f), hv = av;
         if (valid) {
@@ -246,6 +262,17 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         a2[1] = av.y * kLog2e;
         h[0] = hv.x;
         h[1] = hv.y;
+        if constexpr (kStructA) {
+            // (every channel of a lean launch is in range) the lane's two states
+            const float a0 = p.A[d * kDState];
+            const bool ok = av.x == (float)(2 * pr + 1) * a0 && av.y == (float)(2 * pr + 2) * a0;
+            if (tid == 0) sFlag[0] = 1;
+            __syncthreads();
+            if (!ok) sFlag[0] = 0;
+            __syncthreads();
+            sall = __builtin_amdgcn_readfirstlane(sFlag[0]) != 0;   // uniform
+            a0q = p.A[dq * kDState] * kLog2e;
+        }
     }
     const float bias = (validq && p.bias) ? p.bias[dq] : 0.0f;
     const float Dd = (validq && p.D) ? p.D[dq] : 0.0f;
@@ -353,6 +380,8 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
     float* const myUq = sU + cq * kLdsRow + 4 * jq;
     const float* const coreD = sD + cc * kLdsRow;     // core: the lane's channel
     const float* const coreU = sU + cc * kLdsRow;
+    float* const myRq = sR + (kStructA ? cq * kLdsRow + 4 * jq : 0);
+    const float* const coreR = sR + (kStructA ? cc * kLdsRow : 0);
 
     Raw4<IO> rx, rdl, rz;
     float4 rbc[kMoves];
@@ -443,7 +472,9 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             if (kOut) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    post_g[k] = LEAN == 2 ? 1.0f : (kFast || zr) ? silu_f(zv[k]) : 1.0f;
+                    post_g[k] = (LEAN == 2 || LEAN == 5) ? 1.0f
+                                : (kFast || zr)              ? silu_f(zv[k])
+                                                             : 1.0f;
                     post_a[k] = Dd * xv[k];
                 }
             }
@@ -452,6 +483,10 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         else pre(std::false_type{});
         *reinterpret_cast<float4*>(myDq) = make_float4(dl[0], dl[1], dl[2], dl[3]);
         *reinterpret_cast<float4*>(myUq) = make_float4(uu[0], uu[1], uu[2], uu[3]);
+        if (kStructA && sall)   // exp(Delta A[d,0]) of the tile's tokens
+            *reinterpret_cast<float4*>(myRq) =
+                make_float4(decay_exp2<IO>(dl[0] * a0q), decay_exp2<IO>(dl[1] * a0q),
+                            decay_exp2<IO>(dl[2] * a0q), decay_exp2<IO>(dl[3] * a0q));
         __syncthreads();
 
         // With 32 channels a CU holds several workgroups, out of phase: the core runs at
@@ -463,7 +498,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         // Every lane of a row reads the same (B0, B1, C0, C1) of a token from LDS, so B
         // and C arrive in VGPRs and every op below is a plain VOP2 with VGPR operands
         // (the fast FP32 issue path; SGPR or DPP operands halve it).
-        const float* bct = sBC + (it & 1) * kBcTile + pr * kBcPair;
+        const float* bct = sBC + (kBcBufs == 2 ? (it & 1) : 0) * kBcTile + pr * kBcPair;
         float* const pout = sP + pr * kPStride + cc * kLdsRow;
 #define SSM_TOKEN(OUT, DS, US, Q)                                                     \
     {                                                                                 \
@@ -473,6 +508,16 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         h[1] = __builtin_fmaf(e1, h[1], Q.y * US);                                    \
         if (kOut) OUT = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                        \
         else if (LOCAL && pr == 0) dsum += DS;                                        \
+    }
+        // the structured form: the odd state's decay from the even one's (RS = exp(Delta
+        // A[d,0]) of the token)
+#define SSM_TOKEN_S(OUT, DS, US, RS, Q)                                               \
+    {                                                                                 \
+        const float e0 = decay_exp2<IO>(DS * a2[0]);                                  \
+        const float e1 = e0 * RS;                                                     \
+        h[0] = __builtin_fmaf(e0, h[0], Q.x * US);                                    \
+        h[1] = __builtin_fmaf(e1, h[1], Q.y * US);                                    \
+        OUT = __builtin_fmaf(Q.w, h[1], Q.z * h[0]);                                  \
     }
         // quiet tile: no sequence starts or ends inside it (always, for batch rows)
         const int64_t tlast = t0 + nvalid - 1;
@@ -486,39 +531,64 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
                     *reinterpret_cast<float2*>(ck + blk * ckstride) = make_float2(h[0], h[1]);
             };
             checkpoint(REV ? t0 / 16 + 1 : t0 / 16);
-            // the LDS operands of 4 tokens, read one group ahead of their use
-            float4 nD, nU, n0, n1, n2, n3;
-            auto fetch = [&](int tq) {
-                nD = *reinterpret_cast<const float4*>(coreD + tq);
-                nU = *reinterpret_cast<const float4*>(coreU + tq);
-                n0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
-                n1 = *reinterpret_cast<const float4*>(bct + (tq + 1) * 4);
-                n2 = *reinterpret_cast<const float4*>(bct + (tq + 2) * 4);
-                n3 = *reinterpret_cast<const float4*>(bct + (tq + 3) * 4);
-            };
-            fetch(REV ? kTile - 4 : 0);
+            // the tile in groups of 4 tokens, the LDS operands of a group read one group
+            // ahead of their use (S: the structured decays)
+            auto groups = [&](auto s_c) {
+                constexpr bool S = decltype(s_c)::value;
+                float4 nD, nU, nR, n0, n1, n2, n3;
+                auto fetch = [&](int tq) {
+                    nD = *reinterpret_cast<const float4*>(coreD + tq);
+                    nU = *reinterpret_cast<const float4*>(coreU + tq);
+                    if (S) nR = *reinterpret_cast<const float4*>(coreR + tq);
+                    n0 = *reinterpret_cast<const float4*>(bct + (tq + 0) * 4);
+                    n1 = *reinterpret_cast<const float4*>(bct + (tq + 1) * 4);
+                    n2 = *reinterpret_cast<const float4*>(bct + (tq + 2) * 4);
+                    n3 = *reinterpret_cast<const float4*>(bct + (tq + 3) * 4);
+                };
+                fetch(REV ? kTile - 4 : 0);
 #pragma unroll
-            for (int gq = 0; gq < kTile; gq += 4) {
-                const int tq = REV ? kTile - 4 - gq : gq;
-                if (gq == 16) checkpoint(REV ? t0 / 16 : t0 / 16 + 1);
-                const float4 D4 = nD, U4 = nU, q0 = n0, q1 = n1, q2 = n2, q3 = n3;
-                if (gq + 4 < kTile) fetch(REV ? kTile - 8 - gq : gq + 4);
-                __builtin_amdgcn_sched_barrier(0);
-                float pp[4];
-                if (!REV) {
-                    SSM_TOKEN(pp[0], D4.x, U4.x, q0)
-                    SSM_TOKEN(pp[1], D4.y, U4.y, q1)
-                    SSM_TOKEN(pp[2], D4.z, U4.z, q2)
-                    SSM_TOKEN(pp[3], D4.w, U4.w, q3)
-                } else {
-                    SSM_TOKEN(pp[3], D4.w, U4.w, q3)
-                    SSM_TOKEN(pp[2], D4.z, U4.z, q2)
-                    SSM_TOKEN(pp[1], D4.y, U4.y, q1)
-                    SSM_TOKEN(pp[0], D4.x, U4.x, q0)
+                for (int gq = 0; gq < kTile; gq += 4) {
+                    const int tq = REV ? kTile - 4 - gq : gq;
+                    if (gq == 16) checkpoint(REV ? t0 / 16 : t0 / 16 + 1);
+                    const float4 D4 = nD, U4 = nU, q0 = n0, q1 = n1, q2 = n2, q3 = n3;
+                    float4 R4;
+                    if (S) R4 = nR;
+                    if (gq + 4 < kTile) fetch(REV ? kTile - 8 - gq : gq + 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                    float pp[4];
+                    if constexpr (S) {
+                        if (!REV) {
+                            SSM_TOKEN_S(pp[0], D4.x, U4.x, R4.x, q0)
+                            SSM_TOKEN_S(pp[1], D4.y, U4.y, R4.y, q1)
+                            SSM_TOKEN_S(pp[2], D4.z, U4.z, R4.z, q2)
+                            SSM_TOKEN_S(pp[3], D4.w, U4.w, R4.w, q3)
+                        } else {
+                            SSM_TOKEN_S(pp[3], D4.w, U4.w, R4.w, q3)
+                            SSM_TOKEN_S(pp[2], D4.z, U4.z, R4.z, q2)
+                            SSM_TOKEN_S(pp[1], D4.y, U4.y, R4.y, q1)
+                            SSM_TOKEN_S(pp[0], D4.x, U4.x, R4.x, q0)
+                        }
+                    } else if (!REV) {
+                        SSM_TOKEN(pp[0], D4.x, U4.x, q0)
+                        SSM_TOKEN(pp[1], D4.y, U4.y, q1)
+                        SSM_TOKEN(pp[2], D4.z, U4.z, q2)
+                        SSM_TOKEN(pp[3], D4.w, U4.w, q3)
+                    } else {
+                        SSM_TOKEN(pp[3], D4.w, U4.w, q3)
+                        SSM_TOKEN(pp[2], D4.z, U4.z, q2)
+                        SSM_TOKEN(pp[1], D4.y, U4.y, q1)
+                        SSM_TOKEN(pp[0], D4.x, U4.x, q0)
+                    }
+                    if (kOut)
+                        *reinterpret_cast<float4*>(pout + tq) =
+                            make_float4(pp[0], pp[1], pp[2], pp[3]);
                 }
-                if (kOut)
-                    *reinterpret_cast<float4*>(pout + tq) =
-                        make_float4(pp[0], pp[1], pp[2], pp[3]);
+            };
+            if constexpr (kStructA) {
+                if (sall) groups(std::true_type{});
+                else groups(std::false_type{});
+            } else {
+                groups(std::false_type{});
             }
         } else {
             // token by token, with the sequence events (padding tokens have none)
@@ -553,6 +623,7 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
             }
         }
 #undef SSM_TOKEN
+#undef SSM_TOKEN_S
         // pass 1 keeps its results in registers only, so the compiler may sink the whole
         // recurrence below the barrier and then has to hold every LDS operand of the tile
         // at once (~160 VGPRs); an empty asm that claims to update the state keeps the
@@ -560,16 +631,16 @@ __global__ __launch_bounds__(CG * 8) void scan_kernel(const ScanParams p) {
         if (LOCAL) asm volatile("" : "+v"(h[0]), "+v"(h[1]), "+v"(dsum));
         if (CG <= 32) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
-        // the next tile's B/C into the other LDS buffer (its last readers finished before
-        // the barrier above; its next readers come after the next barrier). The loads were
-        // issued before the core, so the wait is short; taken here, before this tile's
-        // stores, it does not wait for them.
+        // the next tile's B/C into the other LDS buffer, or the one buffer (the last
+        // readers of either finished before the barrier above; the next ones come after
+        // the next barrier). The loads were issued before the core, so the wait is short;
+        // taken here, before this tile's stores, it does not wait for them.
         wait_vmem();
         if (bc_mover && it + 1 < nt) {
 #pragma unroll
             for (int m = 0; m < kMoves; ++m)
-                *reinterpret_cast<float4*>(bcdst + ((it + 1) & 1) * kBcTile + m * kMoveSrc * kBcPair) =
-                    rbc[m];
+                *reinterpret_cast<float4*>(bcdst + (kBcBufs == 2 ? ((it + 1) & 1) : 0) * kBcTile +
+                                           m * kMoveSrc * kBcPair) = rbc[m];
         }
 
         // ---- post: this thread's 4 tokens: sum the 8 pairs' partials, skip, gate, store
@@ -764,6 +835,19 @@ hipError_t launch_scan_cg(int cg, dim3 grid, hipStream_t stream, const ScanParam
     return hipGetLastError();
 }
 
+// the structured-A lean form (16 or 32 channels per workgroup, the groups the planner
+// picks where it applies)
+template <typename IO, bool REV, int LEAN>
+hipError_t launch_scan_cg_sa(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
+    if (cg == 16)
+        hipLaunchKernelGGL((scan_kernel<IO, false, REV, false, false, 16, LEAN>), grid, dim3(128),
+                           0, stream, prm);
+    else
+        hipLaunchKernelGGL((scan_kernel<IO, false, REV, false, false, 32, LEAN>), grid, dim3(256),
+                           0, stream, prm);
+    return hipGetLastError();
+}
+
 template <typename IO, bool LOCAL, bool REV, bool PACKED, bool CKPT>
 hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanParams& prm) {
     // the lean instantiation (bf16): see scan_kernel
@@ -773,6 +857,10 @@ hipError_t launch_scan_kernel(int cg, dim3 grid, hipStream_t stream, const ScanP
         if (prm.aligned && prm.softplus && prm.seqlen % tile == 0 &&
             prm.chunk_len % tile == 0 && prm.dim % cg == 0 &&
             (int64_t)cg * prm.seqlen * 2 < (int64_t(1) << 31) && prm.lpad * 128 < (int64_t(1) << 31)) {
+            if constexpr (!LOCAL && !PACKED && !CKPT)
+                if (prm.structured_a && !prm.accumulate && (cg == 16 || cg == 32))
+                    return prm.z ? launch_scan_cg_sa<IO, REV, 4>(cg, grid, stream, prm)
+                                 : launch_scan_cg_sa<IO, REV, 5>(cg, grid, stream, prm);
             // Pass 1 of the chunked plan writes no y (the gate and accumulation do not apply);
             // accumulating takes the lean form with the gate and without checkpoints only
             // (the bidirectional use), the general form otherwise.

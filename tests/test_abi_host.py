@@ -93,13 +93,11 @@ def test_scan_rejects_bad_options(b):
     assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 2, 40))) == 1  # group size
     assert scan(b, opts=ctypes.byref(b.ScanOptions(64, 2, 112))) == 1
     assert scan(b, opts=ctypes.byref(b.ScanOptions(-32, 2, 0))) == 1
-    # structured_a: a flag of the wave-scan plan only
-    o = b.ScanOptions(0, 2, 0)
-    o.structured_a = 1
-    assert scan(b, opts=ctypes.byref(o)) == 2
-    o = b.ScanOptions(0, 3, 0)
-    o.structured_a = 2
-    assert scan(b, opts=ctypes.byref(o)) == 1
+    # structured_a: 0 or 1, with any plan
+    for plan in (0, 1, 2, 3):
+        o = b.ScanOptions(0, plan, 0)
+        o.structured_a = 2
+        assert scan(b, opts=ctypes.byref(o)) == 1
 
 
 def noalloc(b, batch=2, seqlen=64, dim=64, dstate=16, io=1, opts=None, **over):
