@@ -15,11 +15,12 @@
 // art; what carries over is keeping the state on chip, streaming the sequence once
 // and writing back only boundary states):
 //
-//  * A workgroup owns CG channels of one batch row and all 16 states (CG a multiple of
-//    16, chosen by the planner: 80 on the 2.8B layer, i.e. 640 threads and one
-//    workgroup per CU). Each lane keeps one state pair (2 states) of one channel in
-//    VGPRs for the whole sequence (or chunk); a 16-lane row holds one pair of 16
-//    consecutive channels.
+//  * A workgroup owns CG channels of one batch row and all 16 states: CG * 8 threads,
+//    i.e. CG / 8 waves (CG a multiple of 16, chosen by the planner's cost model: 16 on
+//    the Mamba-130M and 2.8B layer shapes, two waves per workgroup and five workgroups
+//    per CU; 32 for the chunked plans of long rows). Each lane keeps one state pair (2
+//    states) of one channel in VGPRs for the whole sequence (or chunk); a 16-lane row
+//    holds one pair of 16 consecutive channels, a wave four pairs of the same channels.
 //  * B_t and C_t do not depend on the channel. A small pass widens them once into
 //    fp32 per state pair ([batch][pair][token][B0 B1 C0 C1]); the scan stages each
 //    tile's slice through LDS, and a row reads its pair's four values with one
