@@ -43,6 +43,12 @@
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
+// No implicit fusing of a multiply and an add into an FMA in this file: every FMA is
+// written out, so a kernel's results do not depend on how the compiler happened to
+// schedule or unroll it (the unrolled tile loop would otherwise fuse a few of the adds
+// that the rolled loop does not, and change the gradients' last bits).
+#pragma clang fp contract(off)
+
 namespace ssm {
 
 namespace {
@@ -388,20 +394,52 @@ void scan_bwd_kernel(const BwdParams p) {
     // moved to a scalar register right away, and the wait for it would also wait for the
     // next tile's prefetched inputs issued before it.)
     uint32_t rev = 0;
-    // ti: tile of the chunk; its checkpoint is the global tile t0 / 16
-    auto load_tile = [&](int ti) {
+    // LEAN batch rows in whole 64-token groups: a 128-byte line of an input row holds the
+    // thread's 2 tokens of four consecutive tiles. Loaded tile by tile, a line fetched for
+    // one tile was often evicted from the L2 before the next tile's turn (~1.8x the input
+    // bytes read); here the first tile of a group loads the four tiles' words at once and
+    // holds the later three in `hold` (15 VGPRs), so each line is fetched once. The tile
+    // loop is unrolled by the group, so hold[j] stays in fixed registers (moving them
+    // along tile by tile cost 3% of the kernel). Not for 48 channels or packed rows: their
+    // kernels would spill.
+    constexpr bool kGroupLoads = LEAN && !PACKED && CG != 48;
+    static_assert(!LEAN || sizeof(IO) == 2, "lean rows are bf16");
+    constexpr int kGrp = 4;
+    constexpr int kU = kGroupLoads ? kGrp : 1;
+    const bool grouped = kGroupLoads && (t_beg % (kGrp * kT)) == 0 && (ntiles % kGrp) == 0;
+    uint32_t hold[kGrp - 1][5];
+    // the five input rows' words of tile ti (LEAN)
+    auto lean_rows = [&](int ti, uint32_t (&w)[5]) {
+        const int so = (int)((t_beg + (int64_t)ti * kT) * (int64_t)sizeof(IO));
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(lio.x, (int)lio.vo, so, 0);
+        w[1] = __builtin_amdgcn_raw_buffer_load_b32(lio.d, (int)lio.vo, so, 0);
+        w[2] = __builtin_amdgcn_raw_buffer_load_b32(lio.z, (int)lio.vo, so, 0);
+        w[3] = __builtin_amdgcn_raw_buffer_load_b32(lio.q, (int)lio.vo, so, 0);
+        w[4] = __builtin_amdgcn_raw_buffer_load_b32(lio.g, (int)lio.vo, so, 0);
+    };
+    auto take = [&](const uint32_t (&w)[5]) {
+        if constexpr (LEAN) {
+            rx.w = w[0];
+            rd.w = w[1];
+            rz.w = w[2];
+            rq.w = w[3];
+            rg.w = w[4];
+        }
+    };
+    // ti: tile of the chunk; its checkpoint is the global tile t0 / 16. rows = false: the
+    // rows' words come from a group load.
+    auto load_tile = [&](int ti, bool rows) {
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
         const int nq = nvalid - 2 * jq;
         const bool vec = p.aligned && nvalid == kT;
         // one uniform branch for the tile rather than one per load
         if constexpr (LEAN) {
-            const int so = (int)(t0 * (int64_t)sizeof(IO));
-            rx.w = __builtin_amdgcn_raw_buffer_load_b32(lio.x, (int)lio.vo, so, 0);
-            rd.w = __builtin_amdgcn_raw_buffer_load_b32(lio.d, (int)lio.vo, so, 0);
-            rz.w = __builtin_amdgcn_raw_buffer_load_b32(lio.z, (int)lio.vo, so, 0);
-            rq.w = __builtin_amdgcn_raw_buffer_load_b32(lio.q, (int)lio.vo, so, 0);
-            rg.w = __builtin_amdgcn_raw_buffer_load_b32(lio.g, (int)lio.vo, so, 0);
+            if (rows) {
+                uint32_t w[5];
+                lean_rows(ti, w);
+                take(w);
+            }
         } else if (vec) {
             if (validq) {
                 const uint32_t o = at(t0);
@@ -439,13 +477,41 @@ void scan_bwd_kernel(const BwdParams p) {
     rz.zero();
     rg.zero();
     rq.zero();
-    load_tile(REV ? 0 : ntiles - 1);
+    // grouped: tile tn starts a group (the first of its four in the walk's order): its
+    // words and the next three tiles' words
+    auto load_group = [&](int tn) {
+        uint32_t w[5];
+        lean_rows(tn, w);
+#pragma unroll
+        for (int j = 0; j < kGrp - 1; ++j) lean_rows(REV ? tn + 1 + j : tn - 1 - j, hold[j]);
+        take(w);
+        load_tile(tn, false);
+    };
+    // the next tile tn, which is the (jj + 1)-th of the current group (grouped, jj <
+    // kGrp - 1) or the first of the next group
+    auto load_next = [&](int tn, auto jj_c) {
+        constexpr int jj = decltype(jj_c)::value;
+        if constexpr (kGroupLoads && jj < kGrp - 1) {
+            if (grouped) {
+                take(hold[jj]);
+                load_tile(tn, false);
+                return;
+            }
+        }
+        if (grouped) load_group(tn);
+        else load_tile(tn, true);
+    };
+    if (grouped) load_group(REV ? 0 : ntiles - 1);
+    else load_tile(REV ? 0 : ntiles - 1, true);
 
     if (bc_mover) *reinterpret_cast<float4*>(bcdst) = rbc;
     wait_vmem();   // nothing in flight at the loop's entry: no wait at its top
 
     float dDacc = 0.0f, dbacc = 0.0f;
-    for (int it = 0; it < ntiles; ++it) {
+    for (int it0 = 0; it0 < ntiles; it0 += kU) {
+    auto tile_body = [&](auto jj_c) __attribute__((always_inline)) {
+        constexpr int jj = decltype(jj_c)::value;
+        const int it = it0 + jj;
         const int ti = REV ? it : ntiles - 1 - it;   // the adjoint runs against the scan
         const int64_t t0 = t_beg + (int64_t)ti * kT;
         const int nvalid = (t_end - t0 < kT) ? (int)(t_end - t0) : kT;
@@ -463,7 +529,7 @@ void scan_bwd_kernel(const BwdParams p) {
         // after the token that follows it)
         const float hs0 = rck.x, hs1 = rck.y;
         if (PACKED && tid == 0) sEv = rev;
-        if (it + 1 < ntiles) load_tile(REV ? ti + 1 : ti - 1);
+        if (it + 1 < ntiles) load_next(REV ? ti + 1 : ti - 1, jj_c);
         float dl[2], sg[2], dqv[2], uu[2], dzv[2];
         // the usual case (a whole tile, softplus on, a gate) in straight-line code, the
         // general one with its selects for padding tokens and options (bf16 only: with
@@ -671,6 +737,15 @@ void scan_bwd_kernel(const BwdParams p) {
             for (int j = 0; j < kRowsPerPair; ++j)
                 sum += sRed[(k * kLaneRows + (n >> 1) * kRowsPerPair + j) * 4 + which * 2 + (n & 1)];
             if (LEAN || k < nvalid) __builtin_nontemporal_store(sum, &pbc[(t0 + k) * 32 + v]);
+        }
+    };
+        tile_body(std::integral_constant<int, 0>{});
+        if constexpr (kU > 1) {
+            if (it0 + 1 < ntiles) tile_body(std::integral_constant<int, 1>{});
+        }
+        if constexpr (kU > 2) {
+            if (it0 + 2 < ntiles) tile_body(std::integral_constant<int, 2>{});
+            if (it0 + 3 < ntiles) tile_body(std::integral_constant<int, 3>{});
         }
     }
 
