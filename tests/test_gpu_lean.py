@@ -93,13 +93,19 @@ def test_bidirectional_accumulate_lean_equals_general():
 
 
 @pytest.mark.parametrize("reverse", [False, True], ids=["causal", "anticausal"])
-def test_backward_lean_equals_general(reverse):
+@pytest.mark.parametrize("L,bwd_chunk", [(256, 0), (272, 0), (512, 128), (512, 96), (512, 192)],
+                         ids=["L256", "L272", "L512_c128", "L512_c96", "L512_c192"])
+def test_backward_lean_equals_general(reverse, L, bwd_chunk):
     # 64 channels: backward groups of 32 (lean) or 48 (a ragged last group: general); the
-    # forward checkpoint pass likewise in groups of 16 (lean) or 48 (general)
+    # forward checkpoint pass likewise in groups of 16 (lean) or 48 (general). The lean
+    # kernel loads the input rows of four 16-token tiles together when its chunk starts on
+    # a 64-token line and holds a multiple of four tiles (L256; L512 with chunks of 128 or
+    # 192 tokens, the last one 128), and tile by tile otherwise (L272: 17 tiles; chunks of
+    # 96 tokens: 6 tiles, every other one starting mid-line).
     from selective_state_space_53_amd import binding
-    batch, L, dim = 2, 256, 64
+    batch, dim = 2, 64
     cfg = synth.ScanConfig("leanb", batch, L, dim, io="bf16", seed=911)
-    say("case lean backward", reverse)
+    say("case lean backward", reverse, L, bwd_chunk)
     inp = synth.scan_inputs(cfg, DEV)
     dy = synth.scan_inputs(cfg, DEV, seed=912)["z"]
     gen = torch.Generator(device="cpu").manual_seed(913)
@@ -109,8 +115,9 @@ def test_backward_lean_equals_general(reverse):
     def run(fwd_cg, bwd_cg):
         g = binding.ssm_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
                                  D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], h0=h0,
-                                 dh_final=dhf, want_dh0=True, group_channels=fwd_cg,
-                                 bwd_group_channels=bwd_cg, reverse=reverse)
+                                 dh_final=dhf, want_dh0=True, plan=1, group_channels=fwd_cg,
+                                 bwd_group_channels=bwd_cg, bwd_chunk_len=bwd_chunk,
+                                 reverse=reverse)
         torch.cuda.synchronize()
         return g
 
