@@ -29,6 +29,12 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 KERNEL_SOURCES = ["ssm_kernels.hip", "ssm_wavescan.hip", "ssm_conv.hip", "ssm_bwd.hip",
                   "ssm_noalloc.hip"]
+# Per-source code generation flags. The forward scan kernels are scheduled for
+# instruction-level parallelism (LLVM's max-ilp machine scheduler for AMDGPU): same-box
+# A/B against the default scheduler, identical results, 130M layer 139.3 -> 136.2 us,
+# anti-causal 2.8B 187.0 -> 182.3 us, 2.8B layer 197.6 -> 197.8 us, million-token pass 2
+# 6.75 -> 6.80 ms. The backward kernel keeps the default (610 -> 637 us with max-ilp).
+SOURCE_FLAGS = {"ssm_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _run(cmd, verbose):
@@ -51,7 +57,8 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     if save_temps:
         extra = ["--save-temps"]
     k_objs = [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in KERNEL_SOURCES]
-    cmds = [["hipcc", "-c", *DEVICE_FLAGS, *inc, *extra, os.path.join(CSRC, src), "-o", obj]
+    cmds = [["hipcc", "-c", *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *inc, *extra,
+             os.path.join(CSRC, src), "-o", obj]
             for src, obj in zip(KERNEL_SOURCES, k_objs)]
     cmds.append(["hipcc", "-c", *HOST_FLAGS, *inc, os.path.join(CSRC, "ssm_abi.cpp"), "-o", a_obj])
     cwd = os.getcwd()
